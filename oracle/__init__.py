@@ -1,0 +1,175 @@
+"""CPU oracle for dynamic block-scaled quantization (MXFP4, MXFP8, NVFP4).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
+with the GPU library (``fp8_quantization_amd``) and neither imports the other.
+
+Two independent implementations live here:
+
+* ``liboracle.so`` (``oracle.c``): plain scalar C, the reference the GPU output
+  is compared with byte for byte.  Wrapped below with numpy arrays.
+* ``spec`` (``spec.py``): exact rational arithmetic (``fractions.Fraction``) and
+  brute-force nearest-value search; it pins the C oracle on the CPU.
+
+Formats follow the Modular "block_scaled_quantization" module page (three
+formats: NVFP4, MXFP4, MXFP8) and the two kernel pages
+("quantize_dynamic_scaled_async_fp4_kernel": scalar fp32 tensor_sf and
+SF_VECTOR_SIZE; "grouped_quantize_dynamic_scaled_fp4_async_kernel": offsets,
+expert ids, per-expert sf, optional row_indices).  Parity with the pages' own
+kernels is unpinned (the pages print no values); the pins are the format
+definitions, exhaustive brute force, invariants and error bounds.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+MXFP4, MXFP8, NVFP4 = 0, 1, 2
+BLOCK = {MXFP4: 32, MXFP8: 32, NVFP4: 16}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _build
+
+        _build.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, i32, p = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    lib.oracle_quantize.argtypes = [i32, i32, p, i64, i64, i64, p, i64, p, i64, ctypes.c_float, i32]
+    lib.oracle_quantize.restype = i32
+    lib.oracle_grouped_quantize.argtypes = [i32, i32, p, i64, i64, i64, p, p, p, p, p, i64, i64,
+                                            p, i64, p, i64, i32]
+    lib.oracle_grouped_quantize.restype = i32
+    lib.oracle_validate_grouped.argtypes = [p, p, p, p, i64, i64, i64, i64, i64]
+    lib.oracle_validate_grouped.restype = i32
+    lib.oracle_dequantize.argtypes = [i32, i32, p, i64, i64, i64, p, i64, ctypes.c_float, p]
+    lib.oracle_dequantize.restype = i32
+    for name in ("oracle_e2m1_code", "oracle_e4m3_code"):
+        getattr(lib, name).argtypes = [ctypes.c_double]
+        getattr(lib, name).restype = i32
+    for name in ("oracle_e2m1_decode", "oracle_e4m3_decode", "oracle_e8m0_decode",
+                 "oracle_bf16_decode"):
+        getattr(lib, name).argtypes = [i32]
+        getattr(lib, name).restype = ctypes.c_double
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _ld(a, unit: int) -> int:
+    """Row stride in elements of size ``unit``; a single-row view may report 0."""
+    return a.strides[0] // unit if a.shape[0] > 1 else a.shape[1]
+
+
+def code_width(fmt: int, K: int) -> int:
+    """Bytes of packed codes per row: two FP4 codes per byte, one FP8 code per byte."""
+    return K if fmt == MXFP8 else K // 2
+
+
+def quantize(x_bits: np.ndarray, fmt: int, tensor_sf: float = 1.0, bs: int | None = None,
+             nthreads: int = 1, codes: np.ndarray | None = None,
+             scales: np.ndarray | None = None):
+    """Dense form.  ``x_bits``: uint16 [M, K] BF16 bit patterns (row stride may
+    exceed K).  Returns (codes uint8 [M, K/2 or K], scales uint8 [M, K/bs]).
+    Pre-filled ``codes``/``scales`` may be passed (their bytes outside the
+    written area are left alone)."""
+    lib = _load()
+    bs = BLOCK[fmt] if bs is None else bs
+    assert x_bits.dtype == np.uint16 and x_bits.ndim == 2 and x_bits.strides[1] == 2
+    M, K = x_bits.shape
+    ldx = _ld(x_bits, 2)
+    if codes is None:
+        codes = np.zeros((M, code_width(fmt, K)), np.uint8)
+    if scales is None:
+        scales = np.zeros((M, K // bs), np.uint8)
+    assert codes.dtype == np.uint8 and codes.strides[1] == 1 and codes.shape[0] >= M
+    assert scales.dtype == np.uint8 and scales.strides[1] == 1 and scales.shape[0] >= M
+    rc = lib.oracle_quantize(fmt, bs, _ptr(x_bits), M, K, ldx, _ptr(codes), _ld(codes, 1),
+                             _ptr(scales), _ld(scales, 1), float(np.float32(tensor_sf)),
+                             nthreads)
+    if rc != 0:
+        raise ValueError("oracle_quantize rejected its arguments")
+    return codes, scales
+
+
+def grouped_quantize(x_bits, fmt, row_offsets, scales_offsets, expert_ids, tensor_sf,
+                     max_rows, num_scale_rows, row_indices=None, codes=None, scales=None,
+                     bs=None, nthreads=1):
+    """Grouped per-expert form.  Returns (codes [max_rows, ...], scales
+    [num_scale_rows, K/bs]); rows no group owns keep their prior bytes (zero
+    unless pre-filled buffers are passed)."""
+    lib = _load()
+    bs = BLOCK[fmt] if bs is None else bs
+    assert x_bits.dtype == np.uint16 and x_bits.ndim == 2 and x_bits.strides[1] == 2
+    S, K = x_bits.shape
+    row_offsets = np.ascontiguousarray(row_offsets, np.uint32)
+    scales_offsets = np.ascontiguousarray(scales_offsets, np.uint32)
+    expert_ids = np.ascontiguousarray(expert_ids, np.int32)
+    G = expert_ids.shape[0]
+    assert row_offsets.shape[0] == G + 1 and scales_offsets.shape[0] == G + 1
+    sf = None if tensor_sf is None else np.ascontiguousarray(tensor_sf, np.float32)
+    E = 0 if sf is None else sf.shape[0]
+    ri = None if row_indices is None else np.ascontiguousarray(row_indices, np.int32)
+    if codes is None:
+        codes = np.zeros((max_rows, code_width(fmt, K)), np.uint8)
+    if scales is None:
+        scales = np.zeros((num_scale_rows, K // bs), np.uint8)
+    e_bound = E if sf is not None else 2**31 - 1  # MX formats read no per-expert scale
+    bad = lib.oracle_validate_grouped(_ptr(row_offsets), _ptr(scales_offsets), _ptr(expert_ids),
+                                      _ptr(ri), G, e_bound, max_rows, num_scale_rows, S)
+    if bad:
+        raise ValueError(f"grouped preconditions violated (check {bad})")
+    rc = lib.oracle_grouped_quantize(fmt, bs, _ptr(x_bits), S, K, _ld(x_bits, 2),
+                                     _ptr(ri), _ptr(row_offsets), _ptr(scales_offsets),
+                                     _ptr(expert_ids), _ptr(sf), G, E, _ptr(codes),
+                                     _ld(codes, 1), _ptr(scales), _ld(scales, 1), nthreads)
+    if rc != 0:
+        raise ValueError("oracle_grouped_quantize rejected its arguments")
+    return codes, scales
+
+
+def dequantize(codes, scales, fmt, K, tensor_sf=1.0, bs=None):
+    """Decode codes and block scales into float64 [M, K] (exact products)."""
+    lib = _load()
+    bs = BLOCK[fmt] if bs is None else bs
+    M = codes.shape[0]
+    out = np.empty((M, K), np.float64)
+    rc = lib.oracle_dequantize(fmt, bs, _ptr(codes), M, K, _ld(codes, 1), _ptr(scales),
+                               _ld(scales, 1), float(np.float32(tensor_sf)), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_dequantize rejected its arguments")
+    return out
+
+
+def e2m1_code(v: float) -> int:
+    return _load().oracle_e2m1_code(float(v))
+
+
+def e4m3_code(v: float) -> int:
+    return _load().oracle_e4m3_code(float(v))
+
+
+def e2m1_decode(c: int) -> float:
+    return _load().oracle_e2m1_decode(int(c))
+
+
+def e4m3_decode(c: int) -> float:
+    return _load().oracle_e4m3_decode(int(c))
+
+
+def e8m0_decode(b: int) -> float:
+    return _load().oracle_e8m0_decode(int(b))
+
+
+def bf16_decode(h: int) -> float:
+    return _load().oracle_bf16_decode(int(h))
