@@ -1,0 +1,163 @@
+"""Python binding of libbsq: block-scaled quantization of BF16 activations to
+MXFP4, MXFP8 and NVFP4 on AMD Instinct MI355X (gfx950).
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of ``libbsq.so``; torch provides device memory (``torch.empty``),
+pointers (``data_ptr``) and the current stream.  There is no CPU fallback:
+if the library is not built, importing this package raises ``ImportError``.
+
+The two entry points carry the names of the C ABI (``include/bsq.h``), the
+MI355X counterparts of the launchers on the Modular
+"block_scaled_quantization" module page; the grouped arguments follow the
+"grouped_quantize_dynamic_scaled_fp4_async_kernel" page (uint32 row_offsets
+and scales_offsets, int32 expert_ids, fp32 per-expert scale, optional int32
+row_indices).
+"""
+import ctypes
+import os
+
+import torch
+
+MXFP4, MXFP8, NVFP4 = 0, 1, 2
+BLOCK_SIZE = {MXFP4: 32, MXFP8: 32, NVFP4: 16}
+SCALES_ROW_MAJOR = 0
+FORMAT_NAMES = {"mxfp4": MXFP4, "mxfp8": MXFP8, "nvfp4": NVFP4}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run fp8_quantization_amd/build.py "
+                      "(or __graft_entry__.build()) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_i64, _i32, _p, _f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_float
+_lib.quantize_block_scaled.argtypes = [_i32, _i32, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _i64,
+                                       _f32, _p]
+_lib.quantize_block_scaled.restype = _i32
+_lib.grouped_quantize_block_scaled.argtypes = [_i32, _i32, _i32, _p, _i64, _i64, _i64, _p, _p, _p,
+                                               _p, _p, _i64, _i64, _i64, _i64, _p, _i64, _p, _i64,
+                                               _p]
+_lib.grouped_quantize_block_scaled.restype = _i32
+_lib.bsq_last_error.argtypes = []
+_lib.bsq_last_error.restype = ctypes.c_char_p
+_lib.bsq_version.argtypes = []
+_lib.bsq_version.restype = ctypes.c_char_p
+
+STATUS = {0: "BSQ_OK", 1: "BSQ_ERR_INVALID_ARG", 2: "BSQ_ERR_UNSUPPORTED", 3: "BSQ_ERR_HIP"}
+
+
+class BsqError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded ``libbsq.so`` (for callers that want the raw C ABI)."""
+    return _lib
+
+
+def version() -> str:
+    return _lib.bsq_version().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise BsqError(status, _lib.bsq_last_error().decode())
+
+
+def _fmt(fmt) -> int:
+    return FORMAT_NAMES[fmt.lower()] if isinstance(fmt, str) else int(fmt)
+
+
+def code_width(fmt, K: int) -> int:
+    """Bytes of codes per row: K/2 (FP4, two per byte) or K (FP8)."""
+    return K if _fmt(fmt) == MXFP8 else K // 2
+
+
+def _stream_ptr(stream, device):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _ld(t: torch.Tensor) -> int:
+    return t.stride(0) if t.dim() == 2 and t.shape[0] > 1 else t.shape[-1]
+
+
+def _as_bf16_matrix(x: torch.Tensor) -> torch.Tensor:
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"x must hold BF16 values (bfloat16/int16/uint16), got {x.dtype}")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D row-major tensor with unit column stride")
+    if not x.is_cuda:
+        raise ValueError("x must be a GPU tensor")
+    return x
+
+
+def quantize_block_scaled(x: torch.Tensor, fmt, tensor_sf: float = 1.0, codes=None, scales=None,
+                          stream=None):
+    """Dense form.  x: BF16 [M, K] on the GPU.  Returns (codes, scales):
+    uint8 [M, K/2] (FP4) or [M, K] (FP8), and uint8 [M, K/block_size].
+    ``tensor_sf`` is the fp32 NVFP4 tensor scale (ignored for MX).  Output
+    tensors may be passed in (any row stride the C ABI accepts)."""
+    f = _fmt(fmt)
+    x = _as_bf16_matrix(x)
+    M, K = x.shape
+    bs = BLOCK_SIZE.get(f, 0)
+    if codes is None:
+        codes = torch.empty((M, code_width(f, K) if bs else 0), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M, K // bs if bs else 0), dtype=torch.uint8, device=x.device)
+    _check(_lib.quantize_block_scaled(f, bs, SCALES_ROW_MAJOR, _ptr(x), M, K, _ld(x), _ptr(codes),
+                                      _ld(codes), _ptr(scales), _ld(scales),
+                                      float(tensor_sf), _stream_ptr(stream, x.device)))
+    return codes, scales
+
+
+def grouped_quantize_block_scaled(x: torch.Tensor, fmt, row_offsets: torch.Tensor,
+                                  scales_offsets: torch.Tensor, expert_ids: torch.Tensor,
+                                  tensor_sf: torch.Tensor | None, max_rows: int,
+                                  num_scale_rows: int, row_indices: torch.Tensor | None = None,
+                                  codes=None, scales=None, stream=None):
+    """Grouped per-expert form.  x: BF16 [num_src_rows, K]; row_offsets /
+    scales_offsets: uint32 (or int32 bit-identical) [G+1]; expert_ids int32
+    [G]; tensor_sf fp32 [num_experts] (NVFP4) or None; row_indices int32
+    [max_rows] or None.  Returns (codes [max_rows, ...], scales
+    [num_scale_rows, K/bs]); bytes no group owns are left as they were (new
+    outputs are uninitialised there)."""
+    f = _fmt(fmt)
+    x = _as_bf16_matrix(x)
+    S, K = x.shape
+    bs = BLOCK_SIZE.get(f, 0)
+    for name, t, dt in (("row_offsets", row_offsets, (torch.uint32, torch.int32)),
+                        ("scales_offsets", scales_offsets, (torch.uint32, torch.int32)),
+                        ("expert_ids", expert_ids, (torch.int32,))):
+        if t.dtype not in dt or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous GPU tensor of dtype {dt}")
+    G = expert_ids.shape[0]
+    if row_offsets.shape[0] != G + 1 or scales_offsets.shape[0] != G + 1:
+        raise ValueError("row_offsets and scales_offsets must have num_groups + 1 entries")
+    E = 0
+    if tensor_sf is not None:
+        if tensor_sf.dtype != torch.float32 or not tensor_sf.is_cuda or not tensor_sf.is_contiguous():
+            raise TypeError("tensor_sf must be a contiguous float32 GPU tensor")
+        E = tensor_sf.shape[0]
+    if row_indices is not None:
+        if row_indices.dtype != torch.int32 or not row_indices.is_cuda or \
+                not row_indices.is_contiguous() or row_indices.shape[0] < max_rows:
+            raise TypeError("row_indices must be a contiguous int32 GPU tensor of >= max_rows")
+    if codes is None:
+        codes = torch.empty((max_rows, code_width(f, K) if bs else 0), dtype=torch.uint8,
+                            device=x.device)
+    if scales is None:
+        scales = torch.empty((num_scale_rows, K // bs if bs else 0), dtype=torch.uint8,
+                             device=x.device)
+    _check(_lib.grouped_quantize_block_scaled(
+        f, bs, SCALES_ROW_MAJOR, _ptr(x), S, K, _ld(x), _ptr(row_indices), _ptr(row_offsets),
+        _ptr(scales_offsets), _ptr(expert_ids), _ptr(tensor_sf), G, E, max_rows, num_scale_rows,
+        _ptr(codes), _ld(codes), _ptr(scales), _ld(scales), _stream_ptr(stream, x.device)))
+    return codes, scales

@@ -1,0 +1,250 @@
+// bsq_api.cpp -- the C ABI of libbsq (declared in include/bsq.h): argument
+// validation, launch geometry and error reporting.  Every check runs on the
+// host before any HIP call, so a rejected call touches neither the device nor
+// the HIP runtime.
+//
+// The entry points are the MI355X counterparts of the dispatcher and the
+// launchers on the Modular "block_scaled_quantization" module page
+// (quantize_dynamic_block_scaled, quantize_mx_amd,
+// grouped_quantize_dynamic_scaled_fp4_async); format and block width replace
+// the pages' compile-time output dtype and SF_VECTOR_SIZE parameter
+// ("quantize_dynamic_scaled_async_fp4_kernel", Parameters).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "bsq.h"
+#include "bsq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return BSQ_OK;
+}
+
+bool log_enabled() {
+    static const bool on = [] {
+        const char* v = std::getenv("BSQ_LOG");
+        return v && v[0] && std::strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+// Optional override of the chunks (512 elements) one wave quantizes, for
+// launch-shape sweeps.  0 = use the heuristic.
+int tile_override() {
+    static const int v = [] {
+        const char* s = std::getenv("BSQ_CHUNKS_PER_TILE");
+        return s ? std::atoi(s) : 0;
+    }();
+    return v;
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+const char* fmt_name(int f) {
+    return f == BSQ_MXFP4 ? "MXFP4" : f == BSQ_MXFP8 ? "MXFP8" : f == BSQ_NVFP4 ? "NVFP4" : "?";
+}
+
+int expected_block(int format) {
+    switch (format) {
+        case BSQ_MXFP4: return 32;
+        case BSQ_MXFP8: return 32;
+        case BSQ_NVFP4: return 16;
+        default: return -1;
+    }
+}
+
+// Checks shared by both forms.  rows is M (dense) or the source row count.
+int check_common(int format, int block_size, int scale_layout, const void* x, int64_t rows,
+                 int64_t K, int64_t ldx, const void* codes, int64_t ldq, const void* scales,
+                 int64_t lds, bool has_work) {
+    const int bs = expected_block(format);
+    if (bs < 0) return fail(BSQ_ERR_UNSUPPORTED, "unknown format %d", format);
+    if (block_size != bs)
+        return fail(BSQ_ERR_UNSUPPORTED, "%s uses %d-element blocks, got block_size=%d",
+                    fmt_name(format), bs, block_size);
+    if (scale_layout != BSQ_SCALES_ROW_MAJOR)
+        return fail(BSQ_ERR_UNSUPPORTED, "scale layout %d is not provided (only row-major = 0)",
+                    scale_layout);
+    if (rows < 0 || K < 0) return fail(BSQ_ERR_INVALID_ARG, "negative size (rows=%lld K=%lld)",
+                                       (long long)rows, (long long)K);
+    if (K % bs != 0)
+        return fail(BSQ_ERR_INVALID_ARG, "K=%lld is not a multiple of the block size %d",
+                    (long long)K, bs);
+    if (K > (int64_t(1) << 30)) return fail(BSQ_ERR_INVALID_ARG, "K=%lld too large", (long long)K);
+    if (!has_work) return BSQ_OK;
+    const int64_t code_row = (format == BSQ_MXFP8) ? K : K / 2;
+    const int code_align = (format == BSQ_MXFP8) ? 8 : 4;
+    if (!x || !codes || !scales)
+        return fail(BSQ_ERR_INVALID_ARG, "null pointer (x=%p codes=%p scales=%p)", x, codes,
+                    scales);
+    if (!aligned(x, 16)) return fail(BSQ_ERR_INVALID_ARG, "x must be 16-byte aligned");
+    if (ldx < K || ldx % 8 != 0)
+        return fail(BSQ_ERR_INVALID_ARG, "ldx=%lld must be >= K=%lld and a multiple of 8",
+                    (long long)ldx, (long long)K);
+    if (!aligned(codes, code_align))
+        return fail(BSQ_ERR_INVALID_ARG, "codes must be %d-byte aligned for %s", code_align,
+                    fmt_name(format));
+    if (ldq < code_row || ldq % code_align != 0)
+        return fail(BSQ_ERR_INVALID_ARG, "ldq=%lld must be >= %lld and a multiple of %d",
+                    (long long)ldq, (long long)code_row, code_align);
+    if (lds < K / bs)
+        return fail(BSQ_ERR_INVALID_ARG, "lds=%lld must be >= K/block_size=%lld", (long long)lds,
+                    (long long)(K / bs));
+    return BSQ_OK;
+}
+
+bool tsf_in_domain(float t) {
+    // s * tsf must be a normal fp32 (or zero) for every E4M3 s, and its
+    // reciprocal finite: 2^-9 * tsf >= 2^-126 and 448 * tsf < 2^127 hold on
+    // [2^-117, 2^100].
+    return std::isfinite(t) && t >= std::ldexp(1.0f, -117) && t <= std::ldexp(1.0f, 100);
+}
+
+// Launch geometry: chunks of 512 elements per wave.  Start from 8 chunks
+// (4 KiB of BF16 per lane-row, two load batches) and split rows further while
+// the grid would hold fewer than 2048 waves (8 per CU), so small problems
+// still spread over the chip.  The tile is balanced across the row.
+void choose_tiles(int64_t rows, int chunks_per_row, int* chunks_per_tile, int* tiles_per_row) {
+    int target = 8;
+    if (tile_override() > 0) {
+        target = tile_override();
+    } else {
+        while (target > 1 && rows * ((chunks_per_row + target - 1) / target) < 2048) target /= 2;
+    }
+    int tiles = (chunks_per_row + target - 1) / target;
+    if (tiles < 1) tiles = 1;
+    *tiles_per_row = tiles;
+    *chunks_per_tile = (chunks_per_row + tiles - 1) / tiles;
+}
+
+int launch(int format, bool grouped, bsq::KernelArgs& a, hipStream_t stream) {
+    a.chunks_per_row = (int32_t)((a.K + bsq::kChunkElems - 1) / bsq::kChunkElems);
+    choose_tiles(a.rows, a.chunks_per_row, &a.chunks_per_tile, &a.tiles_per_row);
+    const int64_t waves = a.rows * a.tiles_per_row;
+    const int64_t blocks = (waves + bsq::kWavesPerBlock - 1) / bsq::kWavesPerBlock;
+    if (blocks > 0x7FFFFFFFLL)
+        return fail(BSQ_ERR_INVALID_ARG, "problem too large for one launch (%lld blocks)",
+                    (long long)blocks);
+    if (log_enabled())
+        std::fprintf(stderr,
+                     "[bsq] %s %s rows=%lld K=%d chunks/row=%d chunks/tile=%d tiles/row=%d "
+                     "blocks=%lld\n",
+                     grouped ? "grouped" : "dense", fmt_name(format), (long long)a.rows, a.K,
+                     a.chunks_per_row, a.chunks_per_tile, a.tiles_per_row, (long long)blocks);
+    const hipError_t e = bsq::launch_quantize(format, grouped, a, blocks, stream);
+    if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int quantize_block_scaled(int format, int block_size, int scale_layout, const void* x,
+                          int64_t M, int64_t K, int64_t ldx, void* codes, int64_t ldq,
+                          void* scales, int64_t lds, float tensor_sf, void* stream) {
+    const bool work = M > 0 && K > 0;
+    int st = check_common(format, block_size, scale_layout, x, M, K, ldx, codes, ldq, scales, lds,
+                          work);
+    if (st != BSQ_OK) return st;
+    if (format == BSQ_NVFP4 && !tsf_in_domain(tensor_sf))
+        return fail(BSQ_ERR_INVALID_ARG,
+                    "tensor_sf=%g must be finite and within [2^-117, 2^100]", (double)tensor_sf);
+    if (!work) return ok();
+    bsq::KernelArgs a{};
+    a.x = static_cast<const uint16_t*>(x);
+    a.ldx = ldx;
+    a.codes = static_cast<uint8_t*>(codes);
+    a.ldq = ldq;
+    a.scales = static_cast<uint8_t*>(scales);
+    a.lds = lds;
+    a.rows = M;
+    a.K = (int32_t)K;
+    a.tensor_sf = tensor_sf;
+    return launch(format, false, a, static_cast<hipStream_t>(stream));
+}
+
+int grouped_quantize_block_scaled(int format, int block_size, int scale_layout, const void* x,
+                                  int64_t num_src_rows, int64_t K, int64_t ldx,
+                                  const int32_t* row_indices, const uint32_t* row_offsets,
+                                  const uint32_t* scales_offsets, const int32_t* expert_ids,
+                                  const float* tensor_sf, int64_t num_groups,
+                                  int64_t num_experts, int64_t max_rows, int64_t num_scale_rows,
+                                  void* codes, int64_t ldq, void* scales, int64_t lds,
+                                  void* stream) {
+    if (num_groups < 0 || max_rows < 0 || num_scale_rows < 0 || num_experts < 0)
+        return fail(BSQ_ERR_INVALID_ARG,
+                    "negative size (num_groups=%lld max_rows=%lld num_scale_rows=%lld "
+                    "num_experts=%lld)",
+                    (long long)num_groups, (long long)max_rows, (long long)num_scale_rows,
+                    (long long)num_experts);
+    const bool work = num_groups > 0 && max_rows > 0 && K > 0;
+    int st = check_common(format, block_size, scale_layout, x, num_src_rows, K, ldx, codes, ldq,
+                          scales, lds, work);
+    if (st != BSQ_OK) return st;
+    if (!work) return ok();
+    if (num_groups > 0x7FFFFFFFLL - 64)
+        return fail(BSQ_ERR_INVALID_ARG, "num_groups=%lld too large", (long long)num_groups);
+    if (max_rows > (int64_t(1) << 32))
+        return fail(BSQ_ERR_INVALID_ARG, "max_rows=%lld exceeds the uint32 offset range",
+                    (long long)max_rows);
+    if (!row_offsets || !scales_offsets)
+        return fail(BSQ_ERR_INVALID_ARG, "row_offsets and scales_offsets are required");
+    if (!row_indices && max_rows > num_src_rows)
+        return fail(BSQ_ERR_INVALID_ARG,
+                    "without row_indices, max_rows=%lld may not exceed num_src_rows=%lld",
+                    (long long)max_rows, (long long)num_src_rows);
+    if (row_indices && num_src_rows == 0)
+        return fail(BSQ_ERR_INVALID_ARG, "row_indices given but x has no rows");
+    if (format == BSQ_NVFP4) {
+        if (!expert_ids || !tensor_sf || num_experts < 1 || num_experts > 0x7FFFFFFFLL)
+            return fail(BSQ_ERR_INVALID_ARG,
+                        "NVFP4 needs expert_ids, a per-expert tensor_sf and num_experts >= 1");
+    }
+    bsq::KernelArgs a{};
+    a.x = static_cast<const uint16_t*>(x);
+    a.ldx = ldx;
+    a.codes = static_cast<uint8_t*>(codes);
+    a.ldq = ldq;
+    a.scales = static_cast<uint8_t*>(scales);
+    a.lds = lds;
+    a.rows = max_rows;
+    a.K = (int32_t)K;
+    a.tensor_sf = 1.0f;
+    a.row_indices = row_indices;
+    a.row_offsets = row_offsets;
+    a.scales_offsets = scales_offsets;
+    a.expert_ids = expert_ids;
+    a.expert_sf = tensor_sf;
+    a.num_src_rows = num_src_rows;
+    a.num_scale_rows = num_scale_rows;
+    a.num_groups = (int32_t)num_groups;
+    a.num_experts = (int32_t)num_experts;
+    return launch(format, true, a, static_cast<hipStream_t>(stream));
+}
+
+const char* bsq_last_error(void) { return g_last_error.c_str(); }
+
+const char* bsq_version(void) { return "1.0.0"; }
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// bsq_internal.h -- launch interface between the C-ABI host layer
+// (bsq_api.cpp) and the gfx950 kernels (bsq_kernels.hip).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsq {
+
+// One wave quantizes a "tile": up to chunks_per_tile consecutive chunks of
+// one row, a chunk being 512 BF16 elements (64 lanes x one 16-byte load).
+constexpr int kWaveSize = 64;
+constexpr int kWavesPerBlock = 4;
+constexpr int kThreadsPerBlock = kWaveSize * kWavesPerBlock;
+constexpr int kElemsPerLane = 8;
+constexpr int kChunkElems = kWaveSize * kElemsPerLane;
+
+struct KernelArgs {
+    const uint16_t* x;            // BF16 source rows
+    int64_t ldx;                  // elements
+    uint8_t* codes;
+    int64_t ldq;                  // bytes
+    uint8_t* scales;
+    int64_t lds;                  // bytes
+    int64_t rows;                 // dense: M; grouped: max_rows (routed rows)
+    int32_t K;
+    int32_t chunks_per_row;       // ceil(K / 512)
+    int32_t chunks_per_tile;
+    int32_t tiles_per_row;
+    float tensor_sf;              // dense NVFP4
+
+    // grouped form only
+    const int32_t* row_indices;   // nullable
+    const uint32_t* row_offsets;  // [G + 1]
+    const uint32_t* scales_offsets;
+    const int32_t* expert_ids;
+    const float* expert_sf;       // [num_experts] (NVFP4)
+    int64_t num_src_rows;
+    int64_t num_scale_rows;
+    int32_t num_groups;
+    int32_t num_experts;
+};
+
+// Launch the dense (grouped = false) or grouped kernel for format fmt
+// (0 MXFP4, 1 MXFP8, 2 NVFP4).  Returns the launch status.
+hipError_t launch_quantize(int fmt, bool grouped, const KernelArgs& a, int64_t blocks,
+                           hipStream_t stream);
+
+}  // namespace bsq

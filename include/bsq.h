@@ -1,0 +1,156 @@
+/*
+ * bsq.h -- C ABI of libbsq, dynamic block-scaled quantization of BF16
+ * activations to MXFP4, MXFP8 and NVFP4 on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one listed on the Modular "block_scaled_quantization"
+ * module page: block-scaled quantization kernels for NVFP4, MXFP4 and MXFP8,
+ * reached through a dispatcher (function list: quantize_dynamic_block_scaled,
+ * quantize_dynamic_scaled_fp4fp8, quantize_mx_amd for AMD CDNA4).  The dense
+ * NVFP4 arguments (a scalar fp32 tensor scale) and the number of elements per
+ * block scale come from the "quantize_dynamic_scaled_async_fp4_kernel" page
+ * (signature; Parameters: SF_VECTOR_SIZE).  The grouped per-expert arguments
+ * (row_offsets and scales_offsets uint32, expert_ids int32, per-expert fp32
+ * tensor scale, optional int32 row_indices gather) come from the
+ * "grouped_quantize_dynamic_scaled_fp4_async_kernel" page (signature,
+ * summary and Parameters).
+ *
+ * Formats and rules (the pages name the formats but define none of them):
+ *   MXFP4  E2M1 codes, 2 per byte, 32-element blocks, E8M0 scale byte.
+ *   MXFP8  E4M3 (FN) codes, 1 per byte, 32-element blocks, E8M0 scale byte.
+ *   NVFP4  E2M1 codes, 2 per byte, 16-element blocks, E4M3 scale byte under
+ *          an fp32 tensor scale tsf (decode: value = code * s * tsf).
+ *   MX scale: X = max(floor(log2 amax) - emax, -127), emax = 2 (E2M1) or
+ *          8 (E4M3); scale byte X + 127; code = RNE with saturation of
+ *          x * 2^-X (OCP MX v1.0).
+ *   NVFP4 scale: s = RNE_sat_E4M3(fl32(fl32(amax / 6) / tsf));
+ *          inv = 0 if fl32(s * tsf) == 0 else fl32(1 / fl32(s * tsf));
+ *          code = RNE_sat_E2M1(fl32(x * inv)).
+ *   A block holding a NaN or Inf gets the NaN scale (0xFF for E8M0, 0x7F
+ *          for E4M3) and all-zero codes.  Codes keep the sign bit of x, so
+ *          -0 encodes as 0x8 (FP4) or 0x80 (FP8).  No subnormal is flushed.
+ *   FP4 packing: element 2j in the low nibble of byte j, 2j+1 in the high.
+ *   Blocks run along K, the contiguous dimension.
+ *
+ * Conventions for every entry point:
+ *   - All pointers are device memory owned by the caller.  The library
+ *     allocates nothing and keeps no device state.
+ *   - The call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  Outputs are valid once the stream has been synchronised.
+ *     Calls are thread-safe.
+ *   - Arguments are validated on the host before any HIP call.  On failure
+ *     nothing is launched, the status is returned, and bsq_last_error()
+ *     describes it.  A launch failure returns BSQ_ERR_HIP.
+ *   - M == 0, K == 0 and (grouped) num_groups == 0 or max_rows == 0 are
+ *     no-ops that return BSQ_OK.
+ *   - Bytes of `codes` and `scales` outside what the call defines to write
+ *     are never touched.
+ */
+#ifndef BSQ_H
+#define BSQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum bsq_format { BSQ_MXFP4 = 0, BSQ_MXFP8 = 1, BSQ_NVFP4 = 2 };
+
+/* Scale layouts.  Only row-major scales exist in this version; any other
+   value is rejected with BSQ_ERR_UNSUPPORTED. */
+enum bsq_scale_layout { BSQ_SCALES_ROW_MAJOR = 0 };
+
+enum bsq_status {
+    BSQ_OK = 0,
+    BSQ_ERR_INVALID_ARG = 1, /* bad size, stride, alignment, pointer or scale */
+    BSQ_ERR_UNSUPPORTED = 2, /* (format, block_size) pair or layout not provided */
+    BSQ_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+};
+
+/*
+ * Dense form: quantize every row of a BF16 matrix.
+ *
+ *   format, block_size  (BSQ_MXFP4, 32), (BSQ_MXFP8, 32) or (BSQ_NVFP4, 16);
+ *                       any other pair -> BSQ_ERR_UNSUPPORTED.
+ *   scale_layout        BSQ_SCALES_ROW_MAJOR.
+ *   x                   BF16 [M, K], row-major, row stride ldx elements.
+ *                       16-byte aligned; ldx >= K and ldx % 8 == 0.
+ *   M, K                M >= 0, K >= 0, K % block_size == 0.
+ *   codes               uint8 [M, ldq]: row r holds K/2 bytes (FP4) or K
+ *                       bytes (FP8) of codes.  FP4: 4-byte aligned,
+ *                       ldq % 4 == 0, ldq >= K/2.  FP8: 8-byte aligned,
+ *                       ldq % 8 == 0, ldq >= K.
+ *   scales              uint8 [M, lds]: row r holds the K/block_size block
+ *                       scales of row r; lds >= K/block_size.
+ *   tensor_sf           NVFP4 only (ignored for MX): finite and within
+ *                       [2^-117, 2^100], so that s * tsf is a normal fp32 or
+ *                       zero and its reciprocal is finite; else
+ *                       BSQ_ERR_INVALID_ARG.
+ *   stream              hipStream_t or NULL.
+ *   Returns a bsq_status.
+ */
+int quantize_block_scaled(int format, int block_size, int scale_layout,
+                          const void* x, int64_t M, int64_t K, int64_t ldx,
+                          void* codes, int64_t ldq,
+                          void* scales, int64_t lds,
+                          float tensor_sf, void* stream);
+
+/*
+ * Grouped per-expert form (MoE).  Group g in [0, num_groups) owns the
+ * routed rows [row_offsets[g], row_offsets[g+1]).  Routed row r:
+ *   - reads source row row_indices[r] of x, or row r when row_indices is NULL;
+ *   - is quantized like a dense row, NVFP4 with tsf = tensor_sf[expert_ids[g]];
+ *   - writes its codes to row r of `codes` (routed order, unpadded);
+ *   - writes its scales to row scales_offsets[g] + (r - row_offsets[g]) of
+ *     `scales`.
+ * Rows no group owns, and scale rows between groups (padding), are not
+ * touched.  The group of r is found on the device (no host synchronisation):
+ * g is the last index with row_offsets[g] <= r, so empty groups (repeated
+ * offsets) are skipped.
+ *
+ *   x, num_src_rows, K, ldx   source BF16 rows, as for the dense form.
+ *   row_indices      int32 [max_rows] or NULL.  With NULL, max_rows must not
+ *                    exceed num_src_rows.
+ *   row_offsets      uint32 [num_groups + 1], nondecreasing,
+ *                    row_offsets[num_groups] <= max_rows.
+ *   scales_offsets   uint32 [num_groups + 1], nondecreasing, with
+ *                    scales_offsets[g+1] - scales_offsets[g] >= the rows of g.
+ *   expert_ids       int32 [num_groups], values in [0, num_experts).
+ *   tensor_sf        fp32 [num_experts] for NVFP4 (each value obeying the
+ *                    dense tensor_sf domain); ignored (may be NULL) for MX.
+ *   num_groups       >= 0.  num_experts >= 1 for NVFP4.
+ *   max_rows         host-side bound on routed rows; sizes the grid, so the
+ *                    device offsets are never read on the host.  <= 2^32.
+ *   num_scale_rows   rows in the scales buffer.
+ *   codes, ldq       uint8 [max_rows, ldq], as for the dense form.
+ *   scales, lds      uint8 [num_scale_rows, lds].
+ * The device-array contents above are preconditions and are not checked on
+ * the host.  The kernels still never access memory outside the buffers the
+ * sizes describe: a routed row whose group, source row, expert id or scale
+ * row falls outside them is skipped.
+ */
+int grouped_quantize_block_scaled(int format, int block_size, int scale_layout,
+                                  const void* x, int64_t num_src_rows, int64_t K, int64_t ldx,
+                                  const int32_t* row_indices,
+                                  const uint32_t* row_offsets,
+                                  const uint32_t* scales_offsets,
+                                  const int32_t* expert_ids,
+                                  const float* tensor_sf,
+                                  int64_t num_groups, int64_t num_experts,
+                                  int64_t max_rows, int64_t num_scale_rows,
+                                  void* codes, int64_t ldq,
+                                  void* scales, int64_t lds,
+                                  void* stream);
+
+/* Message for the last non-OK status returned on the calling thread ("" if
+   none).  The pointer stays valid until the next call on that thread. */
+const char* bsq_last_error(void);
+
+/* Library version, e.g. "1.0.0". */
+const char* bsq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSQ_H */

@@ -1,0 +1,161 @@
+"""Host-side checks of the C ABI that need no GPU.
+
+The library loads, exports every function ``include/bsq.h`` declares, and
+rejects bad arguments on the host before any HIP call (those paths return
+without touching the runtime, so they run on a machine with no GPU).  The
+pointers passed here are never dereferenced: every call below fails
+validation or is a no-op.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsq.h")
+LIB = os.path.join(ROOT, "fp8_quantization_amd", "libbsq.so")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+MXFP4, MXFP8, NVFP4 = 0, 1, 2
+FAKE = 0x10000  # aligned, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from fp8_quantization_amd import build
+
+        build.build()
+    lib = ctypes.CDLL(LIB)
+    i64, i32, p = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    lib.quantize_block_scaled.argtypes = [i32, i32, i32, p, i64, i64, i64, p, i64, p, i64,
+                                          ctypes.c_float, p]
+    lib.grouped_quantize_block_scaled.argtypes = [i32, i32, i32, p, i64, i64, i64, p, p, p, p, p,
+                                                  i64, i64, i64, i64, p, i64, p, i64, p]
+    lib.bsq_last_error.restype = ctypes.c_char_p
+    lib.bsq_version.restype = ctypes.c_char_p
+    return lib
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(["quantize_block_scaled",
+                                           "grouped_quantize_block_scaled", "bsq_last_error",
+                                           "bsq_version"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.bsq_version().decode().count(".") == 2
+
+
+def dense(lib, fmt=MXFP4, bs=32, layout=0, x=FAKE, M=4, K=64, ldx=64, codes=FAKE, ldq=None,
+          scales=FAKE, lds=None, tsf=1.0):
+    if ldq is None:
+        ldq = K if fmt == MXFP8 else K // 2
+    if lds is None:
+        lds = K // bs if bs > 0 else 1
+    return lib.quantize_block_scaled(fmt, bs, layout, x, M, K, ldx, codes, ldq, scales, lds, tsf,
+                                     None)
+
+
+@pytest.mark.parametrize("fmt,bs", [(MXFP4, 16), (MXFP8, 16), (NVFP4, 32), (3, 32), (-1, 32),
+                                    (MXFP4, 0)])
+def test_unsupported_pairs(lib, fmt, bs):
+    assert dense(lib, fmt=fmt, bs=bs) == UNSUPPORTED
+    assert lib.bsq_last_error()
+
+
+def test_unsupported_layout(lib):
+    assert dense(lib, layout=1) == UNSUPPORTED
+    assert b"layout" in lib.bsq_last_error()
+
+
+@pytest.mark.parametrize("kw", [
+    dict(M=-1), dict(K=-32), dict(K=48, ldx=48),                 # negative, K % bs
+    dict(x=None), dict(codes=None), dict(scales=None),           # null pointers
+    dict(x=FAKE + 8), dict(ldx=60), dict(ldx=32),                # x alignment, ldx
+    dict(codes=FAKE + 2), dict(ldq=30), dict(ldq=34),            # FP4 codes
+    dict(lds=1),                                                 # scale row too short
+], ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_invalid_dense_args(lib, kw):
+    assert dense(lib, **kw) == INVALID
+    assert lib.bsq_last_error()
+
+
+def test_fp8_code_alignment(lib):
+    assert dense(lib, fmt=MXFP8, codes=FAKE + 4) == INVALID
+    assert dense(lib, fmt=MXFP8, ldq=68) == INVALID
+
+
+@pytest.mark.parametrize("tsf", [0.0, -1.0, float("inf"), float("nan"), 2.0 ** -118, 2.0 ** 101])
+def test_nvfp4_tensor_scale_domain(lib, tsf):
+    assert dense(lib, fmt=NVFP4, bs=16, tsf=tsf) == INVALID
+    assert b"tensor_sf" in lib.bsq_last_error()
+
+
+def test_noops_touch_nothing(lib):
+    # M == 0 or K == 0 with null pointers: nothing to do, nothing launched
+    assert dense(lib, M=0, x=None, codes=None, scales=None) == OK
+    assert dense(lib, K=0, ldx=0, x=None, codes=None, scales=None, ldq=0, lds=0) == OK
+    assert lib.bsq_last_error() == b""
+
+
+def grouped(lib, fmt=MXFP4, bs=32, S=8, K=64, ri=None, ro=FAKE, so=FAKE, ids=FAKE, sf=None,
+            G=2, E=0, max_rows=8, nsr=8, x=FAKE, codes=FAKE, scales=FAKE):
+    ldq = K if fmt == MXFP8 else K // 2
+    return lib.grouped_quantize_block_scaled(fmt, bs, 0, x, S, K, K, ri, ro, so, ids, sf, G, E,
+                                             max_rows, nsr, codes, ldq, scales, K // bs, None)
+
+
+def test_grouped_validation(lib):
+    assert grouped(lib, G=-1) == INVALID
+    assert grouped(lib, max_rows=-1) == INVALID
+    assert grouped(lib, ro=None) == INVALID
+    assert grouped(lib, so=None) == INVALID
+    assert grouped(lib, max_rows=9) == INVALID                 # no gather: max_rows > S
+    assert grouped(lib, fmt=NVFP4, bs=16) == INVALID           # NVFP4 without sf / experts
+    assert grouped(lib, fmt=NVFP4, bs=16, sf=FAKE, E=0) == INVALID
+    assert grouped(lib, fmt=NVFP4, bs=16, sf=FAKE, E=4, ids=None) == INVALID
+    assert grouped(lib, max_rows=(1 << 32) + 1, ri=FAKE) == INVALID
+    assert grouped(lib, bs=16) == UNSUPPORTED
+    assert grouped(lib, G=0, ro=None, so=None) == OK           # no groups: no-op
+    assert grouped(lib, max_rows=0) == OK
+
+
+def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    """The binding has no CPU fallback: with the library missing, import raises."""
+    import importlib.util
+
+    src = os.path.join(ROOT, "fp8_quantization_amd", "__init__.py")
+    pkg = tmp_path / "fp8_quantization_amd"
+    pkg.mkdir()
+    (pkg / "__init__.py").write_text(open(src).read())
+    spec = importlib.util.spec_from_file_location("bsq_nolib", pkg / "__init__.py")
+    mod = importlib.util.module_from_spec(spec)
+    with pytest.raises(ImportError):
+        spec.loader.exec_module(mod)
+
+
+def test_oracle_and_product_share_no_code():
+    """Neither side imports, includes or links the other."""
+    prod = os.path.join(ROOT, "fp8_quantization_amd")
+    for dirpath, _, files in os.walk(prod):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                for bad in ("import oracle", "from oracle", "liboracle", "oracle.c", "spec.py"):
+                    assert bad not in text, (f, bad)
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith((".py", ".c", ".h")):
+            text = open(os.path.join(ROOT, "oracle", f)).read()
+            for bad in ("import fp8_quantization_amd", "from fp8_quantization_amd", "bsq.h",
+                        "libbsq", "bsq_internal"):
+                assert bad not in text, (f, bad)

@@ -37,10 +37,13 @@ def bf16_to_f32(h: np.ndarray) -> np.ndarray:
 
 
 def amax_of(h: np.ndarray) -> np.float32:
-    """Largest |value| of finite BF16 patterns, as float32 (exact)."""
-    if h.size == 0:
+    """Largest |value| over the finite BF16 patterns (NaN/Inf skipped), as
+    float32 (exact)."""
+    mag = np.asarray(h) & np.uint16(0x7FFF)
+    mag = mag[mag < np.uint16(0x7F80)]
+    if mag.size == 0:
         return np.float32(0.0)
-    return np.float32(bf16_to_f32(np.asarray(h) & np.uint16(0x7FFF)).max())
+    return np.float32(bf16_to_f32(mag).max())
 
 
 def tensor_scale(h: np.ndarray) -> np.float32:
