@@ -1,0 +1,331 @@
+#!/usr/bin/env python3
+"""Throughput of dynamic block-scaled quantization on one MI355X.
+
+Headline: dense BF16 -> MXFP8 quantization of an [8192, 7168] activation
+matrix (N(0, 1) rows scaled by 2^U(-8, 8), 0.1% outliers x100), block 32, E8M0
+scales.  One step = one call of the whole hot path (load, block amax, scale,
+quantize, pack, store codes and scales) over that matrix.  Metric: achieved
+HBM GB/s counting algorithmic bytes (BF16 read + codes + scales written), as a
+fraction of the 8 TB/s HBM3E peak.
+
+Protocol: inputs are resident in HBM before timing starts.  The timed loop
+rotates over several copies of the input/output buffers whose combined size is
+well above the 256 MB last-level (MALL) cache, so each step streams from HBM
+(no warm-cache reuse).  Each launch is bracketed by HIP events on the stream
+it runs on; the roofline figure uses their mean, the headline ``value`` the
+wall clock of the whole timed loop.  The CPU oracle is timed on a bounded
+sample of the same workload on the host's cores (``cpu_baseline``), and its
+output doubles as a parity check of that sample.
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+       [--workload dense_mxfp8] [--no-secondary] [--no-cpu-baseline]
+       python bench.py --copy-bytes N   (plain copy kernel, for counter calibration)
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 << 20
+METRIC = "achieved HBM GB/s (% of 8 TB/s) for BF16→MXFP4/MXFP8/NVFP4 quant, 1 GPU"
+KERNEL_SRC = os.path.join(ROOT, "fp8_quantization_amd", "csrc", "bsq_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ workloads
+
+def load_workload(name):
+    import workloads as W
+    table = {
+        "dense_mxfp4": W.dense_mxfp4_small,
+        "dense_mxfp8": W.dense_mxfp8_scaled_rows,
+        "dense_nvfp4": W.dense_nvfp4_scaled_rows,
+        "grouped_nvfp4": W.grouped_nvfp4_prefill,
+        "grouped_mxfp4_decode": lambda: W.grouped_mx_decode(W.MXFP4),
+        "grouped_mxfp8_decode": lambda: W.grouped_mx_decode(W.MXFP8),
+    }
+    return table[name]()
+
+
+def bytes_per_element(fmt):
+    """BF16 read (2) + code bytes (1/2 or 1) + one scale byte per block."""
+    bs = 16 if fmt == 2 else 32
+    return 2.0 + (1.0 if fmt == 1 else 0.5) + 1.0 / bs
+
+
+def algorithmic_bytes(case):
+    """Bytes one launch must move at minimum (read + written)."""
+    import workloads as W
+    if isinstance(case, W.DenseCase):
+        M, K = case.x.shape
+        return int(M * K * bytes_per_element(case.fmt)), M * K
+    K = case.x.shape[1]
+    routed = int(case.row_offsets[-1]) - int(case.row_offsets[0])
+    fmt = case.fmt
+    out = routed * K * (bytes_per_element(fmt) - 2.0)
+    if case.row_indices is None:
+        src_read = routed * K * 2
+    else:  # each distinct source row must be read once
+        used = np.unique(case.row_indices[int(case.row_offsets[0]):int(case.row_offsets[-1])])
+        src_read = used.size * K * 2
+    meta = (case.row_offsets.size + case.scales_offsets.size + case.expert_ids.size) * 4
+    if case.tensor_sf is not None:
+        meta += case.tensor_sf.size * 4
+    if case.row_indices is not None:
+        meta += routed * 4
+    return int(src_read + out + meta), routed * K
+
+
+class Runner:
+    """Holds NB resident copies of one workload's buffers and launches one
+    step on copy i."""
+
+    def __init__(self, case, nb):
+        import torch
+
+        import fp8_quantization_amd as bsq
+        import workloads as W
+        self.bsq, self.torch, self.case = bsq, torch, case
+        self.grouped = not isinstance(case, W.DenseCase)
+        xd = torch.from_numpy(np.ascontiguousarray(case.x).view(np.int16)).cuda()
+        K = case.x.shape[1]
+        bs = bsq.BLOCK_SIZE[case.fmt]
+        self.sets = []
+        for i in range(nb):
+            s = {"x": xd if i == 0 else xd.clone()}
+            if self.grouped:
+                t = lambda a, dt: None if a is None else torch.from_numpy(
+                    np.ascontiguousarray(a).view(dt)).cuda()
+                s["ro"] = t(case.row_offsets, np.int32)
+                s["so"] = t(case.scales_offsets, np.int32)
+                s["ids"] = t(case.expert_ids, np.int32)
+                s["sf"] = t(case.tensor_sf, np.float32)
+                s["ri"] = t(case.row_indices, np.int32)
+                s["q"] = torch.empty((case.max_rows, bsq.code_width(case.fmt, K)),
+                                     dtype=torch.uint8, device="cuda")
+                s["s"] = torch.empty((case.num_scale_rows, K // bs), dtype=torch.uint8,
+                                     device="cuda")
+            else:
+                M = case.x.shape[0]
+                s["q"] = torch.empty((M, bsq.code_width(case.fmt, K)), dtype=torch.uint8,
+                                     device="cuda")
+                s["s"] = torch.empty((M, K // bs), dtype=torch.uint8, device="cuda")
+            self.sets.append(s)
+        torch.cuda.synchronize()
+
+    def step(self, i):
+        s = self.sets[i % len(self.sets)]
+        c = self.case
+        if self.grouped:
+            self.bsq.grouped_quantize_block_scaled(
+                s["x"], c.fmt, s["ro"], s["so"], s["ids"], s["sf"], c.max_rows,
+                c.num_scale_rows, row_indices=s["ri"], codes=s["q"], scales=s["s"])
+        else:
+            self.bsq.quantize_block_scaled(s["x"], c.fmt, c.tensor_sf, codes=s["q"],
+                                           scales=s["s"])
+
+
+def time_steps(runner, steps, warmup):
+    """Wall time of `steps` launches plus per-launch event durations."""
+    torch = runner.torch
+    for i in range(warmup):
+        runner.step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        runner.step(warmup + i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    return wall, kern_ms
+
+
+def measure(name, steps, warmup, rotate=True):
+    case = load_workload(name)
+    nbytes, elems = algorithmic_bytes(case)
+    nb = max(2, -(-3 * MALL_BYTES // max(nbytes, 1)) + 1) if rotate else 1
+    nb = min(nb, 64)
+    runner = Runner(case, nb)
+    wall, kern = time_steps(runner, steps, warmup)
+    return case, runner, nbytes, elems, nb, wall, kern
+
+
+def summary(name, nbytes, elems, wall, kern, steps, nb):
+    k_mean = float(kern.mean()) * 1e-3
+    return {
+        "workload": name,
+        "bytes_per_launch": nbytes,
+        "elements": elems,
+        "buffer_sets": nb,
+        "kernel_us_mean": round(k_mean * 1e6, 3),
+        "kernel_us_p10": round(float(np.percentile(kern, 10)) * 1e3, 3),
+        "kernel_us_p90": round(float(np.percentile(kern, 90)) * 1e3, 3),
+        "kernel_GBps": round(nbytes / k_mean / 1e9, 1),
+        "kernel_frac_of_8TBps": round(nbytes / k_mean / 1e9 / PEAK_HBM_GBS, 4),
+        "Gelem_per_s": round(elems / k_mean / 1e9, 1),
+        "wall_GBps": round(nbytes * steps / wall / 1e9, 1),
+    }
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(case, runner, target_seconds=8.0):
+    """Time the oracle (as it stands) on the first rows of the same input on
+    the host's cores; check the GPU's output for those rows."""
+    import oracle
+    torch = runner.torch
+    threads = max(1, min(16, os.cpu_count() or 1))
+    M, K = case.x.shape
+    probe = min(M, 64)
+    t = time.perf_counter()
+    oracle.quantize(case.x[:probe], case.fmt, case.tensor_sf, nthreads=threads)
+    per_row = (time.perf_counter() - t) / probe
+    rows = int(min(M, max(probe, target_seconds / max(per_row, 1e-9))))
+    t = time.perf_counter()
+    qh, sh = oracle.quantize(case.x[:rows], case.fmt, case.tensor_sf, nthreads=threads)
+    dt = time.perf_counter() - t
+    nbytes = rows * K * bytes_per_element(case.fmt)
+    runner.step(0)
+    torch.cuda.synchronize()
+    s0 = runner.sets[0]
+    ok = bool(np.array_equal(s0["q"][:rows].cpu().numpy(), qh) and
+              np.array_equal(s0["s"][:rows].cpu().numpy(), sh))
+    return {
+        "value": round(nbytes / dt / 1e9, 3),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {rows} of {M} rows of the {case.name} input ({rows * K} elements, "
+                  f"{nbytes / 1e6:.1f} MB algorithmic), {dt:.2f} s wall on {threads} "
+                  f"thread(s)",
+        "parity_of_sample": "identical" if ok else "MISMATCH",
+    }
+
+
+def traffic_from_counters(nbytes_per_launch):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    counters, valid only while the kernel source is the one they were taken
+    on (sha256 recorded beside them)."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None, "no counter file"
+    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != sha:
+        return None, "kernel changed since the counters were taken"
+    return int(rec["hbm_bytes_per_launch"]), rec.get("note", "")
+
+
+# ------------------------------------------------------------------ main
+
+def copy_calibration(nbytes, steps):
+    import torch
+    n = nbytes // 4
+    a = torch.empty(n, dtype=torch.int32, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "steps": steps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dense_mxfp8")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would "
+              "quantize its own shard with no exchange); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes, args.steps)
+        return
+
+    import fp8_quantization_amd as bsq
+
+    case, runner, nbytes, elems, nb, wall, kern = measure(args.workload, args.steps, args.warmup)
+    head = summary(args.workload, nbytes, elems, wall, kern, args.steps, nb)
+    log("[bench] headline", json.dumps(head))
+    k_mean_s = float(kern.mean()) * 1e-3
+    achieved = nbytes / k_mean_s / 1e9
+    traffic, traffic_note = traffic_from_counters(nbytes)
+
+    secondary = []
+    if not args.no_secondary:
+        for name in ("dense_nvfp4", "grouped_nvfp4", "dense_mxfp4", "grouped_mxfp4_decode",
+                     "grouped_mxfp8_decode"):
+            if name == args.workload:
+                continue
+            c2, r2, nb2, el2, nbs2, w2, k2 = measure(name, args.steps, args.warmup)
+            s = summary(name, nb2, el2, w2, k2, args.steps, nbs2)
+            log("[bench] secondary", json.dumps(s))
+            secondary.append(s)
+            del r2, c2
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, runner)
+        log("[bench] cpu_baseline", json.dumps(cpu))
+
+    fmt_name = {0: "MXFP4", 1: "MXFP8", 2: "NVFP4"}[case.fmt]
+    K = case.x.shape[1]
+    line = {
+        "metric": METRIC,
+        "value": round(nbytes * args.steps / wall / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": case.name, "format": fmt_name, "rows": int(case.x.shape[0]),
+                   "K": int(K), "block": bsq.BLOCK_SIZE[case.fmt],
+                   "bytes_per_step": nbytes, "buffer_sets_rotated": nb,
+                   "version": bsq.version()},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "traffic_note": traffic_note,
+                     "kernel_us_mean": head["kernel_us_mean"]},
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

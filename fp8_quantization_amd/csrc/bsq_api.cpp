@@ -48,12 +48,13 @@ bool log_enabled() {
     return on;
 }
 
-// Optional override of the chunks (512 elements) one wave quantizes, for
-// launch-shape sweeps.  0 = use the heuristic.
-int tile_override() {
+// Launch-shape knob, read once from the environment for sweeps:
+//   BSQ_TILE_CHUNKS   chunks of 512 elements per wave: 1, 2 or 4 (default 2)
+int tile_chunks() {
     static const int v = [] {
-        const char* s = std::getenv("BSQ_CHUNKS_PER_TILE");
-        return s ? std::atoi(s) : 0;
+        const char* s = std::getenv("BSQ_TILE_CHUNKS");
+        const int u = (s && s[0]) ? std::atoi(s) : 2;
+        return (u == 1 || u == 2 || u == 4) ? u : 2;
     }();
     return v;
 }
@@ -120,37 +121,28 @@ bool tsf_in_domain(float t) {
     return std::isfinite(t) && t >= std::ldexp(1.0f, -117) && t <= std::ldexp(1.0f, 100);
 }
 
-// Launch geometry: chunks of 512 elements per wave.  Start from 8 chunks
-// (4 KiB of BF16 per lane-row, two load batches) and split rows further while
-// the grid would hold fewer than 2048 waves (8 per CU), so small problems
-// still spread over the chip.  The tile is balanced across the row.
-void choose_tiles(int64_t rows, int chunks_per_row, int* chunks_per_tile, int* tiles_per_row) {
-    int target = 8;
-    if (tile_override() > 0) {
-        target = tile_override();
-    } else {
-        while (target > 1 && rows * ((chunks_per_row + target - 1) / target) < 2048) target /= 2;
-    }
-    int tiles = (chunks_per_row + target - 1) / target;
-    if (tiles < 1) tiles = 1;
-    *tiles_per_row = tiles;
-    *chunks_per_tile = (chunks_per_row + tiles - 1) / tiles;
-}
-
+// Launch geometry: one wave per tile of 2 chunks (1024 elements: two 16-byte
+// loads per lane), four waves per workgroup.  Small tiles give many short
+// waves, which keeps the most loads in flight across the chip and leaves the
+// smallest tail; the measured alternatives (1 or 4 chunks per wave, or a
+// persistent grid walking the tiles) were slower.
 int launch(int format, bool grouped, bsq::KernelArgs& a, hipStream_t stream) {
     a.chunks_per_row = (int32_t)((a.K + bsq::kChunkElems - 1) / bsq::kChunkElems);
-    choose_tiles(a.rows, a.chunks_per_row, &a.chunks_per_tile, &a.tiles_per_row);
-    const int64_t waves = a.rows * a.tiles_per_row;
-    const int64_t blocks = (waves + bsq::kWavesPerBlock - 1) / bsq::kWavesPerBlock;
-    if (blocks > 0x7FFFFFFFLL)
-        return fail(BSQ_ERR_INVALID_ARG, "problem too large for one launch (%lld blocks)",
-                    (long long)blocks);
+    const int u = tile_chunks();
+    a.chunks_per_tile = u;
+    a.tiles_per_row = (a.chunks_per_row + u - 1) / u;
+    a.total_tiles = a.rows * a.tiles_per_row;
+    if (a.total_tiles > 0x7FFFFFFFLL)
+        return fail(BSQ_ERR_INVALID_ARG, "problem too large for one launch (%lld tiles)",
+                    (long long)a.total_tiles);
+    const int64_t blocks = (a.total_tiles + bsq::kWavesPerBlock - 1) / bsq::kWavesPerBlock;
     if (log_enabled())
         std::fprintf(stderr,
-                     "[bsq] %s %s rows=%lld K=%d chunks/row=%d chunks/tile=%d tiles/row=%d "
+                     "[bsq] %s %s rows=%lld K=%d chunks/row=%d chunks/tile=%d tiles=%lld "
                      "blocks=%lld\n",
                      grouped ? "grouped" : "dense", fmt_name(format), (long long)a.rows, a.K,
-                     a.chunks_per_row, a.chunks_per_tile, a.tiles_per_row, (long long)blocks);
+                     a.chunks_per_row, a.chunks_per_tile, (long long)a.total_tiles,
+                     (long long)blocks);
     const hipError_t e = bsq::launch_quantize(format, grouped, a, blocks, stream);
     if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

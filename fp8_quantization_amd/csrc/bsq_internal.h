@@ -7,8 +7,9 @@
 
 namespace bsq {
 
-// One wave quantizes a "tile": up to chunks_per_tile consecutive chunks of
-// one row, a chunk being 512 BF16 elements (64 lanes x one 16-byte load).
+// Work is cut into tiles: up to chunks_per_tile (1, 2 or 4) consecutive
+// chunks of one row, a chunk being 512 BF16 elements (64 lanes x one 16-byte
+// load).  One wave converts one tile.
 constexpr int kWaveSize = 64;
 constexpr int kWavesPerBlock = 4;
 constexpr int kThreadsPerBlock = kWaveSize * kWavesPerBlock;
@@ -27,6 +28,7 @@ struct KernelArgs {
     int32_t chunks_per_row;       // ceil(K / 512)
     int32_t chunks_per_tile;
     int32_t tiles_per_row;
+    int64_t total_tiles;          // rows * tiles_per_row (< 2^31)
     float tensor_sf;              // dense NVFP4
 
     // grouped form only

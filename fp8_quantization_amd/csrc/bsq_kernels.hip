@@ -42,8 +42,6 @@
 namespace bsq {
 namespace {
 
-constexpr int kBatch = 4;  // chunks loaded per batch (16-byte loads in flight per lane)
-
 template <int FMT>
 struct FormatTraits;
 // MXFP4: E2M1 codes (2 per byte), 32-element blocks (4 lanes), E8M0 scale.
@@ -62,58 +60,63 @@ struct FormatTraits<2> {
     static constexpr int kBlock = 16, kLanesPerBlock = 2, kFp4 = 1;
 };
 
-// ---------------------------------------------------------------- element codes
+// ---------------------------------------------------------------- conversions
+//
+// Element codes come from gfx950's scaled conversion instructions.  Their
+// rounding was checked exhaustively against the software definition of
+// round-to-nearest-even with saturation (every BF16 pattern under every E8M0
+// scale; every fp32 pattern at scale 1):
+//  * v_cvt_scalef32_pk_fp4_bf16 with a scale operand whose exponent field is
+//    the E8M0 byte b computes RNE_sat_E2M1(x / 2^(b-127)) (b = 0 included);
+//  * v_cvt_scalef32_pk_fp4_f32 at scale 1.0 is RNE_sat_E2M1 of any fp32,
+//    +-Inf saturating to +-6;
+//  * the FP8 forms are RNE to E4M3 except on overflow, where they return
+//    the NaN code instead of saturating, so inputs are first clamped to
+//    448 * scale (which RNE maps to 448 anyway).
+// All of them take the sign from the input, so -0 keeps its sign bit, and
+// the low nibble / low byte receives the lower-indexed element.
 
-// E2M1 magnitude code (0..7 for 0, .5, 1, 1.5, 2, 3, 4, 6) of a >= 0 (may be
-// +Inf): round to nearest even, saturating at 6.
-//  - a >= 1: E2M1 keeps one mantissa bit, so round the fp32 pattern at bit
-//    22 (adding 2^21 - 1 plus the kept LSB gives ties-to-even) and rebias the
-//    exponent (fp32 1.0 -> code 2).
-//  - a < 1: the E2M1 grid there is the multiples of 0.5; adding 2^22 (whose
-//    fp32 ulp is 0.5) rounds the exact sum once, to nearest even, so the
-//    pattern difference counts halves: code 0, 1 or 2.
-__device__ __forceinline__ uint32_t e2m1_magnitude_code(float a) {
-    a = fminf(a, 6.0f);
-    const uint32_t u = __float_as_uint(a);
-    const uint32_t normal = ((u + 0x1FFFFFu + ((u >> 22) & 1u)) >> 22) - 0xFCu;
-    const uint32_t sub = __float_as_uint(a + 4194304.0f) - 0x4A800000u;
-    return a < 1.0f ? sub : normal;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2_t, w); }
+
+// Byte k of the result <- E2M1 codes of the two fp32 values (lo in the low
+// nibble), at scale 1.0.
+template <int K>
+__device__ __forceinline__ uint32_t fp4_pair_f32(uint32_t acc, float lo, float hi) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, lo, hi, 1.0f, K);
+}
+// Byte k of the result <- E2M1 codes of the two BF16 elements of w divided by
+// the power of two whose exponent field is in `scale`.
+template <int K>
+__device__ __forceinline__ uint32_t fp4_pair_bf16(uint32_t acc, uint32_t w, float scale) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(acc, as_bf16x2(w), scale, K);
 }
 
-// E4M3 (FN) magnitude code (0..0x7E) of a >= 0 (may be +Inf): round to
-// nearest even, saturating at 448 = 0x7E.
-//  - a >= 2^-6: three mantissa bits, round at bit 20 and rebias
-//    (fp32 exponent 127 -> E4M3 exponent 7: subtract 120 << 3).
-//  - a < 2^-6: the subnormal grid is the multiples of 2^-9; adding 2^14
-//    (fp32 ulp 2^-9) rounds once; the pattern difference is the code 0..8.
-__device__ __forceinline__ uint32_t e4m3_magnitude_code(float a) {
-    a = fminf(a, 448.0f);
-    const uint32_t u = __float_as_uint(a);
-    const uint32_t normal = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - 0x3C0u;
-    const uint32_t sub = __float_as_uint(a + 16384.0f) - 0x46800000u;
-    return a < 0.015625f ? sub : normal;
-}
-
-// fp32 value of a positive E4M3 magnitude code (exact).
-__device__ __forceinline__ float e4m3_decode(uint32_t s) {
-    const uint32_t e = s >> 3, m = s & 7u;
-    return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+// E4M3 magnitude code of t in [0, +Inf]: RNE, saturating at 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_code_of(float t) {
+    i16x2_t r = {0, 0};
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, fminf(t, 448.0f), 0.0f, 1.0f, false);
+    return (uint32_t)__builtin_bit_cast(uint32_t, r) & 0xFFu;
 }
 
 // ---------------------------------------------------------------- block amax
 
+// |x| of two packed BF16 elements (the patterns without their sign bits).
+__device__ __forceinline__ uint32_t magnitudes(uint32_t w) { return w & 0x7FFF7FFFu; }
+
 // max |x| over the lane's 8 BF16 elements, as a 15-bit magnitude pattern.
 // Integer order of |BF16| patterns is value order, with Inf above every
 // finite value and NaN above Inf.
-__device__ __forceinline__ uint32_t lane_amax_bits(const uint4& w) {
-    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-    const uint32_t k = 0x7FFF7FFFu;
-    u16x2 a = __builtin_bit_cast(u16x2, w.x & k);
-    u16x2 b = __builtin_bit_cast(u16x2, w.y & k);
-    u16x2 c = __builtin_bit_cast(u16x2, w.z & k);
-    u16x2 d = __builtin_bit_cast(u16x2, w.w & k);
-    u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
-                                        __builtin_elementwise_max(c, d));
+__device__ __forceinline__ uint32_t lane_amax_bits(const uint32_t (&mag)[4]) {
+    u16x2_t a = __builtin_bit_cast(u16x2_t, mag[0]);
+    u16x2_t b = __builtin_bit_cast(u16x2_t, mag[1]);
+    u16x2_t c = __builtin_bit_cast(u16x2_t, mag[2]);
+    u16x2_t d = __builtin_bit_cast(u16x2_t, mag[3]);
+    u16x2_t m = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                          __builtin_elementwise_max(c, d));
     return (uint32_t)(m.x > m.y ? m.x : m.y);
 }
 
@@ -131,6 +134,62 @@ __device__ __forceinline__ uint32_t block_amax_bits(uint32_t m) {
     return (uint32_t)v;
 }
 
+
+// ---------------------------------------------------------------- NVFP4 scale
+//
+// The reading fixes s = RNE_sat_E4M3(t2), t2 = fl(fl(amax / 6) / tsf), and
+// inv = fl(1 / fl(dec(s) * tsf)).  Both are computed exactly, but without a
+// division per block:
+//
+//  * s: q = fl(amax * k), k = fl(1 / fl(6 * tsf)), is within 6 fp32 ulps of
+//    t2 (each of the four roundings involved adds at most 2^-24 relative
+//    error; no over/underflow in the normal range).  E4M3 decisions in the
+//    normal range change only at midpoints, whose fp32 patterns end in the 20
+//    bits 0x80000, and none lies near a binade edge; so unless q is within 16
+//    ulps of such a pattern, or below 2^-6 (the E4M3 subnormal range, zero
+//    included), t2 and q round to the same s.  Those rare lanes take the
+//    exact two divisions.
+//  * inv: with s = (8 + m) * 2^(e-10) (e >= 1) or m * 2^-9 (e = 0), and
+//    s * tsf and its reciprocal normal (the tensor-scale domain), rounding
+//    commutes with the power of two, so inv = T[m or 8 + m] * 2^(10-e or 9)
+//    with T[j] = fl(1 / fl((8 + j) * tsf)) and T[8 + j] = fl(1 / fl(j * tsf))
+//    (T[8] = 0: s = 0 gives inv = 0).  Lanes 0..15 of each wave hold the 16
+//    entries; lane 16 computes k.
+
+struct Nvfp4Wave {
+    float k;      // fl(1 / fl(6 * tsf)), wave-uniform
+    int table;    // this lane's entry T[lane] (lanes 0..15), as bits
+    float tsf;
+};
+
+__device__ __forceinline__ Nvfp4Wave nvfp4_wave_setup(float tsf, int lane) {
+    const float mult = lane < 8 ? (float)(8 + lane) : lane < 16 ? (float)(lane - 8) : 6.0f;
+    const float d = mult * tsf;
+    const float r = (d == 0.0f) ? 0.0f : 1.0f / d;
+    Nvfp4Wave w;
+    w.k = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 16));
+    w.table = __float_as_int(r);
+    w.tsf = tsf;
+    return w;
+}
+
+// Returns the E4M3 block scale s and sets inv.  amax_f is the block's amax.
+__device__ __forceinline__ uint32_t nvfp4_scale(float amax_f, const Nvfp4Wave& nw, float& inv) {
+    float q = amax_f * nw.k;
+    const uint32_t qb = __float_as_uint(q);
+    const bool near_midpoint = ((qb & 0xFFFFFu) - 0x7FFF0u) < 0x21u;  // within 16 ulps
+    if (q < 0.015625f || near_midpoint) {
+        const float t1 = amax_f / 6.0f;
+        q = t1 / nw.tsf;
+    }
+    const uint32_t s = e4m3_code_of(q);
+    const uint32_t e = s >> 3, m = s & 7u;
+    const int idx = e ? (int)m : 8 + (int)m;
+    const float t = __int_as_float(__builtin_amdgcn_ds_bpermute(idx << 2, nw.table));
+    inv = ldexpf(t, e ? 10 - (int)e : 9);
+    return s;
+}
+
 // ---------------------------------------------------------------- one chunk
 
 struct LaneOut {
@@ -138,31 +197,29 @@ struct LaneOut {
     uint32_t scale;   // the block's scale byte
 };
 
-__device__ __forceinline__ uint32_t bf16_at(const uint4& w, int i) {
-    const uint32_t d = (i < 2) ? w.x : (i < 4) ? w.y : (i < 6) ? w.z : w.w;
-    return (i & 1) ? (d >> 16) : (d & 0xFFFFu);
-}
-
 template <int FMT>
-__device__ __forceinline__ LaneOut quantize_lane(const uint4& w, float tsf) {
+__device__ __forceinline__ LaneOut quantize_lane(const uint4& w, const Nvfp4Wave& nw) {
     using T = FormatTraits<FMT>;
-    const uint32_t amax = block_amax_bits<T::kLanesPerBlock>(lane_amax_bits(w));
+    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+    const uint32_t mag[4] = {magnitudes(w.x), magnitudes(w.y), magnitudes(w.z), magnitudes(w.w)};
+    const uint32_t amax = block_amax_bits<T::kLanesPerBlock>(lane_amax_bits(mag));
     const bool special = amax >= 0x7F80u;  // exponent field 255: Inf or NaN
     LaneOut o;
-    uint32_t codes[8];
     if constexpr (FMT == 2) {
-        const float amax_f = __uint_as_float(amax << 16);
-        const float t1 = amax_f / 6.0f;
-        const float t2 = t1 / tsf;
-        const uint32_t s = e4m3_magnitude_code(t2);
-        const float d = e4m3_decode(s) * tsf;
-        const float inv = (d == 0.0f) ? 0.0f : 1.0f / d;
+        float inv;
+        const uint32_t s = nvfp4_scale(__uint_as_float(amax << 16), nw, inv);
+        float v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t h = bf16_at(w, i);
-            const float v = __uint_as_float(h << 16) * inv;
-            codes[i] = e2m1_magnitude_code(fabsf(v)) | ((h >> 15) << 3);
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = __uint_as_float(wv[k] << 16) * inv;
+            v[2 * k + 1] = __uint_as_float(wv[k] & 0xFFFF0000u) * inv;
         }
+        uint32_t p = fp4_pair_f32<0>(0u, v[0], v[1]);
+        p = fp4_pair_f32<1>(p, v[2], v[3]);
+        p = fp4_pair_f32<2>(p, v[4], v[5]);
+        p = fp4_pair_f32<3>(p, v[6], v[7]);
+        o.c0 = special ? 0u : p;
+        o.c1 = 0;
         o.scale = special ? 0x7Fu : s;
     } else {
         // floor(log2 amax): exponent field minus bias, or for a subnormal
@@ -171,79 +228,86 @@ __device__ __forceinline__ LaneOut quantize_lane(const uint4& w, float tsf) {
         const int e = (int)(amax >> 7);
         const int E = e ? e - 127 : (31 - __clz((int)(amax & 0x7Fu))) - 133;
         const int X = max(E - T::kEmax, -127);
-        const float sf = __uint_as_float((uint32_t)(127 - X) << 23);  // 2^-X, X in [-127, 126]
+        const uint32_t sbyte = (uint32_t)(X + 127);
+        const float scale = __uint_as_float(sbyte << 23);  // exponent field = E8M0 byte
+        if constexpr (FMT == 0) {
+            uint32_t p = fp4_pair_bf16<0>(0u, wv[0], scale);
+            p = fp4_pair_bf16<1>(p, wv[1], scale);
+            p = fp4_pair_bf16<2>(p, wv[2], scale);
+            p = fp4_pair_bf16<3>(p, wv[3], scale);
+            o.c0 = special ? 0u : p;
+            o.c1 = 0;
+        } else {
+            // clamp |x| to 448 * 2^X (BF16 pattern 1.75 * 2^(X+8)), keeping the sign
+            const uint32_t cap = ((uint32_t)(X + 135) << 7) | 0x60u;
+            const u16x2_t cap2 = __builtin_bit_cast(u16x2_t, cap | (cap << 16));
+            uint32_t cw[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t h = bf16_at(w, i);
-            const float v = __uint_as_float(h << 16) * sf;
-            if constexpr (FMT == 0)
-                codes[i] = e2m1_magnitude_code(fabsf(v)) | ((h >> 15) << 3);
-            else
-                codes[i] = e4m3_magnitude_code(fabsf(v)) | ((h >> 15) << 7);
+            for (int k = 0; k < 4; ++k) {
+                const u16x2_t m = __builtin_elementwise_min(__builtin_bit_cast(u16x2_t, mag[k]), cap2);
+                cw[k] = __builtin_bit_cast(uint32_t, m) | (wv[k] & 0x80008000u);
+            }
+            i16x2_t r0 = {0, 0}, r1 = {0, 0};
+            r0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r0, as_bf16x2(cw[0]), scale, false);
+            r0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r0, as_bf16x2(cw[1]), scale, true);
+            r1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r1, as_bf16x2(cw[2]), scale, false);
+            r1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r1, as_bf16x2(cw[3]), scale, true);
+            o.c0 = special ? 0u : __builtin_bit_cast(uint32_t, r0);
+            o.c1 = special ? 0u : __builtin_bit_cast(uint32_t, r1);
         }
-        o.scale = special ? 0xFFu : (uint32_t)(X + 127);
-    }
-    if constexpr (FormatTraits<FMT>::kFp4) {
-        uint32_t p = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) p |= codes[i] << (4 * i);
-        o.c0 = special ? 0u : p;
-        o.c1 = 0;
-    } else {
-        uint32_t p0 = 0, p1 = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            p0 |= codes[i] << (8 * i);
-            p1 |= codes[i + 4] << (8 * i);
-        }
-        o.c0 = special ? 0u : p0;
-        o.c1 = special ? 0u : p1;
+        o.scale = special ? 0xFFu : sbyte;
     }
     return o;
 }
 
 // ---------------------------------------------------------------- kernel
+//
+// One wave converts one tile: U consecutive chunks (U * 512 elements) of one
+// row.  Loads and stores carry the non-temporal hint: the data streams through
+// once, so it should not displace anything from the caches.
 
-__device__ __forceinline__ void load_batch(uint4 (&w)[kBatch], const uint16_t* xrow, int c,
-                                           int c_end, int lane, int K) {
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-        const int col = (c + u) * kChunkElems + lane * kElemsPerLane;
-        w[u] = make_uint4(0u, 0u, 0u, 0u);
-        if (c + u < c_end && col < K) w[u] = *reinterpret_cast<const uint4*>(xrow + col);
-    }
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <int FMT>
-__device__ __forceinline__ void convert_batch(const uint4 (&w)[kBatch], uint8_t* qrow,
-                                              uint8_t* srow, int c, int c_end, int lane, int K,
-                                              float tsf) {
-    using T = FormatTraits<FMT>;
+// The owning group of routed row r, found with one wave-wide pass per 256
+// offsets: lane l compares row_offsets[4l .. 4l+3] with r, four ballots count
+// the offsets <= r, and that count minus one is the last g with
+// row_offsets[g] <= r (so empty groups, whose offsets repeat, never win).
+// Returns -1 when r is before the first or at/after the last group.
+__device__ __forceinline__ int find_group(const uint32_t* __restrict__ ro, int G, uint32_t r,
+                                          int lane) {
+    int cnt = 0;
+    const bool vec = (reinterpret_cast<uintptr_t>(ro) & 15) == 0;  // 16-byte loads allowed
+    for (int base = 0; base <= G; base += 4 * kWaveSize) {
+        const int i = base + 4 * lane;
+        uint32_t v[4];
+        if (vec && i + 3 <= G) {
+            const uint4 q = *reinterpret_cast<const uint4*>(ro + i);
+            v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+        } else {
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-        if (c + u >= c_end) break;  // wave-uniform
-        const LaneOut o = quantize_lane<FMT>(w[u], tsf);
-        const int col = (c + u) * kChunkElems + lane * kElemsPerLane;
-        if (col < K) {
-            if constexpr (T::kFp4) {
-                *reinterpret_cast<uint32_t*>(qrow + col / 2) = o.c0;
-            } else {
-                *reinterpret_cast<uint2*>(qrow + col) = make_uint2(o.c0, o.c1);
-            }
-            if ((lane & (T::kLanesPerBlock - 1)) == 0) srow[col / T::kBlock] = (uint8_t)o.scale;
+            for (int k = 0; k < 4; ++k) v[k] = (i + k <= G) ? ro[i + k] : 0xFFFFFFFFu;
         }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) cnt += __popcll(__ballot(v[k] <= r && i + k <= G));
     }
+    return (cnt == 0 || cnt > G) ? -1 : cnt - 1;
 }
 
-template <int FMT, bool GROUPED>
+template <int FMT, bool GROUPED, int U>
 __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const KernelArgs a) {
+    using T = FormatTraits<FMT>;
     const int lane = (int)(threadIdx.x & (kWaveSize - 1));
-    const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWaveSize);
-    const int64_t row = wave / a.tiles_per_row;
-    if (row >= a.rows) return;
-    const int tile = (int)(wave - row * a.tiles_per_row);
-    const int c_begin = tile * a.chunks_per_tile;
-    const int c_end = min(c_begin + a.chunks_per_tile, a.chunks_per_row);
+    const uint32_t t = blockIdx.x * kWavesPerBlock + (threadIdx.x / kWaveSize);
+    if (t >= (uint32_t)a.total_tiles) return;
+    const uint32_t row = t / (uint32_t)a.tiles_per_row;
+    const int c0 = (int)(t - row * (uint32_t)a.tiles_per_row) * U;
+    const int nch = min(U, a.chunks_per_row - c0);  // chunks in this tile (>= 1)
 
     int64_t src = row;
     if constexpr (GROUPED) {
@@ -254,24 +318,21 @@ __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const Kernel
     }
     const uint16_t* xrow = a.x + src * a.ldx;
 
-    uint4 cur[kBatch];
-    load_batch(cur, xrow, c_begin, c_end, lane, a.K);
+    // issue this tile's loads before anything that waits on memory
+    uint4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int col = (c0 + u) * kChunkElems + lane * kElemsPerLane;
+        w[u] = make_uint4(0u, 0u, 0u, 0u);
+        if (u < nch && col < a.K) w[u] = load_stream(xrow + col);
+    }
 
     int64_t scale_row = row;
     float tsf = a.tensor_sf;
     if constexpr (GROUPED) {
-        // Count the offsets <= r over row_offsets[0..G] with a wave ballot;
-        // that count minus one is the owning group (upper bound - 1).
-        const uint32_t r = (uint32_t)row;
-        int cnt = 0;
-        for (int base = 0; base <= a.num_groups; base += kWaveSize) {
-            const int i = base + lane;
-            const bool le = (i <= a.num_groups) && (a.row_offsets[i] <= r);
-            cnt += __popcll(__ballot(le));
-        }
-        if (cnt == 0 || cnt > a.num_groups) return;  // before the first or past the last group
-        const int g = __builtin_amdgcn_readfirstlane(cnt - 1);
-        scale_row = (int64_t)a.scales_offsets[g] + ((int64_t)r - (int64_t)a.row_offsets[g]);
+        const int g = __builtin_amdgcn_readfirstlane(find_group(a.row_offsets, a.num_groups, row, lane));
+        if (g < 0) return;
+        scale_row = (int64_t)a.scales_offsets[g] + ((int64_t)row - (int64_t)a.row_offsets[g]);
         if (scale_row < 0 || scale_row >= a.num_scale_rows) return;
         if constexpr (FMT == 2) {
             const int e = a.expert_ids[g];
@@ -279,26 +340,44 @@ __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const Kernel
             tsf = a.expert_sf[e];
         }
     }
-    uint8_t* qrow = a.codes + row * a.ldq;
+    uint8_t* qrow = a.codes + (int64_t)row * a.ldq;
     uint8_t* srow = a.scales + scale_row * a.lds;
+    Nvfp4Wave nw{};
+    if constexpr (FMT == 2) nw = nvfp4_wave_setup(tsf, lane);
 
-    for (int c = c_begin; c < c_end; c += kBatch) {
-        uint4 nxt[kBatch];
-        const bool more = c + kBatch < c_end;
-        if (more) load_batch(nxt, xrow, c + kBatch, c_end, lane, a.K);
-        convert_batch<FMT>(cur, qrow, srow, c, c_end, lane, a.K, tsf);
-        if (more) {
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) cur[u] = nxt[u];
+    for (int u = 0; u < U; ++u) {
+        if (u >= nch) continue;  // wave-uniform
+        const LaneOut o = quantize_lane<FMT>(w[u], nw);
+        const int col = (c0 + u) * kChunkElems + lane * kElemsPerLane;
+        if (col < a.K) {
+            if constexpr (T::kFp4) {
+                __builtin_nontemporal_store(o.c0, reinterpret_cast<uint32_t*>(qrow + col / 2));
+            } else {
+                const u32x2_t v = {o.c0, o.c1};
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(qrow + col));
+            }
+            if ((lane & (T::kLanesPerBlock - 1)) == 0)
+                __builtin_nontemporal_store((uint8_t)o.scale, srow + col / T::kBlock);
         }
     }
 }
 
-template <int FMT, bool GROUPED>
+template <int FMT, bool GROUPED, int U>
 hipError_t launch(const KernelArgs& a, int64_t blocks, hipStream_t stream) {
-    hipLaunchKernelGGL((quantize_kernel<FMT, GROUPED>), dim3((uint32_t)blocks),
+    hipLaunchKernelGGL((quantize_kernel<FMT, GROUPED, U>), dim3((uint32_t)blocks),
                        dim3(kThreadsPerBlock), 0, stream, a);
     return hipGetLastError();
+}
+
+template <int FMT, bool GROUPED>
+hipError_t launch_u(const KernelArgs& a, int64_t blocks, hipStream_t stream) {
+    switch (a.chunks_per_tile) {
+        case 1: return launch<FMT, GROUPED, 1>(a, blocks, stream);
+        case 2: return launch<FMT, GROUPED, 2>(a, blocks, stream);
+        case 4: return launch<FMT, GROUPED, 4>(a, blocks, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -306,12 +385,12 @@ hipError_t launch(const KernelArgs& a, int64_t blocks, hipStream_t stream) {
 hipError_t launch_quantize(int fmt, bool grouped, const KernelArgs& a, int64_t blocks,
                            hipStream_t stream) {
     switch (fmt * 2 + (grouped ? 1 : 0)) {
-        case 0: return launch<0, false>(a, blocks, stream);
-        case 1: return launch<0, true>(a, blocks, stream);
-        case 2: return launch<1, false>(a, blocks, stream);
-        case 3: return launch<1, true>(a, blocks, stream);
-        case 4: return launch<2, false>(a, blocks, stream);
-        case 5: return launch<2, true>(a, blocks, stream);
+        case 0: return launch_u<0, false>(a, blocks, stream);
+        case 1: return launch_u<0, true>(a, blocks, stream);
+        case 2: return launch_u<1, false>(a, blocks, stream);
+        case 3: return launch_u<1, true>(a, blocks, stream);
+        case 4: return launch_u<2, false>(a, blocks, stream);
+        case 5: return launch_u<2, true>(a, blocks, stream);
         default: return hipErrorInvalidValue;
     }
 }
