@@ -49,14 +49,15 @@ bool log_enabled() {
 }
 
 // Launch-shape knob, read once from the environment for sweeps:
-//   BSQ_TILE_CHUNKS   chunks of 512 elements per wave: 1, 2 or 4 (default 2)
-int tile_chunks() {
+//   BSQ_TILE_CHUNKS   chunks of 512 elements per wave: 1, 2 or 4 (0 / unset:
+//                     2 for the dense form, 4 for the grouped form)
+int tile_chunks(bool grouped) {
     static const int v = [] {
         const char* s = std::getenv("BSQ_TILE_CHUNKS");
-        const int u = (s && s[0]) ? std::atoi(s) : 2;
-        return (u == 1 || u == 2 || u == 4) ? u : 2;
+        const int u = (s && s[0]) ? std::atoi(s) : 0;
+        return (u == 1 || u == 2 || u == 4) ? u : 0;
     }();
-    return v;
+    return v ? v : (grouped ? 4 : 2);
 }
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
@@ -121,20 +122,28 @@ bool tsf_in_domain(float t) {
     return std::isfinite(t) && t >= std::ldexp(1.0f, -117) && t <= std::ldexp(1.0f, 100);
 }
 
-// Launch geometry: one wave per tile of 2 chunks (1024 elements: two 16-byte
-// loads per lane), four waves per workgroup.  Small tiles give many short
-// waves, which keeps the most loads in flight across the chip and leaves the
-// smallest tail; the measured alternatives (1 or 4 chunks per wave, or a
-// persistent grid walking the tiles) were slower.
+// Launch geometry: one wave per tile, four waves per workgroup.  Dense tiles
+// are 2 chunks (1024 elements: two 16-byte loads per lane): many short waves
+// keep the most loads in flight across the chip and leave the smallest tail;
+// the measured alternatives (1 or 4 chunks per wave, or a persistent grid
+// walking the tiles) were slower.  Grouped tiles are 4 chunks, which halves
+// the number of group searches per row and measured faster there.
 int launch(int format, bool grouped, bsq::KernelArgs& a, hipStream_t stream) {
     a.chunks_per_row = (int32_t)((a.K + bsq::kChunkElems - 1) / bsq::kChunkElems);
-    const int u = tile_chunks();
+    const int u = tile_chunks(grouped);
     a.chunks_per_tile = u;
     a.tiles_per_row = (a.chunks_per_row + u - 1) / u;
     a.total_tiles = a.rows * a.tiles_per_row;
     if (a.total_tiles > 0x7FFFFFFFLL)
         return fail(BSQ_ERR_INVALID_ARG, "problem too large for one launch (%lld tiles)",
                     (long long)a.total_tiles);
+    if (a.tiles_per_row == 1) {
+        a.tpr_magic_lo = a.tpr_magic_hi = 0;
+    } else {  // ceil(2^64 / d) = floor((2^64 - 1) / d) + 1 for every d >= 2
+        const uint64_t m = UINT64_MAX / (uint64_t)a.tiles_per_row + 1;
+        a.tpr_magic_lo = (uint32_t)m;
+        a.tpr_magic_hi = (uint32_t)(m >> 32);
+    }
     const int64_t blocks = (a.total_tiles + bsq::kWavesPerBlock - 1) / bsq::kWavesPerBlock;
     if (log_enabled())
         std::fprintf(stderr,

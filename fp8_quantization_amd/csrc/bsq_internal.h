@@ -29,6 +29,8 @@ struct KernelArgs {
     int32_t chunks_per_tile;
     int32_t tiles_per_row;
     int64_t total_tiles;          // rows * tiles_per_row (< 2^31)
+    uint32_t tpr_magic_lo;        // ceil(2^64 / tiles_per_row), low and high words:
+    uint32_t tpr_magic_hi;        //   t / tiles_per_row = (t * magic) >> 64 for t < 2^32
     float tensor_sf;              // dense NVFP4
 
     // grouped form only

@@ -299,13 +299,25 @@ __device__ __forceinline__ int find_group(const uint32_t* __restrict__ ro, int G
     return (cnt == 0 || cnt > G) ? -1 : cnt - 1;
 }
 
+// t / tiles_per_row by multiply-high with the host's magic constant
+// M = ceil(2^64 / d): for t < 2^32, floor(t * M / 2^64) = floor(t / d)
+// because t * (M - 2^64 / d) / 2^64 < 2^-32 <= 1/d.  d = 1 is sent as M = 0.
+__device__ __forceinline__ uint32_t div_tiles(uint32_t t, const KernelArgs& a) {
+    if ((a.tpr_magic_lo | a.tpr_magic_hi) == 0) return t;
+    const uint64_t lo = (uint64_t)t * a.tpr_magic_lo;
+    const uint64_t hi = (uint64_t)t * a.tpr_magic_hi + (lo >> 32);
+    return (uint32_t)(hi >> 32);
+}
+
 template <int FMT, bool GROUPED, int U>
 __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const KernelArgs a) {
     using T = FormatTraits<FMT>;
     const int lane = (int)(threadIdx.x & (kWaveSize - 1));
-    const uint32_t t = blockIdx.x * kWavesPerBlock + (threadIdx.x / kWaveSize);
+    // the tile index is wave-uniform: keep it (and all row arithmetic) scalar
+    const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock +
+                                                      (threadIdx.x / kWaveSize));
     if (t >= (uint32_t)a.total_tiles) return;
-    const uint32_t row = t / (uint32_t)a.tiles_per_row;
+    const uint32_t row = div_tiles(t, a);
     const int c0 = (int)(t - row * (uint32_t)a.tiles_per_row) * U;
     const int nch = min(U, a.chunks_per_row - c0);  // chunks in this tile (>= 1)
 
