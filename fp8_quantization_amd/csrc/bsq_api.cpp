@@ -48,16 +48,24 @@ bool log_enabled() {
     return on;
 }
 
-// Launch-shape knob, read once from the environment for sweeps:
-//   BSQ_TILE_CHUNKS   chunks of 512 elements per wave: 1, 2 or 4 (0 / unset:
-//                     2 for the dense form, 4 for the grouped form)
-int tile_chunks(bool grouped) {
+// Launch-shape knobs, read once from the environment for sweeps (0 / unset:
+// the built-in choice below):
+//   BSQ_TILE_CHUNKS   chunks of 512 elements per wave: 1, 2 or 4
+//   BSQ_WIDE_LOOKUP   grouped form: 1 one-round-trip group lookup, 2 narrow
+int env_knob(const char* name) {
+    const char* s = std::getenv(name);
+    return (s && s[0]) ? std::atoi(s) : 0;
+}
+int tile_knob() {
     static const int v = [] {
-        const char* s = std::getenv("BSQ_TILE_CHUNKS");
-        const int u = (s && s[0]) ? std::atoi(s) : 0;
+        const int u = env_knob("BSQ_TILE_CHUNKS");
         return (u == 1 || u == 2 || u == 4) ? u : 0;
     }();
-    return v ? v : (grouped ? 4 : 2);
+    return v;
+}
+int wide_knob() {
+    static const int v = env_knob("BSQ_WIDE_LOOKUP");
+    return v;
 }
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
@@ -122,15 +130,21 @@ bool tsf_in_domain(float t) {
     return std::isfinite(t) && t >= std::ldexp(1.0f, -117) && t <= std::ldexp(1.0f, 100);
 }
 
-// Launch geometry: one wave per tile, four waves per workgroup.  Dense tiles
-// are 2 chunks (1024 elements: two 16-byte loads per lane): many short waves
-// keep the most loads in flight across the chip and leave the smallest tail;
-// the measured alternatives (1 or 4 chunks per wave, or a persistent grid
-// walking the tiles) were slower.  Grouped tiles are 4 chunks, which halves
-// the number of group searches per row and measured faster there.
+// Launch geometry: one wave per tile, four waves per workgroup.
+//  * Dense: tiles of 2 chunks (1024 elements: two 16-byte loads per lane).
+//    Many short waves keep the most loads in flight across the chip and
+//    leave the smallest tail; 1 or 4 chunks per wave, and a persistent grid
+//    walking the tiles, measured slower.
+//  * Grouped, large (more than 2^22 routed elements, bandwidth-bound): tiles
+//    of 4 chunks, halving the group searches per row, with the narrow lookup.
+//  * Grouped, small (decode-sized, latency-bound): tiles of 1 chunk for the
+//    most parallel waves, with the one-round-trip wide lookup.
 int launch(int format, bool grouped, bsq::KernelArgs& a, hipStream_t stream) {
     a.chunks_per_row = (int32_t)((a.K + bsq::kChunkElems - 1) / bsq::kChunkElems);
-    const int u = tile_chunks(grouped);
+    const bool small = (double)a.rows * (double)a.K <= (double)(1 << 22);
+    int u = grouped ? (small ? 1 : 4) : 2;
+    if (tile_knob()) u = tile_knob();
+    a.wide_lookup = grouped && (wide_knob() ? wide_knob() == 1 : small);
     a.chunks_per_tile = u;
     a.tiles_per_row = (a.chunks_per_row + u - 1) / u;
     a.total_tiles = a.rows * a.tiles_per_row;
@@ -148,10 +162,10 @@ int launch(int format, bool grouped, bsq::KernelArgs& a, hipStream_t stream) {
     if (log_enabled())
         std::fprintf(stderr,
                      "[bsq] %s %s rows=%lld K=%d chunks/row=%d chunks/tile=%d tiles=%lld "
-                     "blocks=%lld\n",
+                     "blocks=%lld wide_lookup=%d\n",
                      grouped ? "grouped" : "dense", fmt_name(format), (long long)a.rows, a.K,
                      a.chunks_per_row, a.chunks_per_tile, (long long)a.total_tiles,
-                     (long long)blocks);
+                     (long long)blocks, a.wide_lookup);
     const hipError_t e = bsq::launch_quantize(format, grouped, a, blocks, stream);
     if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

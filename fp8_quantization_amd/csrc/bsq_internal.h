@@ -43,6 +43,7 @@ struct KernelArgs {
     int64_t num_scale_rows;
     int32_t num_groups;
     int32_t num_experts;
+    int32_t wide_lookup;          // 1: one-round-trip group lookup (small problems)
 };
 
 // Launch the dense (grouped = false) or grouped kernel for format fmt

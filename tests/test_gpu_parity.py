@@ -248,6 +248,19 @@ def test_grouped_random_offsets(bsq, fmt, G, gather, first, extra):
     assert_same(*grouped_pair(bsq, c, pad_rows=2, pad_scale_rows=3), c.name)
 
 
+@pytest.mark.parametrize("fmt", [oracle.MXFP4, oracle.MXFP8, oracle.NVFP4],
+                         ids=["mxfp4", "mxfp8", "nvfp4"])
+@pytest.mark.parametrize("G,gather", [(5, False), (129, True), (600, False)])
+def test_grouped_large_problem_path(bsq, fmt, G, gather):
+    """Over 2^22 routed elements the library switches to 4-chunk tiles and the
+    offsets-only group search; K = 4608 leaves a ragged 1-chunk last tile."""
+    rows, K = 1200, 4608
+    assert rows * K > (1 << 22)
+    c = make_grouped(fmt, S=1300, K=K, G=G, E=G + 3, rows=rows, gather=gather, seed=G + 7,
+                     first_row=2, extra_rows=5)
+    assert_same(*grouped_pair(bsq, c, pad_rows=1, pad_scale_rows=2), c.name)
+
+
 def test_grouped_single_group_equals_dense(bsq):
     x = W.random_bf16((130, 2048), seed=77)
     for fmt, tsf in ((oracle.MXFP4, 1.0), (oracle.MXFP8, 1.0), (oracle.NVFP4, 0.004)):
