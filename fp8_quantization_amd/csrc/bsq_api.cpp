@@ -50,7 +50,7 @@ bool log_enabled() {
 
 // Launch-shape knobs, read once from the environment for sweeps (0 / unset:
 // the built-in choice below):
-//   BSQ_TILE_CHUNKS   chunks of 512 elements per wave: 1, 2 or 4
+//   BSQ_TILE_CHUNKS   chunks of 512 elements per wave: 1, 2, 4 (or 8, grouped)
 //   BSQ_WIDE_LOOKUP   grouped form: 1 one-round-trip group lookup, 2 narrow
 int env_knob(const char* name) {
     const char* s = std::getenv(name);
@@ -59,7 +59,7 @@ int env_knob(const char* name) {
 int tile_knob() {
     static const int v = [] {
         const int u = env_knob("BSQ_TILE_CHUNKS");
-        return (u == 1 || u == 2 || u == 4) ? u : 0;
+        return (u == 1 || u == 2 || u == 4 || u == 8) ? u : 0;
     }();
     return v;
 }
@@ -67,6 +67,7 @@ int wide_knob() {
     static const int v = env_knob("BSQ_WIDE_LOOKUP");
     return v;
 }
+
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
@@ -135,15 +136,19 @@ bool tsf_in_domain(float t) {
 //    Many short waves keep the most loads in flight across the chip and
 //    leave the smallest tail; 1 or 4 chunks per wave, and a persistent grid
 //    walking the tiles, measured slower.
-//  * Grouped, large (more than 2^22 routed elements, bandwidth-bound): tiles
-//    of 4 chunks, halving the group searches per row, with the narrow lookup.
+//  * Grouped, large (more than 2^22 routed elements, bandwidth-bound): the
+//    narrow lookup, with tiles of 8 chunks for NVFP4 (whose per-wave set-up
+//    -- the expert's scale and reciprocal table -- is the largest to
+//    amortise; 51.4 us against 55.4 with 4 chunks on the 16384 x 7168
+//    prefill) and 4 chunks for MXFP4 / MXFP8 (48.7 / 57.1 us against 49.7 /
+//    61.2 with 8).
 //  * Grouped, small (decode-sized, latency-bound): tiles of 1 chunk for the
 //    most parallel waves, with the one-round-trip wide lookup.
 int launch(int format, bool grouped, bsq::KernelArgs& a, hipStream_t stream) {
     a.chunks_per_row = (int32_t)((a.K + bsq::kChunkElems - 1) / bsq::kChunkElems);
     const bool small = (double)a.rows * (double)a.K <= (double)(1 << 22);
-    int u = grouped ? (small ? 1 : 4) : 2;
-    if (tile_knob()) u = tile_knob();
+    int u = grouped ? (small ? 1 : (format == BSQ_NVFP4 ? 8 : 4)) : 2;
+    if (tile_knob() && (tile_knob() != 8 || (grouped && format == BSQ_NVFP4))) u = tile_knob();
     a.wide_lookup = grouped && (wide_knob() ? wide_knob() == 1 : small);
     a.chunks_per_tile = u;
     a.tiles_per_row = (a.chunks_per_row + u - 1) / u;

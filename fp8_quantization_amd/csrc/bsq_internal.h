@@ -7,7 +7,7 @@
 
 namespace bsq {
 
-// Work is cut into tiles: up to chunks_per_tile (1, 2 or 4) consecutive
+// Work is cut into tiles: up to chunks_per_tile (1, 2, 4 or 8) consecutive
 // chunks of one row, a chunk being 512 BF16 elements (64 lanes x one 16-byte
 // load).  One wave converts one tile.
 constexpr int kWaveSize = 64;

@@ -121,19 +121,16 @@ __device__ __forceinline__ uint32_t lane_amax_bits(const uint32_t (&mag)[4]) {
 }
 
 // Reduce across the lanes of one block (2 or 4 adjacent lanes) with DPP quad
-// permutes: xor-1 swaps neighbours, xor-2 swaps pairs.
+// permutes: xor-1 swaps neighbours, xor-2 swaps pairs.  Written as a DPP move
+// with bound_ctrl and a zero old value feeding an unsigned max (0 is the
+// identity), which the compiler folds into a single v_max_u32_dpp.
 template <int LANES>
 __device__ __forceinline__ uint32_t block_amax_bits(uint32_t m) {
-    int v = (int)m;
-    int o = __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
-    v = max(v, o);
-    if constexpr (LANES == 4) {
-        o = __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
-        v = max(v, o);
-    }
-    return (uint32_t)v;
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
+    if constexpr (LANES == 4)
+        m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
+    return m;
 }
-
 
 // ---------------------------------------------------------------- NVFP4 scale
 //
@@ -222,13 +219,11 @@ __device__ __forceinline__ LaneOut quantize_lane(const uint4& w, const Nvfp4Wave
         o.c1 = 0;
         o.scale = special ? 0x7Fu : s;
     } else {
-        // floor(log2 amax): exponent field minus bias, or for a subnormal
-        // (field 0) the position of the top mantissa bit minus 133.  amax = 0
-        // gives -134, which the clamp below turns into X = -127.
-        const int e = (int)(amax >> 7);
-        const int E = e ? e - 127 : (31 - __clz((int)(amax & 0x7Fu))) - 133;
-        const int X = max(E - T::kEmax, -127);
-        const uint32_t sbyte = (uint32_t)(X + 127);
+        // E8M0 byte = X + 127 with X = max(floor(log2 amax) - emax, -127).  For a
+        // normal amax floor(log2 amax) is its exponent field e minus 127, so the
+        // byte is max(e - emax, 0); a subnormal or zero amax (e = 0) has
+        // floor(log2 amax) <= -127 and clamps to byte 0 as well.
+        const uint32_t sbyte = (uint32_t)max((int)(amax >> 7) - T::kEmax, 0);
         const float scale = __uint_as_float(sbyte << 23);  // exponent field = E8M0 byte
         if constexpr (FMT == 0) {
             uint32_t p = fp4_pair_bf16<0>(0u, wv[0], scale);
@@ -238,8 +233,9 @@ __device__ __forceinline__ LaneOut quantize_lane(const uint4& w, const Nvfp4Wave
             o.c0 = special ? 0u : p;
             o.c1 = 0;
         } else {
-            // clamp |x| to 448 * 2^X (BF16 pattern 1.75 * 2^(X+8)), keeping the sign
-            const uint32_t cap = ((uint32_t)(X + 135) << 7) | 0x60u;
+            // clamp |x| to 448 * 2^X: BF16 pattern 1.75 * 2^(X+8), exponent
+            // field X + 135 = sbyte + 8, mantissa 0x60
+            const uint32_t cap = (sbyte << 7) + 0x460u;
             const u16x2_t cap2 = __builtin_bit_cast(u16x2_t, cap | (cap << 16));
             uint32_t cw[4];
 #pragma unroll
@@ -432,9 +428,9 @@ __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const Kernel
     uint4 w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int col = (c0 + u) * kChunkElems + lane * kElemsPerLane;
+        const uint32_t col = (uint32_t)((c0 + u) * kChunkElems + lane * kElemsPerLane);
         w[u] = make_uint4(0u, 0u, 0u, 0u);
-        if (u < nch && col < a.K) w[u] = load_stream(xrow + col);
+        if (u < nch && col < (uint32_t)a.K) w[u] = load_stream(xrow + col);
     }
 
     int64_t scale_row = row;
@@ -455,21 +451,43 @@ __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const Kernel
     Nvfp4Wave nw{};
     if constexpr (FMT == 2) nw = nvfp4_wave_setup(tsf, lane);
 
+    uint32_t sb[U], q0[U], q1[U];  // per chunk: scale byte, packed codes (FP4: q0 only)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        sb[u] = q0[u] = q1[u] = 0;
+        if (u >= nch) continue;  // wave-uniform
+        const LaneOut o = quantize_lane<FMT>(w[u], nw);
+        sb[u] = o.scale;
+        q0[u] = o.c0;
+        q1[u] = o.c1;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (u >= nch) continue;  // wave-uniform
-        const LaneOut o = quantize_lane<FMT>(w[u], nw);
-        const int col = (c0 + u) * kChunkElems + lane * kElemsPerLane;
-        if (col < a.K) {
+        const uint32_t col = (uint32_t)((c0 + u) * kChunkElems + lane * kElemsPerLane);
+        if (col < (uint32_t)a.K) {
             if constexpr (T::kFp4) {
-                __builtin_nontemporal_store(o.c0, reinterpret_cast<uint32_t*>(qrow + col / 2));
+                __builtin_nontemporal_store(q0[u], reinterpret_cast<uint32_t*>(qrow + col / 2));
             } else {
-                const u32x2_t v = {o.c0, o.c1};
+                const u32x2_t v = {q0[u], q1[u]};
                 __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(qrow + col));
             }
-            if ((lane & (T::kLanesPerBlock - 1)) == 0)
-                __builtin_nontemporal_store((uint8_t)o.scale, srow + col / T::kBlock);
         }
+    }
+    // Scale bytes: every lane of a block holds its byte, so one store
+    // instruction covers up to kLanesPerBlock chunks -- lane (block * L + j)
+    // writes chunk (g + j)'s byte for that block.
+    constexpr int L = T::kLanesPerBlock;
+#pragma unroll
+    for (int g = 0; g < U; g += L) {
+        const int j = lane & (L - 1);
+        const int u = g + j;
+        uint32_t v = sb[g];
+#pragma unroll
+        for (int k = 1; k < L && g + k < U; ++k) v = (j == k) ? sb[g + k] : v;
+        const uint32_t col = (uint32_t)((c0 + u) * kChunkElems + (lane - j) * kElemsPerLane);
+        if (u < nch && u < U && col < (uint32_t)a.K)
+            __builtin_nontemporal_store((uint8_t)v, srow + col / T::kBlock);
     }
 }
 
@@ -496,6 +514,9 @@ hipError_t launch_u(const KernelArgs& a, int64_t blocks, hipStream_t stream) {
         case 1: return launch<FMT, GROUPED, 1, false>(a, blocks, stream);
         case 2: return launch<FMT, GROUPED, 2, false>(a, blocks, stream);
         case 4: return launch<FMT, GROUPED, 4, false>(a, blocks, stream);
+        case 8:
+            if constexpr (GROUPED && FMT == 2) return launch<FMT, GROUPED, 8, false>(a, blocks, stream);
+            return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 }
