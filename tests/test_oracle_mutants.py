@@ -1,0 +1,150 @@
+"""The pins catch plausible mistakes in the oracle.
+
+Each case below plants one mistake in a copy of ``oracle/oracle.c`` (on the
+CPU, in a temporary directory), builds it, and runs the pin battery against
+it: the hand-worked blocks and element points, the exact spec on a random
+matrix with special values, and the grouped-reduces-to-dense check.  Every
+mutant must fail at least one pin; the unmutated source must pass them all.
+"""
+import ctypes
+import json
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from oracle import build as oracle_build
+from oracle import spec
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
+GOLDEN = json.load(open(os.path.join(ROOT, "tests", "golden", "hand_examples.json")))
+
+# (name, original text, mutated text): each a mistake someone could make
+MUTANTS = [
+    ("ties_away_from_zero", "return (k % 2 == 0) ? k : k + 1;", "return k + 1;"),
+    ("ties_down", "return (k % 2 == 0) ? k : k + 1;", "return k;"),
+    ("nibble_order_swapped", "qrow[k / 2] = (uint8_t)((qrow[k / 2] & 0xF0) | tmp[i]);",
+     "qrow[k / 2] = (uint8_t)((qrow[k / 2] & 0x0F) | (tmp[i] << 4));"),
+    ("mx_exponent_ceil_like", "int X = (amax == 0.0) ? -127 : floor_log2(amax) - emax;",
+     "int X = (amax == 0.0) ? -127 : floor_log2(amax) - emax + 1;"),
+    ("mx_clamp_at_126", "if (X < -127) X = -127;", "if (X < -126) X = -126;"),
+    ("mx_emax_fp8_wrong", "int emax = (fmt == O_MXFP4) ? 2 : 8;", "int emax = (fmt == O_MXFP4) ? 2 : 7;"),
+    ("nvfp4_tsf_multiplied", "float t2 = t1 / tsf;", "float t2 = t1 * tsf;"),
+    ("nvfp4_divides_by_4", "float t1 = amax_f / 6.0f;", "float t1 = amax_f / 4.0f;"),
+    ("nvfp4_d_without_tsf", "float d = (float)E4M3_TAB[s] * tsf;", "float d = (float)E4M3_TAB[s];"),
+    ("signed_zero_dropped", "return (uint8_t)((neg ? 8 : 0) | rne_sat_code(E2M1_TAB, 8, fabs(v)));",
+     "return (uint8_t)(((neg && v != 0) ? 8 : 0) | rne_sat_code(E2M1_TAB, 8, fabs(v)));"),
+    ("e4m3_no_saturation", "if (a >= vals[n - 1]) return n - 1;",
+     "if (a > 464.0) return n; if (a >= vals[n - 1]) return n - 1;"),
+    ("mx_nan_scale_wrong", "*scale = 0xFF;", "*scale = 0x7F;"),
+    ("inf_not_special", "static int bf16_is_special(uint16_t h) { return ((h >> 7) & 0xFF) == 0xFF; }",
+     "static int bf16_is_special(uint16_t h) { return ((h >> 7) & 0xFF) == 0xFF && (h & 0x7F); }"),
+    ("amax_signed", "else if (bf16_magnitude(x[i]) > amax) amax = bf16_magnitude(x[i]);\n    }\n    if (special) {\n        *scale = 0xFF;",
+     "else if (bf16_value(x[i]) > amax) amax = bf16_value(x[i]);\n    }\n    if (special) {\n        *scale = 0xFF;"),
+    ("e4m3_subnormal_decode", "if (e == 0) return ldexp((double)m, -9);", "if (e == 0) return ldexp((double)m, -10);"),
+    ("e2m1_subnormal_decode", "if (e == 0) return 0.5 * m;", "if (e == 0) return 0.25 * m;"),
+    ("grouped_scale_row_unpadded",
+     "int64_t srow = (int64_t)scales_offsets[g] + (r - (int64_t)row_offsets[g]);",
+     "int64_t srow = r;"),
+    ("grouped_sf_by_group", "tsf = sf[e];", "tsf = sf[g];"),
+    ("grouped_gather_ignored", "int64_t src = row_indices ? (int64_t)row_indices[r] : r;",
+     "int64_t src = r;"),
+]
+
+
+def build_variant(tmp_path, text, name):
+    src = tmp_path / f"{name}.c"
+    src.write_text(text)
+    lib = tmp_path / f"lib{name}.so"
+    subprocess.run(["gcc", *oracle_build.CFLAGS, str(src), "-o", str(lib), "-lm"], check=True)
+    return str(lib)
+
+
+@pytest.fixture(scope="module")
+def references():
+    """Expected results that do not come from any build of oracle.c."""
+    x = W.random_bf16((24, 256), seed=91, scale_log2_range=(-30, 30), special_frac=0.02)
+    x[0, :16] = 0x0000
+    x[0, 1] = 0x8000                      # a block of signed zeros
+    x[1, :32] = np.uint16(0x0003)         # a block of subnormals
+    x[2, 40] = 0xFF80                     # -Inf alone in a block
+    rows = [list(map(int, r)) for r in x]
+    ref = {}
+    for fmt, tsfs in ((0, (1.0,)), (1, (1.0,)), (2, (1.0, 0.0123, 2.0 ** -10))):
+        for tsf in tsfs:
+            q, s = spec.quantize_rows(rows, fmt, oracle.BLOCK[fmt], np.float32(tsf))
+            ref[(fmt, tsf)] = (np.array(q, np.uint8), np.array(s, np.uint8))
+    return x, ref
+
+
+def run_battery(lib_path, references):
+    """Returns the names of the pins that fail with the library at lib_path."""
+    failed = []
+    saved = oracle._lib
+    oracle._lib = None
+    real_path = oracle._LIB_PATH
+    oracle._LIB_PATH = lib_path
+    try:
+        oracle._load()
+        # hand-worked blocks and element points
+        for b in GOLDEN["blocks"]:
+            x = np.zeros((1, b["bs"]), np.uint16)
+            for k, v in b["x"].items():
+                x[0, int(k)] = int(v, 16)
+            q, s = oracle.quantize(x, b["fmt"], b["tsf"])
+            if s[0, 0] != int(b["scale"], 16) or q[0].tobytes().hex().upper() != b["codes"]:
+                failed.append("hand:" + b["name"])
+        for v, code, _ in GOLDEN["element_points"]["e2m1"]:
+            if oracle.e2m1_code(v) != code:
+                failed.append("e2m1_point")
+                break
+        for v, code, _ in GOLDEN["element_points"]["e4m3"]:
+            if oracle.e4m3_code(v) != code:
+                failed.append("e4m3_point")
+                break
+        if [oracle.e2m1_decode(c) for c in range(8)] != [0, 0.5, 1, 1.5, 2, 3, 4, 6]:
+            failed.append("e2m1_table")
+        # exact spec on random blocks with specials
+        x, ref = references
+        for (fmt, tsf), (rq, rs) in ref.items():
+            q, s = oracle.quantize(x, fmt, tsf)
+            if not (np.array_equal(q, rq) and np.array_equal(s, rs)):
+                failed.append(f"spec:{fmt}:{tsf}")
+        # grouped reduces to per-row dense runs
+        rng = np.random.default_rng(5)
+        xs = W.random_bf16((30, 128), seed=6)
+        ro = np.array([0, 7, 7, 19, 26], np.uint32)
+        so = np.array([0, 8, 8, 24, 32], np.uint32)
+        ids = np.array([3, 0, 1, 2], np.int32)
+        sf = np.array([0.01, 0.02, 0.005, 0.3], np.float32)
+        ri = rng.integers(0, 30, 26).astype(np.int32)
+        for fmt in (0, 1, 2):
+            qg, sg = oracle.grouped_quantize(xs, fmt, ro, so, ids, sf if fmt == 2 else None, 26,
+                                             32, row_indices=ri)
+            for r in range(26):
+                g = int(np.searchsorted(ro, r, side="right")) - 1
+                qd, sd = oracle.quantize(xs[ri[r]:ri[r] + 1], fmt,
+                                         sf[ids[g]] if fmt == 2 else 1.0)
+                if not (np.array_equal(qg[r], qd[0]) and
+                        np.array_equal(sg[so[g] + r - ro[g]], sd[0])):
+                    failed.append(f"grouped:{fmt}")
+                    break
+    finally:
+        oracle._lib = saved
+        oracle._LIB_PATH = real_path
+    return failed
+
+
+def test_unmutated_source_passes_the_battery(tmp_path, references):
+    assert run_battery(build_variant(tmp_path, SRC, "orig"), references) == []
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_every_mutant_is_caught(tmp_path, references, name, old, new):
+    assert SRC.count(old) == 1, f"mutation site for {name} not unique in oracle.c"
+    failed = run_battery(build_variant(tmp_path, SRC.replace(old, new), name), references)
+    assert failed, f"mutant {name} passed every pin"
