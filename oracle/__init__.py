@@ -51,6 +51,10 @@ def _load():
     lib.oracle_validate_grouped.restype = i32
     lib.oracle_dequantize.argtypes = [i32, i32, p, i64, i64, i64, p, i64, ctypes.c_float, p]
     lib.oracle_dequantize.restype = i32
+    lib.oracle_tensor_scale.argtypes = [p, i64, i64, i64]
+    lib.oracle_tensor_scale.restype = ctypes.c_float
+    lib.oracle_grouped_tensor_scale.argtypes = [p, i64, i64, i64, p, p, p, i64, i64, p]
+    lib.oracle_grouped_tensor_scale.restype = i32
     for name in ("oracle_e2m1_code", "oracle_e4m3_code"):
         getattr(lib, name).argtypes = [ctypes.c_double]
         getattr(lib, name).restype = i32
@@ -148,6 +152,32 @@ def dequantize(codes, scales, fmt, K, tensor_sf=1.0, bs=None):
                                _ld(scales, 1), float(np.float32(tensor_sf)), _ptr(out))
     if rc != 0:
         raise ValueError("oracle_dequantize rejected its arguments")
+    return out
+
+
+def tensor_scale(x_bits: np.ndarray) -> np.float32:
+    """NVFP4 tensor scale of a BF16 matrix: fl32(amax / 2688) over the finite
+    elements, 1.0 when that amax is 0, clamped to [2^-117, 2^100]."""
+    lib = _load()
+    assert x_bits.dtype == np.uint16 and x_bits.ndim == 2
+    assert x_bits.shape[0] == 0 or x_bits.strides[1] == 2
+    M, K = x_bits.shape
+    return np.float32(lib.oracle_tensor_scale(_ptr(x_bits), M, K, _ld(x_bits, 2) if M else K))
+
+
+def grouped_tensor_scale(x_bits, row_offsets, expert_ids, num_experts, row_indices=None):
+    """Per-expert NVFP4 tensor scales over the routed rows of each expert's
+    groups (float32 [num_experts]); experts without rows get 1.0."""
+    lib = _load()
+    S, K = x_bits.shape
+    ro = np.ascontiguousarray(row_offsets, np.uint32)
+    ids = np.ascontiguousarray(expert_ids, np.int32)
+    ri = None if row_indices is None else np.ascontiguousarray(row_indices, np.int32)
+    out = np.empty(num_experts, np.float32)
+    rc = lib.oracle_grouped_tensor_scale(_ptr(x_bits), S, K, _ld(x_bits, 2) if S else K, _ptr(ri),
+                                         _ptr(ro), _ptr(ids), ids.shape[0], num_experts, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_grouped_tensor_scale rejected its arguments")
     return out
 
 

@@ -378,6 +378,66 @@ int oracle_dequantize(int fmt, int bs, const uint8_t* codes, int64_t M, int64_t 
     return O_OK;
 }
 
+/* Tensor scale for NVFP4, the step before the quantizer (the pages take it as
+   an input: the scalar tensor_sf of the dense kernel, the per-expert sf of the
+   grouped one).  tsf = fl32(amax / 2688), 2688 = 6 * 448 mapping the amax onto
+   the largest E2M1 code under the largest E4M3 block scale; amax is the largest
+   |x| over the finite elements (NaN and Inf are skipped); amax = 0 (nothing
+   finite and non-zero) gives 1.0; the result is clamped to [2^-117, 2^100],
+   the domain the quantizer accepts. */
+static float tensor_scale_of(double amax) {
+    if (amax == 0.0) return 1.0f;
+    float t = (float)amax / 2688.0f; /* (float)amax is exact: a BF16 value */
+    if (t < ldexpf(1.0f, -117)) t = ldexpf(1.0f, -117);
+    if (t > ldexpf(1.0f, 100)) t = ldexpf(1.0f, 100);
+    return t;
+}
+
+static double row_amax(const uint16_t* x, int64_t K) {
+    double amax = 0.0;
+    for (int64_t k = 0; k < K; ++k)
+        if (!bf16_is_special(x[k]) && bf16_magnitude(x[k]) > amax) amax = bf16_magnitude(x[k]);
+    return amax;
+}
+
+/* Dense: one tensor scale over the [M, K] matrix. */
+float oracle_tensor_scale(const uint16_t* x, int64_t M, int64_t K, int64_t ldx) {
+    unsigned int old = enter_ieee();
+    double amax = 0.0;
+    for (int64_t r = 0; r < M; ++r) {
+        double a = row_amax(x + r * ldx, K);
+        if (a > amax) amax = a;
+    }
+    float t = tensor_scale_of(amax);
+    leave_ieee(old);
+    return t;
+}
+
+/* Grouped: out[e] for every expert e in [0, E) over the routed rows of the
+   groups whose expert_ids[g] == e (source row row_indices[r] or r); experts
+   with no routed rows get 1.0. */
+int oracle_grouped_tensor_scale(const uint16_t* x, int64_t num_src_rows, int64_t K, int64_t ldx,
+                                const int32_t* row_indices, const uint32_t* row_offsets,
+                                const int32_t* expert_ids, int64_t G, int64_t E, float* out) {
+    if (G < 0 || E < 0 || K < 0) return O_BAD;
+    unsigned int old = enter_ieee();
+    for (int64_t e = 0; e < E; ++e) {
+        double amax = 0.0;
+        for (int64_t g = 0; g < G; ++g) {
+            if (expert_ids[g] != e) continue;
+            for (int64_t r = row_offsets[g]; r < (int64_t)row_offsets[g + 1]; ++r) {
+                int64_t src = row_indices ? (int64_t)row_indices[r] : r;
+                if (src < 0 || src >= num_src_rows) { leave_ieee(old); return O_BAD; }
+                double a = row_amax(x + src * ldx, K);
+                if (a > amax) amax = a;
+            }
+        }
+        out[e] = tensor_scale_of(amax);
+    }
+    leave_ieee(old);
+    return O_OK;
+}
+
 /* Element-level views used by the pin tests. */
 int oracle_e2m1_code(double v) { init_tables(); return e2m1_code(v, signbit(v) != 0); }
 int oracle_e4m3_code(double v) { init_tables(); return e4m3_code(v, signbit(v) != 0); }
