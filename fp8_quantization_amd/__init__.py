@@ -38,6 +38,11 @@ _lib.grouped_quantize_block_scaled.argtypes = [_i32, _i32, _i32, _p, _i64, _i64,
                                                _p, _p, _i64, _i64, _i64, _i64, _p, _i64, _p, _i64,
                                                _p]
 _lib.grouped_quantize_block_scaled.restype = _i32
+_lib.tensor_scale_nvfp4.argtypes = [_p, _i64, _i64, _i64, _p, _p]
+_lib.tensor_scale_nvfp4.restype = _i32
+_lib.grouped_tensor_scale_nvfp4.argtypes = [_p, _i64, _i64, _i64, _p, _p, _p, _i64, _i64, _i64, _p,
+                                            _p]
+_lib.grouped_tensor_scale_nvfp4.restype = _i32
 _lib.bsq_last_error.argtypes = []
 _lib.bsq_last_error.restype = ctypes.c_char_p
 _lib.bsq_version.argtypes = []
@@ -161,3 +166,39 @@ def grouped_quantize_block_scaled(x: torch.Tensor, fmt, row_offsets: torch.Tenso
         _ptr(scales_offsets), _ptr(expert_ids), _ptr(tensor_sf), G, E, max_rows, num_scale_rows,
         _ptr(codes), _ld(codes), _ptr(scales), _ld(scales), _stream_ptr(stream, x.device)))
     return codes, scales
+
+
+def tensor_scale_nvfp4(x: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    """NVFP4 tensor scale of a BF16 matrix on the GPU: fl32(amax / 2688) over
+    the finite elements (1.0 when amax is 0), clamped to [2^-117, 2^100].
+    Returns a float32 [1] GPU tensor (``out`` if given)."""
+    x = _as_bf16_matrix(x)
+    M, K = x.shape
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check(_lib.tensor_scale_nvfp4(_ptr(x), M, K, _ld(x), _ptr(out),
+                                   _stream_ptr(stream, x.device)))
+    return out
+
+
+def grouped_tensor_scale_nvfp4(x: torch.Tensor, row_offsets: torch.Tensor,
+                               expert_ids: torch.Tensor, num_experts: int, max_rows: int,
+                               row_indices: torch.Tensor | None = None,
+                               out: torch.Tensor | None = None, stream=None):
+    """Per-expert NVFP4 tensor scales over each expert's routed rows (float32
+    [num_experts] GPU tensor; experts without rows get 1.0).  The result can be
+    passed as ``tensor_sf`` to ``grouped_quantize_block_scaled``."""
+    x = _as_bf16_matrix(x)
+    S, K = x.shape
+    G = expert_ids.shape[0]
+    if row_offsets.shape[0] != G + 1:
+        raise ValueError("row_offsets must have num_groups + 1 entries")
+    if row_indices is not None and (row_indices.dtype != torch.int32 or
+                                    row_indices.shape[0] < max_rows):
+        raise TypeError("row_indices must be an int32 GPU tensor of >= max_rows")
+    if out is None:
+        out = torch.empty(num_experts, dtype=torch.float32, device=x.device)
+    _check(_lib.grouped_tensor_scale_nvfp4(
+        _ptr(x), S, K, _ld(x), _ptr(row_indices), _ptr(row_offsets), _ptr(expert_ids), G,
+        num_experts, max_rows, _ptr(out), _stream_ptr(stream, x.device)))
+    return out

@@ -131,6 +131,28 @@ bool tsf_in_domain(float t) {
     return std::isfinite(t) && t >= std::ldexp(1.0f, -117) && t <= std::ldexp(1.0f, 100);
 }
 
+// Tile geometry for a launch with u chunks per tile: fills chunks_per_row,
+// chunks_per_tile, tiles_per_row, total_tiles, the tile->row magic divisor,
+// and the number of 4-wave workgroups.
+int st_geometry(bsq::KernelArgs& a, int u, int64_t* blocks) {
+    a.chunks_per_row = (int32_t)((a.K + bsq::kChunkElems - 1) / bsq::kChunkElems);
+    a.chunks_per_tile = u;
+    a.tiles_per_row = (a.chunks_per_row + u - 1) / u;
+    a.total_tiles = a.rows * a.tiles_per_row;
+    if (a.total_tiles > 0x7FFFFFFFLL)
+        return fail(BSQ_ERR_INVALID_ARG, "problem too large for one launch (%lld tiles)",
+                    (long long)a.total_tiles);
+    if (a.tiles_per_row == 1) {
+        a.tpr_magic_lo = a.tpr_magic_hi = 0;
+    } else {  // ceil(2^64 / d) = floor((2^64 - 1) / d) + 1 for every d >= 2
+        const uint64_t m = UINT64_MAX / (uint64_t)a.tiles_per_row + 1;
+        a.tpr_magic_lo = (uint32_t)m;
+        a.tpr_magic_hi = (uint32_t)(m >> 32);
+    }
+    *blocks = (a.total_tiles + bsq::kWavesPerBlock - 1) / bsq::kWavesPerBlock;
+    return BSQ_OK;
+}
+
 // Launch geometry: one wave per tile, four waves per workgroup.
 //  * Dense: tiles of 2 chunks (1024 elements: two 16-byte loads per lane).
 //    Many short waves keep the most loads in flight across the chip and
@@ -145,25 +167,12 @@ bool tsf_in_domain(float t) {
 //  * Grouped, small (decode-sized, latency-bound): tiles of 1 chunk for the
 //    most parallel waves, with the one-round-trip wide lookup.
 int launch(int format, bool grouped, bsq::KernelArgs& a, hipStream_t stream) {
-    a.chunks_per_row = (int32_t)((a.K + bsq::kChunkElems - 1) / bsq::kChunkElems);
     const bool small = (double)a.rows * (double)a.K <= (double)(1 << 22);
     int u = grouped ? (small ? 1 : (format == BSQ_NVFP4 ? 8 : 4)) : 2;
     if (tile_knob() && (tile_knob() != 8 || (grouped && format == BSQ_NVFP4))) u = tile_knob();
     a.wide_lookup = grouped && (wide_knob() ? wide_knob() == 1 : small);
-    a.chunks_per_tile = u;
-    a.tiles_per_row = (a.chunks_per_row + u - 1) / u;
-    a.total_tiles = a.rows * a.tiles_per_row;
-    if (a.total_tiles > 0x7FFFFFFFLL)
-        return fail(BSQ_ERR_INVALID_ARG, "problem too large for one launch (%lld tiles)",
-                    (long long)a.total_tiles);
-    if (a.tiles_per_row == 1) {
-        a.tpr_magic_lo = a.tpr_magic_hi = 0;
-    } else {  // ceil(2^64 / d) = floor((2^64 - 1) / d) + 1 for every d >= 2
-        const uint64_t m = UINT64_MAX / (uint64_t)a.tiles_per_row + 1;
-        a.tpr_magic_lo = (uint32_t)m;
-        a.tpr_magic_hi = (uint32_t)(m >> 32);
-    }
-    const int64_t blocks = (a.total_tiles + bsq::kWavesPerBlock - 1) / bsq::kWavesPerBlock;
+    int64_t blocks = 0;
+    if (st_geometry(a, u, &blocks) != BSQ_OK) return BSQ_ERR_INVALID_ARG;
     if (log_enabled())
         std::fprintf(stderr,
                      "[bsq] %s %s rows=%lld K=%d chunks/row=%d chunks/tile=%d tiles=%lld "
@@ -261,6 +270,87 @@ int grouped_quantize_block_scaled(int format, int block_size, int scale_layout, 
     a.num_groups = (int32_t)num_groups;
     a.num_experts = (int32_t)num_experts;
     return launch(format, true, a, static_cast<hipStream_t>(stream));
+}
+
+int tensor_scale_nvfp4(const void* x, int64_t M, int64_t K, int64_t ldx, float* tensor_sf_out,
+                       void* stream) {
+    if (M < 0 || K < 0) return fail(BSQ_ERR_INVALID_ARG, "negative size (M=%lld K=%lld)",
+                                    (long long)M, (long long)K);
+    if (K % 16 != 0) return fail(BSQ_ERR_INVALID_ARG, "K=%lld is not a multiple of 16", (long long)K);
+    if (K > (int64_t(1) << 30)) return fail(BSQ_ERR_INVALID_ARG, "K=%lld too large", (long long)K);
+    if (!tensor_sf_out) return fail(BSQ_ERR_INVALID_ARG, "tensor_sf_out is required");
+    if (!aligned(tensor_sf_out, 4)) return fail(BSQ_ERR_INVALID_ARG, "tensor_sf_out must be 4-byte aligned");
+    const bool work = M > 0 && K > 0;
+    if (work) {
+        if (!x) return fail(BSQ_ERR_INVALID_ARG, "null x");
+        if (!aligned(x, 16)) return fail(BSQ_ERR_INVALID_ARG, "x must be 16-byte aligned");
+        if (ldx < K || ldx % 8 != 0)
+            return fail(BSQ_ERR_INVALID_ARG, "ldx=%lld must be >= K=%lld and a multiple of 8",
+                        (long long)ldx, (long long)K);
+    }
+    bsq::KernelArgs a{};
+    a.x = static_cast<const uint16_t*>(x);
+    a.ldx = ldx;
+    a.rows = work ? M : 0;
+    a.K = (int32_t)K;
+    int64_t blocks = 0;
+    if (work && (st_geometry(a, 4, &blocks) != BSQ_OK)) return BSQ_ERR_INVALID_ARG;
+    const hipError_t e = bsq::launch_tensor_scale(false, a, blocks, tensor_sf_out, 1,
+                                                  static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int grouped_tensor_scale_nvfp4(const void* x, int64_t num_src_rows, int64_t K, int64_t ldx,
+                               const int32_t* row_indices, const uint32_t* row_offsets,
+                               const int32_t* expert_ids, int64_t num_groups, int64_t num_experts,
+                               int64_t max_rows, float* tensor_sf_out, void* stream) {
+    if (num_src_rows < 0 || K < 0 || num_groups < 0 || max_rows < 0)
+        return fail(BSQ_ERR_INVALID_ARG, "negative size");
+    if (num_experts < 1 || num_experts > (1 << 24))
+        return fail(BSQ_ERR_INVALID_ARG, "num_experts=%lld must be in [1, 2^24]",
+                    (long long)num_experts);
+    if (K % 16 != 0) return fail(BSQ_ERR_INVALID_ARG, "K=%lld is not a multiple of 16", (long long)K);
+    if (K > (int64_t(1) << 30)) return fail(BSQ_ERR_INVALID_ARG, "K=%lld too large", (long long)K);
+    if (!tensor_sf_out || !aligned(tensor_sf_out, 4))
+        return fail(BSQ_ERR_INVALID_ARG, "tensor_sf_out must be a 4-byte aligned device array");
+    if (num_groups > 0x7FFFFFFFLL - 64)
+        return fail(BSQ_ERR_INVALID_ARG, "num_groups=%lld too large", (long long)num_groups);
+    if (max_rows > (int64_t(1) << 32))
+        return fail(BSQ_ERR_INVALID_ARG, "max_rows=%lld exceeds the uint32 offset range",
+                    (long long)max_rows);
+    const bool work = num_groups > 0 && max_rows > 0 && K > 0;
+    if (work) {
+        if (!x || !row_offsets || !expert_ids)
+            return fail(BSQ_ERR_INVALID_ARG, "x, row_offsets and expert_ids are required");
+        if (!aligned(x, 16)) return fail(BSQ_ERR_INVALID_ARG, "x must be 16-byte aligned");
+        if (ldx < K || ldx % 8 != 0)
+            return fail(BSQ_ERR_INVALID_ARG, "ldx=%lld must be >= K=%lld and a multiple of 8",
+                        (long long)ldx, (long long)K);
+        if (!row_indices && max_rows > num_src_rows)
+            return fail(BSQ_ERR_INVALID_ARG,
+                        "without row_indices, max_rows=%lld may not exceed num_src_rows=%lld",
+                        (long long)max_rows, (long long)num_src_rows);
+        if (row_indices && num_src_rows == 0)
+            return fail(BSQ_ERR_INVALID_ARG, "row_indices given but x has no rows");
+    }
+    bsq::KernelArgs a{};
+    a.x = static_cast<const uint16_t*>(x);
+    a.ldx = ldx;
+    a.rows = work ? max_rows : 0;
+    a.K = (int32_t)K;
+    a.row_indices = row_indices;
+    a.row_offsets = row_offsets;
+    a.expert_ids = expert_ids;
+    a.num_src_rows = num_src_rows;
+    a.num_groups = (int32_t)num_groups;
+    a.num_experts = (int32_t)num_experts;
+    int64_t blocks = 0;
+    if (work && (st_geometry(a, 4, &blocks) != BSQ_OK)) return BSQ_ERR_INVALID_ARG;
+    const hipError_t e = bsq::launch_tensor_scale(true, a, blocks, tensor_sf_out, (int)num_experts,
+                                                  static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
 }
 
 const char* bsq_last_error(void) { return g_last_error.c_str(); }

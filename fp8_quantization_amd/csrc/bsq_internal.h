@@ -51,4 +51,9 @@ struct KernelArgs {
 hipError_t launch_quantize(int fmt, bool grouped, const KernelArgs& a, int64_t blocks,
                            hipStream_t stream);
 
+// NVFP4 tensor scale(s) into out[0 .. n_out): zero, amax over the tiles of a
+// (U = 4 chunks per tile; blocks = 0 skips the pass), finish.
+hipError_t launch_tensor_scale(bool grouped, const KernelArgs& a, int64_t blocks, float* out,
+                               int n_out, hipStream_t stream);
+
 }  // namespace bsq

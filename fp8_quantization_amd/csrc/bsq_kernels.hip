@@ -491,6 +491,106 @@ __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const Kernel
     }
 }
 
+// ---------------------------------------------------------------- tensor scale
+//
+// NVFP4 tensor scale, the step before the quantizer: tsf = fl32(amax / 2688)
+// over the finite elements, 1.0 when that amax is 0, clamped to [2^-117,
+// 2^100].  Three kernels on the caller's stream, using the caller's output
+// array (one float per expert; one for the dense form) as the accumulator:
+//  1. zero it;
+//  2. each wave takes the max |x| of its tile over the finite elements and,
+//     unless a relaxed read of the accumulator already holds as much, folds
+//     it in with an atomic max on the fp32 bit pattern (non-negative floats
+//     order like their patterns), so few waves issue an atomic at all;
+//  3. turn each amax into its tensor scale in place.
+
+__global__ void __launch_bounds__(kThreadsPerBlock) tsf_zero_kernel(uint32_t* acc, int n) {
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i < n) acc[i] = 0u;
+}
+
+__global__ void __launch_bounds__(kThreadsPerBlock) tsf_finish_kernel(uint32_t* acc, int n) {
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i >= n) return;
+    const float amax = __uint_as_float(acc[i]);
+    float t = 1.0f;
+    if (amax != 0.0f) {
+        t = amax / 2688.0f;  // 2688 = 6 * 448
+        t = fminf(fmaxf(t, 0x1p-117f), 0x1p100f);
+    }
+    acc[i] = __float_as_uint(t);
+}
+
+// max over the finite |x| of 8 BF16 elements, as a 15-bit pattern (0 if none):
+// adding 0x80 to every magnitude sends finite values to [0x80, 0x7FFF] and
+// Inf/NaN to [0x8000, 0x807F], which a signed 16-bit max never picks over a
+// finite one.
+__device__ __forceinline__ uint32_t lane_finite_amax_bits(const uint4& w) {
+    typedef short i16x2 __attribute__((ext_vector_type(2)));
+    const u16x2_t bias = {0x80, 0x80};
+    i16x2 m = {0, 0};  // below every biased finite value
+    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const u16x2_t b = __builtin_bit_cast(u16x2_t, magnitudes(wv[k])) + bias;
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(i16x2, b));
+    }
+    const int best = max((int)m.x, (int)m.y);
+    return best >= 0x80 ? (uint32_t)(best - 0x80) : 0u;
+}
+
+template <bool GROUPED>
+__global__ void __launch_bounds__(kThreadsPerBlock) tsf_amax_kernel(const KernelArgs a, uint32_t* acc) {
+    constexpr int U = 4;
+    const int lane = (int)(threadIdx.x & (kWaveSize - 1));
+    const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock +
+                                                      (threadIdx.x / kWaveSize));
+    if (t >= (uint32_t)a.total_tiles) return;
+    const uint32_t row = div_tiles(t, a);
+    const int c0 = (int)(t - row * (uint32_t)a.tiles_per_row) * U;
+    const int nch = min(U, a.chunks_per_row - c0);
+    int64_t src = row;
+    if constexpr (GROUPED) {
+        if (a.row_indices) {
+            src = a.row_indices[row];
+            if (src < 0 || src >= a.num_src_rows) return;
+        }
+    }
+    const uint16_t* xrow = a.x + src * a.ldx;
+    uint4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t col = (uint32_t)((c0 + u) * kChunkElems + lane * kElemsPerLane);
+        w[u] = make_uint4(0u, 0u, 0u, 0u);
+        if (u < nch && col < (uint32_t)a.K) w[u] = load_stream(xrow + col);
+    }
+    int slot = 0;
+    if constexpr (GROUPED) {
+        const GroupInfo gi = find_group_narrow<false>(a, row, lane);
+        if (gi.g < 0) return;
+        slot = a.expert_ids[gi.g];
+        if (slot < 0 || slot >= a.num_experts) return;
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) m = max(m, lane_finite_amax_bits(w[u]));
+    // wave max: DPP within rows of 16, then across the four rows
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, true));
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, true));
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x114, 0xF, 0xF, true));  // row_shr:4
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x118, 0xF, 0xF, true));  // row_shr:8
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)m, 15);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)m, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)m, 47);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)m, 63);
+    const uint32_t best = max(max(r0, r1), max(r2, r3)) << 16;  // fp32 pattern of the amax
+    if (lane == 0 && best != 0u) {
+        uint32_t* p = acc + slot;
+        if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < best)
+            __hip_atomic_fetch_max(p, best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 template <int FMT, bool GROUPED, int U, bool WIDE>
 hipError_t launch(const KernelArgs& a, int64_t blocks, hipStream_t stream) {
     hipLaunchKernelGGL((quantize_kernel<FMT, GROUPED, U, WIDE>), dim3((uint32_t)blocks),
@@ -522,6 +622,29 @@ hipError_t launch_u(const KernelArgs& a, int64_t blocks, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_tensor_scale(bool grouped, const KernelArgs& a, int64_t blocks, float* out,
+                               int n_out, hipStream_t stream) {
+    uint32_t* acc = reinterpret_cast<uint32_t*>(out);
+    const uint32_t small_blocks = (uint32_t)((n_out + kThreadsPerBlock - 1) / kThreadsPerBlock);
+    hipLaunchKernelGGL(tsf_zero_kernel, dim3(small_blocks), dim3(kThreadsPerBlock), 0, stream, acc,
+                       n_out);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (blocks > 0) {
+        if (grouped)
+            hipLaunchKernelGGL((tsf_amax_kernel<true>), dim3((uint32_t)blocks),
+                               dim3(kThreadsPerBlock), 0, stream, a, acc);
+        else
+            hipLaunchKernelGGL((tsf_amax_kernel<false>), dim3((uint32_t)blocks),
+                               dim3(kThreadsPerBlock), 0, stream, a, acc);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(tsf_finish_kernel, dim3(small_blocks), dim3(kThreadsPerBlock), 0, stream,
+                       acc, n_out);
+    return hipGetLastError();
+}
 
 hipError_t launch_quantize(int fmt, bool grouped, const KernelArgs& a, int64_t blocks,
                            hipStream_t stream) {

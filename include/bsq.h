@@ -40,8 +40,8 @@
  *   - Arguments are validated on the host before any HIP call.  On failure
  *     nothing is launched, the status is returned, and bsq_last_error()
  *     describes it.  A launch failure returns BSQ_ERR_HIP.
- *   - M == 0, K == 0 and (grouped) num_groups == 0 or max_rows == 0 are
- *     no-ops that return BSQ_OK.
+ *   - For the quantizers, M == 0, K == 0 and (grouped) num_groups == 0 or
+ *     max_rows == 0 are no-ops that return BSQ_OK.
  *   - Bytes of `codes` and `scales` outside what the call defines to write
  *     are never touched.
  */
@@ -141,6 +141,43 @@ int grouped_quantize_block_scaled(int format, int block_size, int scale_layout,
                                   void* codes, int64_t ldq,
                                   void* scales, int64_t lds,
                                   void* stream);
+
+/*
+ * NVFP4 tensor scale, the step before the NVFP4 quantizer (the pages take it
+ * as an input: the scalar tensor_sf of the "quantize_dynamic_scaled_async_fp4_kernel"
+ * page's signature, the per-expert sf of the grouped kernel page's Parameters).
+ *
+ *   tsf = fl32(amax / 2688), 2688 = 6 * 448 (the largest E2M1 code under the
+ *   largest E4M3 block scale), amax = the largest |x| over the finite
+ *   elements (NaN and Inf are skipped); 1.0 when amax is 0 (no finite
+ *   non-zero element, or no element); clamped to [2^-117, 2^100] so that the
+ *   result is always a valid tensor_sf for the quantizer.
+ *
+ * Dense: one value over the [M, K] matrix x (layout as for
+ * quantize_block_scaled; K % 16 == 0) into tensor_sf_out[0], a device float.
+ *
+ * Grouped: tensor_sf_out[e] (device float [num_experts]) for every expert e,
+ * over the routed rows of the groups g with expert_ids[g] == e (each routed
+ * row r reads source row row_indices[r], or r when row_indices is NULL);
+ * experts without routed rows get 1.0.  Arguments as for
+ * grouped_quantize_block_scaled; num_experts >= 1.
+ *
+ * Both run three kernels on `stream` and use tensor_sf_out itself as the
+ * accumulator: it is fully overwritten, and valid after the stream is
+ * synchronised.  Errors and validation as for the quantizer.  The result can
+ * feed grouped_quantize_block_scaled's tensor_sf directly (with one group
+ * covering all rows, the grouped form is the dense form reading its tensor
+ * scale from device memory), so quantization needs no host round trip.
+ */
+int tensor_scale_nvfp4(const void* x, int64_t M, int64_t K, int64_t ldx,
+                       float* tensor_sf_out, void* stream);
+
+int grouped_tensor_scale_nvfp4(const void* x, int64_t num_src_rows, int64_t K, int64_t ldx,
+                               const int32_t* row_indices,
+                               const uint32_t* row_offsets,
+                               const int32_t* expert_ids,
+                               int64_t num_groups, int64_t num_experts, int64_t max_rows,
+                               float* tensor_sf_out, void* stream);
 
 /* Message for the last non-OK status returned on the calling thread ("" if
    none).  The pointer stays valid until the next call on that thread. */

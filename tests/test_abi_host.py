@@ -39,6 +39,8 @@ def lib():
                                           ctypes.c_float, p]
     lib.grouped_quantize_block_scaled.argtypes = [i32, i32, i32, p, i64, i64, i64, p, p, p, p, p,
                                                   i64, i64, i64, i64, p, i64, p, i64, p]
+    lib.tensor_scale_nvfp4.argtypes = [p, i64, i64, i64, p, p]
+    lib.grouped_tensor_scale_nvfp4.argtypes = [p, i64, i64, i64, p, p, p, i64, i64, i64, p, p]
     lib.bsq_last_error.restype = ctypes.c_char_p
     lib.bsq_version.restype = ctypes.c_char_p
     return lib
@@ -47,7 +49,8 @@ def lib():
 def test_header_declares_the_abi():
     assert declared_functions() == sorted(["quantize_block_scaled",
                                            "grouped_quantize_block_scaled", "bsq_last_error",
-                                           "bsq_version"])
+                                           "bsq_version", "tensor_scale_nvfp4",
+                                           "grouped_tensor_scale_nvfp4"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -128,6 +131,28 @@ def test_grouped_validation(lib):
     assert grouped(lib, bs=16) == UNSUPPORTED
     assert grouped(lib, G=0, ro=None, so=None) == OK           # no groups: no-op
     assert grouped(lib, max_rows=0) == OK
+
+
+def test_tensor_scale_validation(lib):
+    ts = lambda **kw: lib.tensor_scale_nvfp4(kw.get("x", FAKE), kw.get("M", 4), kw.get("K", 64),
+                                             kw.get("ldx", 64), kw.get("out", FAKE), None)
+    assert ts(M=-1) == INVALID
+    assert ts(K=40, ldx=40) == INVALID                         # K % 16
+    assert ts(out=None) == INVALID
+    assert ts(out=FAKE + 2) == INVALID
+    assert ts(x=None) == INVALID
+    assert ts(x=FAKE + 8) == INVALID
+    assert ts(ldx=60) == INVALID
+    gts = lambda **kw: lib.grouped_tensor_scale_nvfp4(
+        kw.get("x", FAKE), kw.get("S", 8), 64, 64, kw.get("ri", None), kw.get("ro", FAKE),
+        kw.get("ids", FAKE), kw.get("G", 2), kw.get("E", 4), kw.get("max_rows", 8),
+        kw.get("out", FAKE), None)
+    assert gts(E=0) == INVALID
+    assert gts(G=-1) == INVALID
+    assert gts(ro=None) == INVALID
+    assert gts(ids=None) == INVALID
+    assert gts(max_rows=9) == INVALID                          # no gather: max_rows > S
+    assert gts(out=None) == INVALID
 
 
 def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
