@@ -51,9 +51,36 @@ MUTANTS = [
      "int64_t srow = (int64_t)scales_offsets[g] + (r - (int64_t)row_offsets[g]);",
      "int64_t srow = r;"),
     ("grouped_sf_by_group", "tsf = sf[e];", "tsf = sf[g];"),
-    ("grouped_gather_ignored", "int64_t src = row_indices ? (int64_t)row_indices[r] : r;",
-     "int64_t src = r;"),
+    ("grouped_gather_ignored",
+     "int64_t src = row_indices ? (int64_t)row_indices[r] : r;\n        if (src < 0 || src >= num_src_rows) { bad = 1; continue; }",
+     "int64_t src = r;\n        if (src < 0 || src >= num_src_rows) { bad = 1; continue; }"),
+    # the tensor-scale producer
+    ("tsf_divides_by_448", "float t = (float)amax / 2688.0f;", "float t = (float)amax / 448.0f;"),
+    ("tsf_keeps_specials", "if (!bf16_is_special(x[k]) && bf16_magnitude(x[k]) > amax)",
+     "if (bf16_magnitude(x[k]) > amax)"),
+    ("tsf_zero_gives_zero", "if (amax == 0.0) return 1.0f;", "if (amax == 0.0) return 0.0f;"),
+    ("tsf_no_high_clamp", "    if (t > ldexpf(1.0f, 100)) t = ldexpf(1.0f, 100);\n", ""),
+    ("tsf_low_clamp_wrong", "if (t < ldexpf(1.0f, -117)) t = ldexpf(1.0f, -117);",
+     "if (t < ldexpf(1.0f, -126)) t = ldexpf(1.0f, -126);"),
+    ("grouped_tsf_by_group", "if (expert_ids[g] != e) continue;", "if (g != e) continue;"),
+    ("grouped_tsf_gather_ignored",
+     "int64_t src = row_indices ? (int64_t)row_indices[r] : r;\n                if (src < 0",
+     "int64_t src = r;\n                if (src < 0"),
 ]
+
+
+LO, HI = np.float32(2.0 ** -117), np.float32(2.0 ** 100)
+
+
+def numpy_tensor_scale(x_bits):
+    """The tensor scale from numpy alone: max over the finite |x|, one fp32
+    division by 2688, clamped; 1.0 when that max is 0."""
+    f = W.bf16_to_f32(x_bits).astype(np.float64)
+    f = np.abs(f[np.isfinite(f)])
+    amax = f.max() if f.size else 0.0
+    if amax == 0:
+        return np.float32(1.0)
+    return np.clip(np.float32(amax) / np.float32(2688.0), LO, HI)
 
 
 def build_variant(tmp_path, text, name):
@@ -133,6 +160,21 @@ def run_battery(lib_path, references):
                         np.array_equal(sg[so[g] + r - ro[g]], sd[0])):
                     failed.append(f"grouped:{fmt}")
                     break
+        # tensor-scale producer against numpy
+        with_inf = xs.copy()
+        with_inf[3, 5], with_inf[7, 9] = 0x7F80, 0xFFC0   # Inf and NaN among moderate values
+        for xt in (x, xs, with_inf, np.zeros((2, 32), np.uint16),
+                   np.full((1, 16), 0x7F7F, np.uint16), np.full((1, 16), 0x0001, np.uint16)):
+            if oracle.tensor_scale(xt) != numpy_tensor_scale(xt):
+                failed.append("tsf:dense")
+                break
+        sf_e = oracle.grouped_tensor_scale(xs, ro, ids, 5, row_indices=ri)
+        for e in range(5):
+            rows = [ri[r] for g in range(4) if ids[g] == e for r in range(ro[g], ro[g + 1])]
+            want = numpy_tensor_scale(xs[rows]) if rows else np.float32(1.0)
+            if sf_e[e] != want:
+                failed.append("tsf:grouped")
+                break
     finally:
         oracle._lib = saved
         oracle._LIB_PATH = real_path
