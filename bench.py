@@ -66,6 +66,26 @@ def bytes_per_element(fmt):
     return 2.0 + (1.0 if fmt == 1 else 0.5) + 1.0 / bs
 
 
+# NVFP4 tensor-scale producer steps, measured on the named quantizer input
+PRODUCERS = {"tsf_dense_nvfp4": "dense_nvfp4", "tsf_grouped_nvfp4": "grouped_nvfp4"}
+
+
+def producer_bytes(case):
+    """Bytes one producer step must move: the BF16 rows it reduces (each
+    distinct source row once), the grouping metadata and the fp32 results."""
+    import workloads as W
+    K = case.x.shape[1]
+    if isinstance(case, W.DenseCase):
+        M = case.x.shape[0]
+        return M * K * 2 + 4, M * K
+    lo, hi = int(case.row_offsets[0]), int(case.row_offsets[-1])
+    src = (hi - lo) if case.row_indices is None else np.unique(case.row_indices[lo:hi]).size
+    meta = (case.row_offsets.size + case.expert_ids.size) * 4 + case.tensor_sf.size * 4
+    if case.row_indices is not None:
+        meta += (hi - lo) * 4
+    return int(src * K * 2 + meta), (hi - lo) * K
+
+
 def algorithmic_bytes(case):
     """Bytes one launch must move at minimum (read + written)."""
     import workloads as W
@@ -91,15 +111,17 @@ def algorithmic_bytes(case):
 
 class Runner:
     """Holds NB resident copies of one workload's buffers and launches one
-    step on copy i."""
+    step on copy i (the quantizer, or with ``producer`` the NVFP4 tensor-scale
+    producer on the same input)."""
 
-    def __init__(self, case, nb):
+    def __init__(self, case, nb, producer=False):
         import torch
 
         import fp8_quantization_amd as bsq
         import workloads as W
         self.bsq, self.torch, self.case = bsq, torch, case
         self.grouped = not isinstance(case, W.DenseCase)
+        self.producer = producer
         xd = torch.from_numpy(np.ascontiguousarray(case.x).view(np.int16)).cuda()
         K = case.x.shape[1]
         bs = bsq.BLOCK_SIZE[case.fmt]
@@ -114,10 +136,17 @@ class Runner:
                 s["ids"] = t(case.expert_ids, np.int32)
                 s["sf"] = t(case.tensor_sf, np.float32)
                 s["ri"] = t(case.row_indices, np.int32)
+                if producer:
+                    s["tsf"] = torch.empty(case.tensor_sf.size, dtype=torch.float32,
+                                           device="cuda")
+                    self.sets.append(s)
+                    continue
                 s["q"] = torch.empty((case.max_rows, bsq.code_width(case.fmt, K)),
                                      dtype=torch.uint8, device="cuda")
                 s["s"] = torch.empty((case.num_scale_rows, K // bs), dtype=torch.uint8,
                                      device="cuda")
+            elif producer:
+                s["tsf"] = torch.empty(1, dtype=torch.float32, device="cuda")
             else:
                 M = case.x.shape[0]
                 s["q"] = torch.empty((M, bsq.code_width(case.fmt, K)), dtype=torch.uint8,
@@ -129,7 +158,12 @@ class Runner:
     def step(self, i):
         s = self.sets[i % len(self.sets)]
         c = self.case
-        if self.grouped:
+        if self.producer and self.grouped:
+            self.bsq.grouped_tensor_scale_nvfp4(s["x"], s["ro"], s["ids"], c.tensor_sf.size,
+                                                c.max_rows, row_indices=s["ri"], out=s["tsf"])
+        elif self.producer:
+            self.bsq.tensor_scale_nvfp4(s["x"], out=s["tsf"])
+        elif self.grouped:
             self.bsq.grouped_quantize_block_scaled(
                 s["x"], c.fmt, s["ro"], s["so"], s["ids"], s["sf"], c.max_rows,
                 c.num_scale_rows, row_indices=s["ri"], codes=s["q"], scales=s["s"])
@@ -158,11 +192,12 @@ def time_steps(runner, steps, warmup):
 
 
 def measure(name, steps, warmup, rotate=True):
-    case = load_workload(name)
-    nbytes, elems = algorithmic_bytes(case)
+    producer = name in PRODUCERS
+    case = load_workload(PRODUCERS.get(name, name))
+    nbytes, elems = producer_bytes(case) if producer else algorithmic_bytes(case)
     nb = max(2, -(-3 * MALL_BYTES // max(nbytes, 1)) + 1) if rotate else 1
     nb = min(nb, 64)
-    runner = Runner(case, nb)
+    runner = Runner(case, nb, producer)
     wall, kern = time_steps(runner, steps, warmup)
     return case, runner, nbytes, elems, nb, wall, kern
 
@@ -275,12 +310,15 @@ def main():
     head = summary(args.workload, nbytes, elems, wall, kern, args.steps, nb)
     log("[bench] headline", json.dumps(head))
     achieved = nbytes / (kern * 1e-3) / 1e9
-    traffic, traffic_note = traffic_from_counters(nbytes)
+    if args.workload in PRODUCERS:
+        traffic, traffic_note = None, "counters are taken on the quantizer only"
+    else:
+        traffic, traffic_note = traffic_from_counters(nbytes)
 
     secondary = []
     if not args.no_secondary:
         for name in ("dense_nvfp4", "grouped_nvfp4", "dense_mxfp4", "grouped_mxfp4_decode",
-                     "grouped_mxfp8_decode"):
+                     "grouped_mxfp8_decode", "tsf_dense_nvfp4", "tsf_grouped_nvfp4"):
             if name == args.workload:
                 continue
             c2, r2, nb2, el2, nbs2, w2, k2 = measure(name, args.steps, args.warmup)
@@ -291,7 +329,7 @@ def main():
             torch.cuda.empty_cache()
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload not in PRODUCERS:
         cpu = cpu_baseline(case, runner)
         log("[bench] cpu_baseline", json.dumps(cpu))
 

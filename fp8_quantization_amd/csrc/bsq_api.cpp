@@ -11,6 +11,7 @@
 // ("quantize_dynamic_scaled_async_fp4_kernel", Parameters).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -66,6 +67,38 @@ int tile_knob() {
 int wide_knob() {
     static const int v = env_knob("BSQ_WIDE_LOOKUP");
     return v;
+}
+//   BSQ_TSF_WAVES_PER_CU     tensor-scale reduction: resident waves per CU
+//   BSQ_TSF_WAVES_PER_BLOCK  tensor-scale reduction: waves per workgroup (4, 8, 16)
+constexpr int kTsfWavesPerCu = 16;
+constexpr int kTsfWavesPerBlock = 16;
+int tsf_waves_knob() {
+    static const int v = [] {
+        const int w = env_knob("BSQ_TSF_WAVES_PER_CU");
+        return (w >= 1 && w <= 32) ? w : 0;
+    }();
+    return v;
+}
+int tsf_block_knob() {
+    static const int v = [] {
+        const int w = env_knob("BSQ_TSF_WAVES_PER_BLOCK");
+        return (w == 4 || w == 8 || w == 16) ? w : 0;
+    }();
+    return v;
+}
+
+// Compute units of the current device, read once per device (a launch-shape
+// heuristic only: a wrong count changes speed, never results).
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 
@@ -150,6 +183,28 @@ int st_geometry(bsq::KernelArgs& a, int u, int64_t* blocks) {
         a.tpr_magic_hi = (uint32_t)(m >> 32);
     }
     *blocks = (a.total_tiles + bsq::kWavesPerBlock - 1) / bsq::kWavesPerBlock;
+    return BSQ_OK;
+}
+
+// Tensor-scale reduction: tiles of kTsfChunks chunks, split into contiguous
+// ranges over about waves-per-CU x CUs waves, all resident at once so the
+// grid has no tail of late waves.
+int tsf_geometry(bsq::KernelArgs& a, int64_t* blocks, int* waves_per_block,
+                 uint32_t* tiles_per_wave) {
+    if (st_geometry(a, bsq::kTsfChunks, blocks) != BSQ_OK) return BSQ_ERR_INVALID_ARG;
+    const int wpc = tsf_waves_knob() ? tsf_waves_knob() : kTsfWavesPerCu;
+    const int wpb = tsf_block_knob() ? tsf_block_knob() : kTsfWavesPerBlock;
+    const int64_t target = (int64_t)device_cus() * wpc;
+    const int64_t tpw = (a.total_tiles + target - 1) / target;
+    const int64_t waves = (a.total_tiles + tpw - 1) / tpw;
+    *tiles_per_wave = (uint32_t)tpw;
+    *waves_per_block = wpb;
+    *blocks = (waves + wpb - 1) / wpb;
+    if (log_enabled())
+        std::fprintf(stderr, "[bsq] tensor scale rows=%lld K=%d tiles=%lld tiles/wave=%lld "
+                     "waves=%lld waves/block=%d blocks=%lld\n", (long long)a.rows, a.K,
+                     (long long)a.total_tiles, (long long)tpw, (long long)waves, wpb,
+                     (long long)*blocks);
     return BSQ_OK;
 }
 
@@ -294,8 +349,10 @@ int tensor_scale_nvfp4(const void* x, int64_t M, int64_t K, int64_t ldx, float* 
     a.rows = work ? M : 0;
     a.K = (int32_t)K;
     int64_t blocks = 0;
-    if (work && (st_geometry(a, 4, &blocks) != BSQ_OK)) return BSQ_ERR_INVALID_ARG;
-    const hipError_t e = bsq::launch_tensor_scale(false, a, blocks, tensor_sf_out, 1,
+    uint32_t tpw = 0;
+    int wpb = 0;
+    if (work && tsf_geometry(a, &blocks, &wpb, &tpw) != BSQ_OK) return BSQ_ERR_INVALID_ARG;
+    const hipError_t e = bsq::launch_tensor_scale(false, a, blocks, wpb, tpw, tensor_sf_out, 1,
                                                   static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -346,8 +403,11 @@ int grouped_tensor_scale_nvfp4(const void* x, int64_t num_src_rows, int64_t K, i
     a.num_groups = (int32_t)num_groups;
     a.num_experts = (int32_t)num_experts;
     int64_t blocks = 0;
-    if (work && (st_geometry(a, 4, &blocks) != BSQ_OK)) return BSQ_ERR_INVALID_ARG;
-    const hipError_t e = bsq::launch_tensor_scale(true, a, blocks, tensor_sf_out, (int)num_experts,
+    uint32_t tpw = 0;
+    int wpb = 0;
+    if (work && tsf_geometry(a, &blocks, &wpb, &tpw) != BSQ_OK) return BSQ_ERR_INVALID_ARG;
+    const hipError_t e = bsq::launch_tensor_scale(true, a, blocks, wpb, tpw, tensor_sf_out,
+                                                  (int)num_experts,
                                                   static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -15,6 +15,12 @@ constexpr int kWavesPerBlock = 4;
 constexpr int kThreadsPerBlock = kWaveSize * kWavesPerBlock;
 constexpr int kElemsPerLane = 8;
 constexpr int kChunkElems = kWaveSize * kElemsPerLane;
+// Chunks per tile of the tensor-scale reduction (eight 16-byte loads per lane).
+constexpr int kTsfChunks = 8;
+// Largest workgroup of the tensor-scale reduction, and the most outputs it
+// aggregates in an LDS table per workgroup.
+constexpr int kTsfMaxThreads = 1024;
+constexpr int kTsfLdsSlots = 4096;
 
 struct KernelArgs {
     const uint16_t* x;            // BF16 source rows
@@ -53,7 +59,11 @@ hipError_t launch_quantize(int fmt, bool grouped, const KernelArgs& a, int64_t b
 
 // NVFP4 tensor scale(s) into out[0 .. n_out): zero, amax over the tiles of a
 // (U = 4 chunks per tile; blocks = 0 skips the pass), finish.
-hipError_t launch_tensor_scale(bool grouped, const KernelArgs& a, int64_t blocks, float* out,
-                               int n_out, hipStream_t stream);
+// Zero out[0..n_out), fold the amax of every tile into it (blocks
+// workgroups of waves_per_block waves, each wave taking tiles_per_wave
+// consecutive tiles), and turn each amax into its tensor scale.
+hipError_t launch_tensor_scale(bool grouped, const KernelArgs& a, int64_t blocks,
+                               int waves_per_block, uint32_t tiles_per_wave, float* out, int n_out,
+                               hipStream_t stream);
 
 }  // namespace bsq

@@ -265,6 +265,11 @@ __device__ __forceinline__ LaneOut quantize_lane(const uint4& w, const Nvfp4Wave
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
+// Word 3 of a raw buffer descriptor on gfx9-family chips (32-bit data
+// format; no swizzle, stride 0), and the load's nontemporal cache policy.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kBufferNontemporal = 2;
+
 __device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
     const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
@@ -312,6 +317,22 @@ __device__ __forceinline__ void load4(uint32_t (&v)[4], const uint32_t* __restri
     }
 }
 
+// How many of row_offsets[0..G] are <= r (wave-uniform), 256 offsets per
+// round trip.  For nondecreasing offsets this is one more than the last group
+// starting at or before r.
+__device__ __forceinline__ int offsets_at_or_below(const KernelArgs& a, uint32_t r, int lane) {
+    const int G = a.num_groups;
+    int cnt = 0;
+    for (int base = 0; base <= G; base += 4 * kWaveSize) {
+        uint32_t v[4];
+        const int i = base + 4 * lane;
+        load4(v, a.row_offsets, i, G + 1, 0xFFFFFFFFu);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) cnt += __popcll(__ballot(v[k] <= r && i + k <= G));
+    }
+    return cnt;
+}
+
 // NVFP4 (NEED_SF): with up to 256 experts, the per-expert tensor scales are
 // loaded 4 per lane in the same round trip as the first offsets, and the
 // group's scale is read from registers once its expert id is known.
@@ -323,14 +344,7 @@ __device__ __forceinline__ GroupInfo find_group_narrow(const KernelArgs& a, uint
     const bool sf_regs = NEED_SF && a.num_experts <= 4 * kWaveSize;
     if (sf_regs)
         load4(sf4, reinterpret_cast<const uint32_t*>(a.expert_sf), 4 * lane, a.num_experts, 0u);
-    int cnt = 0;
-    for (int base = 0; base <= G; base += 4 * kWaveSize) {
-        uint32_t v[4];
-        const int i = base + 4 * lane;
-        load4(v, ro, i, G + 1, 0xFFFFFFFFu);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) cnt += __popcll(__ballot(v[k] <= r && i + k <= G));
-    }
+    const int cnt = offsets_at_or_below(a, r, lane);
     GroupInfo gi{-1, 0u, 0u, 0, 1.0f};
     if (cnt == 0 || cnt > G) return gi;
     gi.g = __builtin_amdgcn_readfirstlane(cnt - 1);
@@ -498,10 +512,10 @@ __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const Kernel
 // 2^100].  Three kernels on the caller's stream, using the caller's output
 // array (one float per expert; one for the dense form) as the accumulator:
 //  1. zero it;
-//  2. each wave takes the max |x| of its tile over the finite elements and,
-//     unless a relaxed read of the accumulator already holds as much, folds
-//     it in with an atomic max on the fp32 bit pattern (non-negative floats
-//     order like their patterns), so few waves issue an atomic at all;
+//  2. waves take the max |x| over the finite elements of their rows and,
+//     unless a relaxed read of the accumulator already holds as much, fold it
+//     in with an atomic max on the fp32 bit pattern (non-negative floats
+//     order like their patterns);
 //  3. turn each amax into its tensor scale in place.
 
 __global__ void __launch_bounds__(kThreadsPerBlock) tsf_zero_kernel(uint32_t* acc, int n) {
@@ -539,42 +553,9 @@ __device__ __forceinline__ uint32_t lane_finite_amax_bits(const uint4& w) {
     return best >= 0x80 ? (uint32_t)(best - 0x80) : 0u;
 }
 
-template <bool GROUPED>
-__global__ void __launch_bounds__(kThreadsPerBlock) tsf_amax_kernel(const KernelArgs a, uint32_t* acc) {
-    constexpr int U = 4;
-    const int lane = (int)(threadIdx.x & (kWaveSize - 1));
-    const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock +
-                                                      (threadIdx.x / kWaveSize));
-    if (t >= (uint32_t)a.total_tiles) return;
-    const uint32_t row = div_tiles(t, a);
-    const int c0 = (int)(t - row * (uint32_t)a.tiles_per_row) * U;
-    const int nch = min(U, a.chunks_per_row - c0);
-    int64_t src = row;
-    if constexpr (GROUPED) {
-        if (a.row_indices) {
-            src = a.row_indices[row];
-            if (src < 0 || src >= a.num_src_rows) return;
-        }
-    }
-    const uint16_t* xrow = a.x + src * a.ldx;
-    uint4 w[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const uint32_t col = (uint32_t)((c0 + u) * kChunkElems + lane * kElemsPerLane);
-        w[u] = make_uint4(0u, 0u, 0u, 0u);
-        if (u < nch && col < (uint32_t)a.K) w[u] = load_stream(xrow + col);
-    }
-    int slot = 0;
-    if constexpr (GROUPED) {
-        const GroupInfo gi = find_group_narrow<false>(a, row, lane);
-        if (gi.g < 0) return;
-        slot = a.expert_ids[gi.g];
-        if (slot < 0 || slot >= a.num_experts) return;
-    }
-    uint32_t m = 0;
-#pragma unroll
-    for (int u = 0; u < U; ++u) m = max(m, lane_finite_amax_bits(w[u]));
-    // wave max: DPP within rows of 16, then across the four rows
+// Max over a wave of a per-lane value: DPP within rows of 16 lanes, then the
+// four row results read out.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
     m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, true));
     m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, true));
     m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x114, 0xF, 0xF, true));  // row_shr:4
@@ -583,11 +564,213 @@ __global__ void __launch_bounds__(kThreadsPerBlock) tsf_amax_kernel(const Kernel
     const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)m, 31);
     const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)m, 47);
     const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)m, 63);
-    const uint32_t best = max(max(r0, r1), max(r2, r3)) << 16;  // fp32 pattern of the amax
-    if (lane == 0 && best != 0u) {
-        uint32_t* p = acc + slot;
-        if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < best)
-            __hip_atomic_fetch_max(p, best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return max(max(r0, r1), max(r2, r3));
+}
+
+// Fold amax pattern v into acc[slot] with a device-scope atomic max.  With
+// `check`, a relaxed read first skips the atomic when acc already holds as
+// much (worth it where many blocks share one address, the dense form).
+__device__ __forceinline__ void global_fold(uint32_t* acc, int slot, uint32_t v, bool check) {
+    uint32_t* p = acc + slot;
+    if (check && __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= v) return;
+    __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ int expert_slot(const KernelArgs& a, int g) {
+    const int id = a.expert_ids[g];
+    return (id >= 0 && id < a.num_experts) ? id : -1;
+}
+
+// Step 2.  Each wave walks a contiguous range of tiles_per_wave tiles (of
+// kTsfChunks chunks) in row order, keeping a per-lane running max; the
+// workgroup's waves take consecutive ranges.  In the grouped form a wave
+// carries a cursor over the groups -- found once by counting offsets, then
+// advanced as rows go by -- and flushes its max when the expert changes and
+// at the end.  With at most kTsfLdsSlots outputs a flush is an LDS atomic max
+// into a per-workgroup table; after a barrier the workgroup folds each
+// non-zero entry into the output with one device atomic (the grouped form
+// finds its entries by scanning the groups its waves flushed from: the
+// experts of one workgroup's contiguous rows).  Device atomics on one address
+// are slow when thousands of waves issue them, so this keeps them to about
+// one per workgroup and expert.  With more outputs a flush is a device atomic.
+template <bool GROUPED>
+__global__ void __launch_bounds__(kTsfMaxThreads)
+tsf_amax_kernel(const KernelArgs a, uint32_t* acc, uint32_t tiles_per_wave, int n_out) {
+    constexpr int U = kTsfChunks;
+    extern __shared__ uint32_t s_tab[];  // [n_out] amax table (LDS mode), then the group span
+    const bool lds = n_out <= kTsfLdsSlots;
+    int* s_span = reinterpret_cast<int*>(s_tab + (lds ? n_out : 0));
+    if (lds)
+        for (int i = (int)threadIdx.x; i < n_out; i += (int)blockDim.x) s_tab[i] = 0u;
+    if (threadIdx.x == 0) {
+        s_span[0] = 0x7FFFFFFF;
+        s_span[1] = -1;
+    }
+    __syncthreads();
+
+    const int lane = (int)(threadIdx.x & (kWaveSize - 1));
+    const uint32_t w = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x / kWaveSize) +
+                                                      (threadIdx.x / kWaveSize));
+    // a flush of per-lane maxima m under (slot, from group g)
+    auto flush = [&](int slot, int g, uint32_t m) {
+        const uint32_t best = wave_max_u32(m) << 16;  // fp32 pattern of the amax
+        if (lane != 0 || best == 0u || slot < 0) return;
+        if (lds) {
+            __hip_atomic_fetch_max(s_tab + slot, best, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+            if constexpr (GROUPED) {
+                __hip_atomic_fetch_min(s_span, g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_max(s_span + 1, g, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        } else {
+            global_fold(acc, slot, best, false);
+        }
+    };
+
+    const uint64_t first = (uint64_t)w * tiles_per_wave;
+    bool active = first < (uint64_t)a.total_tiles;
+    uint32_t left = active ? (uint32_t)min((uint64_t)tiles_per_wave,
+                                           (uint64_t)a.total_tiles - first) : 0u;
+    uint32_t row = active ? div_tiles((uint32_t)first, a) : 0u;
+    int c0 = (int)((uint32_t)first - row * (uint32_t)a.tiles_per_row) * U;
+
+    // grouped: g = the last group with row_offsets[g] <= row (-1: none),
+    // hi = row_offsets[g + 1]; slot = its expert (-1: out of range); the
+    // running max belongs to acc_slot, first seen at group acc_g
+    int g = -1, slot = 0, acc_slot = 0, acc_g = 0;
+    uint32_t hi = 0;
+    if constexpr (GROUPED) {
+        if (active) {
+            const int cnt = offsets_at_or_below(a, row, lane);
+            active = cnt <= a.num_groups;  // else at or past the end of the last group
+            g = cnt - 1;
+            if (active) {
+                hi = a.row_offsets[g + 1];
+                slot = g >= 0 ? expert_slot(a, g) : -1;
+            }
+            acc_slot = slot;
+            acc_g = g;
+        }
+    }
+    const bool started = active;
+    // The range's tiles in order.  On entering a row the cursor advances and
+    // the row's source and expert are resolved; a tile is read only when
+    // `use` (owned row, source in range, expert in range).  Past the range,
+    // or past the last group, `done`.
+    struct Tile {
+        const uint16_t* xrow;
+        int cb, slot, g;
+        bool use, done;
+    };
+    const uint16_t* row_ptr = a.x;
+    bool row_use = false;
+    uint32_t row_ready = 0xFFFFFFFFu;
+    auto next = [&]() -> Tile {
+        Tile t{a.x, 0, -1, -1, false, true};
+        if (!active || left == 0) return t;
+        if (row != row_ready) {
+            row_ready = row;
+            int64_t src = row;
+            row_use = true;
+            if constexpr (GROUPED) {
+                bool moved = false;
+                while (row >= hi && g + 1 < a.num_groups) {
+                    ++g;
+                    hi = a.row_offsets[g + 1];
+                    moved = true;
+                }
+                if (row >= hi) {  // rows only grow: nothing later is owned either
+                    active = false;
+                    return t;
+                }
+                if (moved) slot = expert_slot(a, g);
+                row_use = g >= 0 && slot >= 0;
+                if (row_use && a.row_indices) {
+                    src = a.row_indices[row];
+                    row_use = src >= 0 && src < a.num_src_rows;
+                }
+            }
+            row_ptr = row_use ? a.x + src * a.ldx : a.x;
+        }
+        t = Tile{row_ptr, c0, slot, g, row_use, false};
+        --left;
+        c0 += U;
+        if (c0 >= a.chunks_per_row) {
+            c0 = 0;
+            ++row;
+        }
+        return t;
+    };
+    // Eight 16-byte buffer loads per lane through a descriptor that spans
+    // the row from the tile's first element (none for a tile not read):
+    // lanes past the row's end read zeros, which never raise the max, with
+    // no branch and no per-load address registers, so the wait for one
+    // tile's data leaves the next tile's loads in flight.
+    auto issue = [&](const Tile& t, u32x4_t (&v)[U]) {
+        const int bytes = t.use ? (a.K - t.cb * kChunkElems) * 2 : 0;
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(t.xrow + t.cb * kChunkElems), (short)0, bytes, kBufferWord3);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16 + u * kChunkElems * 2, 0,
+                                                         kBufferNontemporal);
+    };
+    uint32_t m = 0;
+    auto reduce = [&](const Tile& t, const u32x4_t (&v)[U]) {
+        if (!t.use) return;
+        if constexpr (GROUPED) {
+            if (t.slot != acc_slot) {
+                flush(acc_slot, acc_g, m);
+                m = 0;
+                acc_slot = t.slot;
+                acc_g = t.g;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            m = max(m, lane_finite_amax_bits(make_uint4(v[u].x, v[u].y, v[u].z, v[u].w)));
+    };
+    // ping-pong over two register sets: load one tile ahead
+    u32x4_t va[U], vb[U];
+    Tile ta = next();
+    if (!ta.done) {
+        issue(ta, va);
+        for (;;) {
+            const Tile tb = next();
+            if (tb.done) {
+                reduce(ta, va);
+                break;
+            }
+            issue(tb, vb);
+            reduce(ta, va);
+            ta = next();
+            if (ta.done) {
+                reduce(tb, vb);
+                break;
+            }
+            issue(ta, va);
+            reduce(tb, vb);
+        }
+    }
+    if (started) flush(acc_slot, acc_g, m);
+    if (!lds) return;  // no barrier follows in this mode
+
+    __syncthreads();
+    if constexpr (!GROUPED) {
+        if (threadIdx.x == 0 && s_tab[0] != 0u) global_fold(acc, 0, s_tab[0], true);
+    } else {
+        // every table entry that is non-zero was flushed from a group in
+        // [span0, span1]; each expert is taken (and cleared) once
+        // (no flush leaves the span empty: span0 = INT_MAX > span1 = -1)
+        const int64_t g0 = max(s_span[0], 0), g1 = min(s_span[1], a.num_groups - 1);
+        for (int64_t gg = g0 + threadIdx.x; gg <= g1; gg += blockDim.x) {
+            const int sl = expert_slot(a, (int)gg);
+            if (sl < 0) continue;
+            const uint32_t v = __hip_atomic_exchange(s_tab + sl, 0u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (v != 0u) global_fold(acc, sl, v, false);
+        }
     }
 }
 
@@ -623,8 +806,9 @@ hipError_t launch_u(const KernelArgs& a, int64_t blocks, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_tensor_scale(bool grouped, const KernelArgs& a, int64_t blocks, float* out,
-                               int n_out, hipStream_t stream) {
+hipError_t launch_tensor_scale(bool grouped, const KernelArgs& a, int64_t blocks,
+                               int waves_per_block, uint32_t tiles_per_wave, float* out, int n_out,
+                               hipStream_t stream) {
     uint32_t* acc = reinterpret_cast<uint32_t*>(out);
     const uint32_t small_blocks = (uint32_t)((n_out + kThreadsPerBlock - 1) / kThreadsPerBlock);
     hipLaunchKernelGGL(tsf_zero_kernel, dim3(small_blocks), dim3(kThreadsPerBlock), 0, stream, acc,
@@ -632,12 +816,14 @@ hipError_t launch_tensor_scale(bool grouped, const KernelArgs& a, int64_t blocks
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (blocks > 0) {
+        const size_t lds_bytes = ((n_out <= kTsfLdsSlots) ? (size_t)n_out : 0u) * 4u + 8u;
+        const dim3 block((uint32_t)(waves_per_block * kWaveSize));
         if (grouped)
-            hipLaunchKernelGGL((tsf_amax_kernel<true>), dim3((uint32_t)blocks),
-                               dim3(kThreadsPerBlock), 0, stream, a, acc);
+            hipLaunchKernelGGL((tsf_amax_kernel<true>), dim3((uint32_t)blocks), block, lds_bytes,
+                               stream, a, acc, tiles_per_wave, n_out);
         else
-            hipLaunchKernelGGL((tsf_amax_kernel<false>), dim3((uint32_t)blocks),
-                               dim3(kThreadsPerBlock), 0, stream, a, acc);
+            hipLaunchKernelGGL((tsf_amax_kernel<false>), dim3((uint32_t)blocks), block, lds_bytes,
+                               stream, a, acc, tiles_per_wave, n_out);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

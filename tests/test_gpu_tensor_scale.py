@@ -26,6 +26,21 @@ def dev(a, dt=np.int16):
     return torch.from_numpy(np.ascontiguousarray(a).view(dt)).cuda()
 
 
+def tame(x):
+    """Keep the NaN/Inf/zero/subnormal specials but map +-max-finite BF16 to
+    +-1.0: one such element would clamp its whole expert's scale to 2^100
+    (covered on its own below), hiding the reduction's other results."""
+    x = x.copy()
+    x[x == 0x7F7F] = 0x3F80
+    x[x == 0xFF7F] = 0xBF80
+    return x
+
+
+def varied(ref, n_nonempty):
+    """The reference takes many distinct values, so a misrouted max shows."""
+    assert len(np.unique(ref)) >= min(n_nonempty, 8) // 2
+
+
 def same_bits(gpu_vals, ref_vals):
     g = np.asarray(gpu_vals, np.float32).view(np.uint32)
     r = np.asarray(ref_vals, np.float32).view(np.uint32)
@@ -37,7 +52,7 @@ def same_bits(gpu_vals, ref_vals):
                                                (300, 1056, (-60, 60), 0.002),
                                                (129, 7168, (-4, 4), 0.0)])
 def test_dense_matches_oracle(bsq, M, K, span, specials):
-    x = W.random_bf16((M, K), seed=M + K, scale_log2_range=span, special_frac=specials)
+    x = tame(W.random_bf16((M, K), seed=M + K, scale_log2_range=span, special_frac=specials))
     out = bsq.tensor_scale_nvfp4(dev(x))
     torch.cuda.synchronize()
     same_bits(out.cpu().numpy(), [oracle.tensor_scale(x)])
@@ -72,7 +87,7 @@ def test_dense_special_cases(bsq):
 def test_grouped_matches_oracle(bsq, G, E, gather, rows):
     rng = np.random.default_rng(G * 7 + E)
     S, K = 1000, 512
-    x = W.random_bf16((S, K), seed=G + 3, scale_log2_range=(-12, 12), special_frac=0.001)
+    x = tame(W.random_bf16((S, K), seed=G + 3, scale_log2_range=(-12, 12), special_frac=0.001))
     w = rng.random(G) * (rng.random(G) > 0.4)
     w[0] += 1e-3
     counts = rng.multinomial(rows, w / w.sum())
@@ -83,7 +98,49 @@ def test_grouped_matches_oracle(bsq, G, E, gather, rows):
     out = bsq.grouped_tensor_scale_nvfp4(dev(x), dev(ro, np.int32), dev(ids, np.int32), E,
                                          max_rows, row_indices=None if ri is None else dev(ri, np.int32))
     torch.cuda.synchronize()
-    same_bits(out.cpu().numpy(), oracle.grouped_tensor_scale(x, ro, ids, E, row_indices=ri))
+    ref = oracle.grouped_tensor_scale(x, ro, ids, E, row_indices=ri)
+    varied(ref, len(np.unique(ids[np.diff(ro) > 0])))
+    same_bits(out.cpu().numpy(), ref)
+
+
+def routed_case(seed, S, K, G, E, rows, gather, empty_frac=0.4, first=2):
+    rng = np.random.default_rng(seed)
+    x = tame(W.random_bf16((S, K), seed=seed + 1, scale_log2_range=(-12, 12),
+                           special_frac=0.0005))
+    w = rng.random(G) * (rng.random(G) > empty_frac)
+    w[0] += 1e-3
+    counts = rng.multinomial(rows, w / w.sum())
+    ro = np.concatenate([[first], first + np.cumsum(counts)]).astype(np.uint32)
+    ids = rng.integers(0, E, G).astype(np.int32)
+    max_rows = int(ro[-1]) + 5
+    ri = rng.integers(0, S, max_rows).astype(np.int32) if gather else None
+    return x, ro, ids, max_rows, ri
+
+
+# Sizes at which every wave of the reduction walks several tiles (its range
+# crosses rows and groups, starts mid-row, and flushes on expert changes), and
+# with more than 4096 experts, where flushes go straight to device atomics.
+@pytest.mark.parametrize("S,K,G,E,rows,gather", [(40000, 512, 600, 9, 39990, False),
+                                                 (30000, 512, 2000, 300, 45000, True),
+                                                 (5000, 7168, 37, 16, 4990, False),
+                                                 (40000, 512, 700, 5000, 39990, False),
+                                                 (20000, 1040, 3000, 6000, 26000, True)])
+def test_grouped_multi_tile_waves(bsq, S, K, G, E, rows, gather):
+    x, ro, ids, max_rows, ri = routed_case(S + G, S, K, G, E, rows, gather)
+    out = bsq.grouped_tensor_scale_nvfp4(dev(x), dev(ro, np.int32), dev(ids, np.int32), E,
+                                         max_rows, row_indices=None if ri is None else dev(ri, np.int32))
+    torch.cuda.synchronize()
+    ref = oracle.grouped_tensor_scale(x, ro, ids, E, row_indices=ri)
+    varied(ref, len(np.unique(ids[np.diff(ro) > 0])))
+    same_bits(out.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("M,K", [(9000, 7168), (5000, 1040), (70000, 512)])
+def test_dense_multi_tile_waves(bsq, M, K):
+    x = tame(W.random_bf16((M, K), seed=M, scale_log2_range=(-30, 30), special_frac=0.0001))
+    out = bsq.tensor_scale_nvfp4(dev(x))
+    torch.cuda.synchronize()
+    same_bits(out.cpu().numpy(), [oracle.tensor_scale(x)])
 
 
 def test_grouped_prefill_workload(bsq):
