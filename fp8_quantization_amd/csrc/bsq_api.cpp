@@ -51,8 +51,7 @@ bool log_enabled() {
 
 // Launch-shape knobs, read once from the environment for sweeps (0 / unset:
 // the built-in choice below):
-//   BSQ_TILE_CHUNKS   chunks of 512 elements per wave: 1, 2, 4 (or 8, grouped)
-//   BSQ_WIDE_LOOKUP   grouped form: 1 one-round-trip group lookup, 2 narrow
+//   BSQ_TILE_CHUNKS   quantizer: chunks of 512 elements per wave (1, 2, 4)
 int env_knob(const char* name) {
     const char* s = std::getenv(name);
     return (s && s[0]) ? std::atoi(s) : 0;
@@ -60,12 +59,8 @@ int env_knob(const char* name) {
 int tile_knob() {
     static const int v = [] {
         const int u = env_knob("BSQ_TILE_CHUNKS");
-        return (u == 1 || u == 2 || u == 4 || u == 8) ? u : 0;
+        return (u == 1 || u == 2 || u == 4) ? u : 0;
     }();
-    return v;
-}
-int wide_knob() {
-    static const int v = env_knob("BSQ_WIDE_LOOKUP");
     return v;
 }
 //   BSQ_TSF_WAVES_PER_CU     tensor-scale reduction: resident waves per CU
@@ -213,28 +208,26 @@ int tsf_geometry(bsq::KernelArgs& a, int64_t* blocks, int* waves_per_block,
 //    Many short waves keep the most loads in flight across the chip and
 //    leave the smallest tail; 1 or 4 chunks per wave, and a persistent grid
 //    walking the tiles, measured slower.
-//  * Grouped, large (more than 2^22 routed elements, bandwidth-bound): the
-//    narrow lookup, with tiles of 8 chunks for NVFP4 (whose per-wave set-up
-//    -- the expert's scale and reciprocal table -- is the largest to
-//    amortise; 51.4 us against 55.4 with 4 chunks on the 16384 x 7168
-//    prefill) and 4 chunks for MXFP4 / MXFP8 (48.7 / 57.1 us against 49.7 /
-//    61.2 with 8).
-//  * Grouped, small (decode-sized, latency-bound): tiles of 1 chunk for the
-//    most parallel waves, with the one-round-trip wide lookup.
+//  * Grouped, large (more than 2^22 routed elements, bandwidth-bound): tiles
+//    of 4 chunks, amortising each wave's group search and (NVFP4) the
+//    expert's reciprocal table.  On the 16384 x 7168 prefill: NVFP4 49.7 us
+//    against 51.8 with 2 chunks and 51.6 with 8; MXFP8 and MXFP4 equal
+//    within noise at 2, 4 and 8.
+//  * Grouped, small (decode-sized, latency-bound): tiles of 1 chunk, for the
+//    most parallel waves.
 int launch(int format, bool grouped, bsq::KernelArgs& a, hipStream_t stream) {
     const bool small = (double)a.rows * (double)a.K <= (double)(1 << 22);
-    int u = grouped ? (small ? 1 : (format == BSQ_NVFP4 ? 8 : 4)) : 2;
-    if (tile_knob() && (tile_knob() != 8 || (grouped && format == BSQ_NVFP4))) u = tile_knob();
-    a.wide_lookup = grouped && (wide_knob() ? wide_knob() == 1 : small);
+    int u = grouped ? (small ? 1 : 4) : 2;
+    if (tile_knob()) u = tile_knob();
     int64_t blocks = 0;
     if (st_geometry(a, u, &blocks) != BSQ_OK) return BSQ_ERR_INVALID_ARG;
     if (log_enabled())
         std::fprintf(stderr,
                      "[bsq] %s %s rows=%lld K=%d chunks/row=%d chunks/tile=%d tiles=%lld "
-                     "blocks=%lld wide_lookup=%d\n",
+                     "blocks=%lld\n",
                      grouped ? "grouped" : "dense", fmt_name(format), (long long)a.rows, a.K,
                      a.chunks_per_row, a.chunks_per_tile, (long long)a.total_tiles,
-                     (long long)blocks, a.wide_lookup);
+                     (long long)blocks);
     const hipError_t e = bsq::launch_quantize(format, grouped, a, blocks, stream);
     if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

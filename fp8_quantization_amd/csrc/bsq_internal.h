@@ -49,7 +49,6 @@ struct KernelArgs {
     int64_t num_scale_rows;
     int32_t num_groups;
     int32_t num_experts;
-    int32_t wide_lookup;          // 1: one-round-trip group lookup (small problems)
 };
 
 // Launch the dense (grouped = false) or grouped kernel for format fmt
@@ -57,11 +56,10 @@ struct KernelArgs {
 hipError_t launch_quantize(int fmt, bool grouped, const KernelArgs& a, int64_t blocks,
                            hipStream_t stream);
 
-// NVFP4 tensor scale(s) into out[0 .. n_out): zero, amax over the tiles of a
-// (U = 4 chunks per tile; blocks = 0 skips the pass), finish.
-// Zero out[0..n_out), fold the amax of every tile into it (blocks
-// workgroups of waves_per_block waves, each wave taking tiles_per_wave
-// consecutive tiles), and turn each amax into its tensor scale.
+// NVFP4 tensor scale(s) into out[0 .. n_out): zero it, fold in the amax of
+// every tile of a (kTsfChunks chunks per tile; blocks workgroups of
+// waves_per_block waves, each wave taking tiles_per_wave consecutive tiles;
+// blocks = 0 skips this pass), and turn each amax into its tensor scale.
 hipError_t launch_tensor_scale(bool grouped, const KernelArgs& a, int64_t blocks,
                                int waves_per_block, uint32_t tiles_per_wave, float* out, int n_out,
                                hipStream_t stream);

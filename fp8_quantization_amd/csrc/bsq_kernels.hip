@@ -13,17 +13,20 @@
 //  * a wave owns a tile of one row: up to chunks_per_tile chunks of 512
 //    elements; lane l holds elements [8l, 8l + 8) of a chunk, fetched with one
 //    16-byte load, so every wave-wide load is 1 KiB contiguous;
-//  * the loads of the next batch of chunks are issued before the current
-//    batch is converted, so each lane keeps several 16-byte loads in flight;
+//  * a wave issues all of its tile's loads before converting any chunk, so
+//    each lane keeps one 16-byte load per chunk in flight;
 //  * a block spans 4 lanes (MX, 32 elements) or 2 lanes (NVFP4, 16); its
 //    amax is an integer max over |BF16| bit patterns, reduced across those
 //    lanes with DPP quad permutes (no LDS, no barrier);
 //  * codes are stored as one dword (FP4) or two dwords (FP8) per lane, so
-//    code stores are contiguous per wave; the first lane of each block
-//    stores its scale byte;
-//  * grouped form: each wave finds its group with a wave-wide ballot over
-//    row_offsets (last g with row_offsets[g] <= r), after its first loads
-//    are already in flight.
+//    code stores are contiguous per wave; every lane of a block holds its
+//    scale byte, and one byte-store instruction writes the scales of up to
+//    4 (MX) or 2 (NVFP4) chunks;
+//  * grouped form: each wave finds its group (last g with row_offsets[g] <=
+//    r) by a binary search on the scalar unit, after its loads are in flight;
+//  * the NVFP4 tensor-scale producer is a separate reduction: persistent
+//    waves over contiguous tile ranges, a per-workgroup LDS table, and one
+//    device atomic max per workgroup and expert.
 //
 // Numerics (identical, byte for byte, to the CPU oracle):
 //  MX:    X = max(floor(log2 amax) - emax, -127) from the amax bit pattern;
@@ -277,16 +280,13 @@ __device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
 
 // The owning group of routed row r and its metadata.  The last g with
 // row_offsets[g] <= r owns r (empty groups repeat an offset and never win).
-// Two ways to find it, chosen by problem size:
-//
-//  * narrow (large problems, bandwidth-bound): one wave-wide pass per 256
-//    offsets (lane l loads row_offsets[4l .. 4l+3], four ballots count the
-//    offsets <= r), then scalar loads of the group's entries: few load
-//    instructions per wave, two dependent round trips;
-//  * wide (small problems, latency-bound): when G < 512, lane l loads
-//    row_offsets, scales_offsets and expert_ids [8l .. 8l+7] at once, eight
-//    ballots find g, and the group's entries are read from the registers of
-//    the lane holding them: one round trip, more load instructions.
+// It is found by a binary search over row_offsets on the scalar unit, then
+// scalar loads of the group's entries: about log2(G) dependent scalar-cache
+// reads, overlapped with the wave's data loads, and no vector memory
+// instruction.  Loading the metadata across the wave's lanes in one round
+// trip (a ballot over 256 or 512 offsets) measured slower at every size: on
+// this chip a wave's vector memory instructions cost more than a short chain
+// of scalar reads.
 struct GroupInfo {
     int g;             // -1: r is before the first or at/after the last group
     uint32_t ro, so;   // row_offsets[g], scales_offsets[g]
@@ -294,114 +294,34 @@ struct GroupInfo {
     float sf;          // expert_sf[id] (NVFP4 only, when id is in range)
 };
 
-// Entry idx (wave-uniform) of an array spread 4 per lane over v.
-__device__ __forceinline__ uint32_t pick4(const uint32_t (&v)[4], int idx) {
-    const int ln = idx >> 2, c = idx & 3;
-    uint32_t out = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t x = (uint32_t)__builtin_amdgcn_readlane((int)v[k], ln);
-        out = (c == k) ? x : out;
-    }
-    return out;
-}
-
-__device__ __forceinline__ void load4(uint32_t (&v)[4], const uint32_t* __restrict__ p, int i,
-                                      int n, uint32_t fill) {
-    if (i + 3 < n && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
-        const uint4 q = *reinterpret_cast<const uint4*>(p + i);
-        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-    } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = (i + k < n) ? p[i + k] : fill;
-    }
-}
-
-// How many of row_offsets[0..G] are <= r (wave-uniform), 256 offsets per
-// round trip.  For nondecreasing offsets this is one more than the last group
-// starting at or before r.
-__device__ __forceinline__ int offsets_at_or_below(const KernelArgs& a, uint32_t r, int lane) {
-    const int G = a.num_groups;
-    int cnt = 0;
-    for (int base = 0; base <= G; base += 4 * kWaveSize) {
-        uint32_t v[4];
-        const int i = base + 4 * lane;
-        load4(v, a.row_offsets, i, G + 1, 0xFFFFFFFFu);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) cnt += __popcll(__ballot(v[k] <= r && i + k <= G));
-    }
-    return cnt;
-}
-
-// NVFP4 (NEED_SF): with up to 256 experts, the per-expert tensor scales are
-// loaded 4 per lane in the same round trip as the first offsets, and the
-// group's scale is read from registers once its expert id is known.
-template <bool NEED_SF>
-__device__ __forceinline__ GroupInfo find_group_narrow(const KernelArgs& a, uint32_t r, int lane) {
+// How many of row_offsets[0..G] are <= r (wave-uniform): an upper-bound
+// binary search on the scalar unit.  For nondecreasing offsets this is one
+// more than the last group starting at or before r.  Every probe index lies
+// in [0, G], whatever the offsets hold.
+__device__ __forceinline__ int offsets_at_or_below(const KernelArgs& a, uint32_t r) {
     const uint32_t* __restrict__ ro = a.row_offsets;
+    int lo = 0, hi = a.num_groups + 1;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (ro[mid] <= r)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    return lo;
+}
+
+template <bool NEED_SF>
+__device__ __forceinline__ GroupInfo find_group_scalar(const KernelArgs& a, uint32_t r) {
     const int G = a.num_groups;
-    uint32_t sf4[4];
-    const bool sf_regs = NEED_SF && a.num_experts <= 4 * kWaveSize;
-    if (sf_regs)
-        load4(sf4, reinterpret_cast<const uint32_t*>(a.expert_sf), 4 * lane, a.num_experts, 0u);
-    const int cnt = offsets_at_or_below(a, r, lane);
+    const int cnt = offsets_at_or_below(a, r);
     GroupInfo gi{-1, 0u, 0u, 0, 1.0f};
     if (cnt == 0 || cnt > G) return gi;
-    gi.g = __builtin_amdgcn_readfirstlane(cnt - 1);
-    gi.ro = ro[gi.g];
+    gi.g = cnt - 1;
+    gi.ro = a.row_offsets[gi.g];
     gi.so = a.scales_offsets[gi.g];
     if constexpr (NEED_SF) {
         gi.id = a.expert_ids[gi.g];
-        if (gi.id >= 0 && gi.id < a.num_experts)
-            gi.sf = sf_regs ? __uint_as_float(pick4(sf4, gi.id)) : a.expert_sf[gi.id];
-    }
-    return gi;
-}
-
-__device__ __forceinline__ void load8(uint32_t (&v)[8], const uint32_t* __restrict__ p, int i,
-                                      int n, uint32_t fill) {
-    if (i + 7 < n && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
-        const uint4 a = *reinterpret_cast<const uint4*>(p + i);
-        const uint4 b = *reinterpret_cast<const uint4*>(p + i + 4);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = (i + k < n) ? p[i + k] : fill;
-    }
-}
-
-// Entry idx (wave-uniform) of an array spread 8 per lane over v.
-__device__ __forceinline__ uint32_t pick8(const uint32_t (&v)[8], int idx) {
-    const int ln = idx >> 3, c = idx & 7;
-    uint32_t out = 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const uint32_t x = (uint32_t)__builtin_amdgcn_readlane((int)v[k], ln);
-        out = (c == k) ? x : out;
-    }
-    return out;
-}
-
-template <bool NEED_ID>
-__device__ __forceinline__ GroupInfo find_group_wide(const KernelArgs& a, uint32_t r, int lane) {
-    const int G = a.num_groups;
-    if (G >= 8 * kWaveSize) return find_group_narrow<NEED_ID>(a, r, lane);
-    GroupInfo gi{-1, 0u, 0u, 0, 1.0f};
-    uint32_t ro[8], so[8], id[8];
-    const int i = 8 * lane;
-    load8(ro, a.row_offsets, i, G + 1, 0xFFFFFFFFu);
-    load8(so, a.scales_offsets, i, G + 1, 0u);
-    if constexpr (NEED_ID) load8(id, reinterpret_cast<const uint32_t*>(a.expert_ids), i, G, 0u);
-    int cnt = 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) cnt += __popcll(__ballot(i + k <= G && ro[k] <= r));
-    if (cnt == 0 || cnt > G) return gi;
-    gi.g = cnt - 1;
-    gi.ro = pick8(ro, gi.g);
-    gi.so = pick8(so, gi.g);
-    if constexpr (NEED_ID) {
-        gi.id = (int32_t)pick8(id, gi.g);
         if (gi.id >= 0 && gi.id < a.num_experts) gi.sf = a.expert_sf[gi.id];
     }
     return gi;
@@ -417,7 +337,7 @@ __device__ __forceinline__ uint32_t div_tiles(uint32_t t, const KernelArgs& a) {
     return (uint32_t)(hi >> 32);
 }
 
-template <int FMT, bool GROUPED, int U, bool WIDE>
+template <int FMT, bool GROUPED, int U>
 __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const KernelArgs a) {
     using T = FormatTraits<FMT>;
     const int lane = (int)(threadIdx.x & (kWaveSize - 1));
@@ -450,8 +370,7 @@ __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const Kernel
     int64_t scale_row = row;
     float tsf = a.tensor_sf;
     if constexpr (GROUPED) {
-        const GroupInfo gi = WIDE ? find_group_wide<FMT == 2>(a, row, lane)
-                                  : find_group_narrow<FMT == 2>(a, row, lane);
+        const GroupInfo gi = find_group_scalar<FMT == 2>(a, row);
         if (gi.g < 0) return;
         scale_row = (int64_t)gi.so + ((int64_t)row - (int64_t)gi.ro);
         if (scale_row < 0 || scale_row >= a.num_scale_rows) return;
@@ -642,7 +561,7 @@ tsf_amax_kernel(const KernelArgs a, uint32_t* acc, uint32_t tiles_per_wave, int 
     uint32_t hi = 0;
     if constexpr (GROUPED) {
         if (active) {
-            const int cnt = offsets_at_or_below(a, row, lane);
+            const int cnt = offsets_at_or_below(a, row);
             active = cnt <= a.num_groups;  // else at or past the end of the last group
             g = cnt - 1;
             if (active) {
@@ -774,32 +693,19 @@ tsf_amax_kernel(const KernelArgs a, uint32_t* acc, uint32_t tiles_per_wave, int 
     }
 }
 
-template <int FMT, bool GROUPED, int U, bool WIDE>
+template <int FMT, bool GROUPED, int U>
 hipError_t launch(const KernelArgs& a, int64_t blocks, hipStream_t stream) {
-    hipLaunchKernelGGL((quantize_kernel<FMT, GROUPED, U, WIDE>), dim3((uint32_t)blocks),
+    hipLaunchKernelGGL((quantize_kernel<FMT, GROUPED, U>), dim3((uint32_t)blocks),
                        dim3(kThreadsPerBlock), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int FMT, bool GROUPED>
 hipError_t launch_u(const KernelArgs& a, int64_t blocks, hipStream_t stream) {
-    if constexpr (GROUPED) {
-        if (a.wide_lookup) {
-            switch (a.chunks_per_tile) {
-                case 1: return launch<FMT, true, 1, true>(a, blocks, stream);
-                case 2: return launch<FMT, true, 2, true>(a, blocks, stream);
-                case 4: return launch<FMT, true, 4, true>(a, blocks, stream);
-                default: return hipErrorInvalidValue;
-            }
-        }
-    }
     switch (a.chunks_per_tile) {
-        case 1: return launch<FMT, GROUPED, 1, false>(a, blocks, stream);
-        case 2: return launch<FMT, GROUPED, 2, false>(a, blocks, stream);
-        case 4: return launch<FMT, GROUPED, 4, false>(a, blocks, stream);
-        case 8:
-            if constexpr (GROUPED && FMT == 2) return launch<FMT, GROUPED, 8, false>(a, blocks, stream);
-            return hipErrorInvalidValue;
+        case 1: return launch<FMT, GROUPED, 1>(a, blocks, stream);
+        case 2: return launch<FMT, GROUPED, 2>(a, blocks, stream);
+        case 4: return launch<FMT, GROUPED, 4>(a, blocks, stream);
         default: return hipErrorInvalidValue;
     }
 }
