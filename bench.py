@@ -326,7 +326,8 @@ def main():
     secondary = []
     if not args.no_secondary:
         for name in ("dense_nvfp4", "grouped_nvfp4", "dense_mxfp4", "grouped_mxfp4_decode",
-                     "grouped_mxfp8_decode", "tsf_dense_nvfp4", "tsf_grouped_nvfp4"):
+                     "grouped_mxfp8_decode", "grouped_mxfp8", "grouped_mxfp4",
+                     "tsf_dense_nvfp4", "tsf_grouped_nvfp4"):
             if name == args.workload:
                 continue
             c2, r2, nb2, el2, nbs2, w2, k2 = measure(name, args.steps, args.warmup)
