@@ -431,10 +431,9 @@ __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const Kernel
 // 2^100].  Three kernels on the caller's stream, using the caller's output
 // array (one float per expert; one for the dense form) as the accumulator:
 //  1. zero it;
-//  2. waves take the max |x| over the finite elements of their rows and,
-//     unless a relaxed read of the accumulator already holds as much, fold it
-//     in with an atomic max on the fp32 bit pattern (non-negative floats
-//     order like their patterns);
+//  2. waves take the max |x| over the finite elements of their rows, and
+//     workgroups fold it in with atomic maxima on the fp32 bit pattern
+//     (non-negative floats order like their patterns);
 //  3. turn each amax into its tensor scale in place.
 
 __global__ void __launch_bounds__(kThreadsPerBlock) tsf_zero_kernel(uint32_t* acc, int n) {
