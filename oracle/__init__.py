@@ -51,6 +51,9 @@ def _load():
     lib.oracle_validate_grouped.restype = i32
     lib.oracle_dequantize.argtypes = [i32, i32, p, i64, i64, i64, p, i64, ctypes.c_float, p]
     lib.oracle_dequantize.restype = i32
+    lib.oracle_block_scaled_matmul.argtypes = [i32, i32, p, i64, p, i64, ctypes.c_float,
+                                               p, i64, p, i64, ctypes.c_float, i64, i64, i64, p]
+    lib.oracle_block_scaled_matmul.restype = i32
     lib.oracle_tensor_scale.argtypes = [p, i64, i64, i64]
     lib.oracle_tensor_scale.restype = ctypes.c_float
     lib.oracle_grouped_tensor_scale.argtypes = [p, i64, i64, i64, p, p, p, i64, i64, p]
@@ -153,6 +156,23 @@ def dequantize(codes, scales, fmt, K, tensor_sf=1.0, bs=None):
     if rc != 0:
         raise ValueError("oracle_dequantize rejected its arguments")
     return out
+
+
+def block_scaled_matmul(a_codes, a_scales, b_codes, b_scales, fmt, K, a_tsf=1.0, b_tsf=1.0,
+                        bs=None):
+    """c = A @ B.T in float64 [M, N], A and B the fp32-rounded dequantized
+    operands ([M, K] and [N, K], blocks along K), summed in ascending k."""
+    lib = _load()
+    bs = BLOCK[fmt] if bs is None else bs
+    M, N = a_codes.shape[0], b_codes.shape[0]
+    c = np.empty((M, N), np.float64)
+    rc = lib.oracle_block_scaled_matmul(
+        fmt, bs, _ptr(a_codes), _ld(a_codes, 1), _ptr(a_scales), _ld(a_scales, 1),
+        float(np.float32(a_tsf)), _ptr(b_codes), _ld(b_codes, 1), _ptr(b_scales),
+        _ld(b_scales, 1), float(np.float32(b_tsf)), M, N, K, _ptr(c))
+    if rc != 0:
+        raise ValueError("oracle_block_scaled_matmul rejected its arguments")
+    return c
 
 
 def tensor_scale(x_bits: np.ndarray) -> np.float32:

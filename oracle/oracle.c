@@ -33,6 +33,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #include <xmmintrin.h>
 #include <float.h>
@@ -376,6 +377,48 @@ int oracle_dequantize(int fmt, int bs, const uint8_t* codes, int64_t M, int64_t 
         }
     }
     return O_OK;
+}
+
+/* Naive block-scaled GEMM, the consumer-side check (the Modular
+   "block_scaled_quantization" module page lists a naive block-scaled matmul
+   as the reference GEMM over such operands).  A and B are both quantized
+   along K ([M, K] and [N, K], the second operand K-major); each is
+   dequantized as above and rounded once to fp32 -- the operands a GEMM
+   consumes -- and c[m * N + n] = sum over k of A[m, k] * B[n, k], summed in
+   double in ascending k.  Each product of two fp32 values is exact in double,
+   so the only roundings are the K - 1 double additions.  A NaN anywhere in
+   row m of A or row n of B makes c[m, n] NaN. */
+int oracle_block_scaled_matmul(int fmt, int bs,
+                               const uint8_t* a_codes, int64_t lda_q, const uint8_t* a_scales,
+                               int64_t lda_s, float a_tsf,
+                               const uint8_t* b_codes, int64_t ldb_q, const uint8_t* b_scales,
+                               int64_t ldb_s, float b_tsf,
+                               int64_t M, int64_t N, int64_t K, double* c) {
+    if (M < 0 || N < 0 || K < 0) return O_BAD;
+    double* A = (double*)malloc((size_t)(M * K + 1) * sizeof(double));
+    double* B = (double*)malloc((size_t)(N * K + 1) * sizeof(double));
+    int rc = O_OK;
+    if (!A || !B) rc = O_BAD;
+    if (rc == O_OK && M > 0 && K > 0)
+        rc = oracle_dequantize(fmt, bs, a_codes, M, K, lda_q, a_scales, lda_s, a_tsf, A);
+    if (rc == O_OK && N > 0 && K > 0)
+        rc = oracle_dequantize(fmt, bs, b_codes, N, K, ldb_q, b_scales, ldb_s, b_tsf, B);
+    if (rc == O_OK) {
+        unsigned int old = enter_ieee();
+        for (int64_t i = 0; i < M * K; ++i) A[i] = (double)(float)A[i];
+        for (int64_t i = 0; i < N * K; ++i) B[i] = (double)(float)B[i];
+        for (int64_t m = 0; m < M; ++m) {
+            for (int64_t n = 0; n < N; ++n) {
+                double sum = 0.0;
+                for (int64_t k = 0; k < K; ++k) sum += A[m * K + k] * B[n * K + k];
+                c[m * N + n] = sum;
+            }
+        }
+        leave_ieee(old);
+    }
+    free(A);
+    free(B);
+    return rc;
 }
 
 /* Tensor scale for NVFP4, the step before the quantizer (the pages take it as

@@ -16,6 +16,7 @@ import pytest
 
 import oracle
 import workloads as W
+from decode_ref import numpy_dequantize, same_f64
 from oracle import build as oracle_build
 from oracle import spec
 
@@ -63,6 +64,16 @@ MUTANTS = [
     ("tsf_low_clamp_wrong", "if (t < ldexpf(1.0f, -117)) t = ldexpf(1.0f, -117);",
      "if (t < ldexpf(1.0f, -126)) t = ldexpf(1.0f, -126);"),
     ("grouped_tsf_by_group", "if (expert_ids[g] != e) continue;", "if (g != e) continue;"),
+    # the consumer side: dequantize and the naive GEMM
+    ("dequant_nvfp4_scale_sign_dropped", "if (fmt == O_NVFP4 && (sb & 0x80)) sc = -sc;", ""),
+    ("dequant_fp4_nibbles_swapped", "c = (k % 2 == 0) ? (b & 0xF) : (b >> 4);",
+     "c = (k % 2 == 0) ? (b >> 4) : (b & 0xF);"),
+    ("gemm_operands_not_rounded", "for (int64_t i = 0; i < M * K; ++i) A[i] = (double)(float)A[i];",
+     ""),
+    ("gemm_b_tsf_from_a", "b_codes, N, K, ldb_q, b_scales, ldb_s, b_tsf, B);",
+     "b_codes, N, K, ldb_q, b_scales, ldb_s, a_tsf, B);"),
+    ("gemm_skips_last_k", "for (int64_t k = 0; k < K; ++k) sum +=",
+     "for (int64_t k = 0; k + 1 < K; ++k) sum +="),
     ("grouped_tsf_gather_ignored",
      "int64_t src = row_indices ? (int64_t)row_indices[r] : r;\n                if (src < 0",
      "int64_t src = r;\n                if (src < 0"),
@@ -175,6 +186,25 @@ def run_battery(lib_path, references):
             if sf_e[e] != want:
                 failed.append("tsf:grouped")
                 break
+        # consumer side: dequantize over every code and scale byte; GEMM vs numpy
+        for fmt, tsf in ((0, 1.0), (1, 1.0), (2, 0.0123)):
+            K = 256 if fmt == 1 else 512
+            codes = np.tile(np.arange(256, dtype=np.uint8), (256, 1))
+            scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], K // oracle.BLOCK[fmt], 1)
+            if not same_f64(oracle.dequantize(codes, scales, fmt, K, tsf),
+                            numpy_dequantize(codes, scales, fmt, K, tsf)):
+                failed.append(f"dequant:{fmt}")
+        g = np.random.default_rng(17)
+        K = 256
+        a_c = g.integers(0, 256, (9, K // 2)).astype(np.uint8)
+        b_c = g.integers(0, 256, (7, K // 2)).astype(np.uint8)
+        a_s = g.integers(0x08, 0x7E, (9, K // 16)).astype(np.uint8)
+        b_s = g.integers(0x08, 0x7E, (7, K // 16)).astype(np.uint8)
+        got = oracle.block_scaled_matmul(a_c, a_s, b_c, b_s, 2, K, 0.0123, 3.5)
+        A = numpy_dequantize(a_c, a_s, 2, K, 0.0123).astype(np.float32).astype(np.float64)
+        B = numpy_dequantize(b_c, b_s, 2, K, 3.5).astype(np.float32).astype(np.float64)
+        if not np.all(np.abs(got - A @ B.T) <= 2 * K * 2.0 ** -53 * (np.abs(A) @ np.abs(B).T)):
+            failed.append("gemm")
     finally:
         oracle._lib = saved
         oracle._LIB_PATH = real_path
