@@ -64,6 +64,10 @@ def load_workload(name):
             name="grouped_mxfp4_prefill_16384x7168_e128"),
         "grouped_mxfp4_decode": lambda: W.grouped_mx_decode(W.MXFP4),
         "grouped_mxfp8_decode": lambda: W.grouped_mx_decode(W.MXFP8),
+        # dequantization of codes and scales of the dense MXFP8 / NVFP4 sizes
+        "dequant_mxfp8": lambda: W.dequant_random_bytes(W.MXFP8, 8192, 7168, seed=1102),
+        "dequant_nvfp4": lambda: W.dequant_random_bytes(W.NVFP4, 16384, 7168, seed=1103,
+                                                        tensor_sf=0.0123),
     }
     return table[name]()
 
@@ -94,9 +98,17 @@ def producer_bytes(case):
     return int(src * K * 2 + meta), (hi - lo) * K
 
 
+def dequant_bytes(case):
+    """Codes and scales read, fp32 values written."""
+    M = case.codes.shape[0]
+    return int(case.codes.nbytes + case.scales.nbytes + 4 * M * case.K), M * case.K
+
+
 def algorithmic_bytes(case):
     """Bytes one launch must move at minimum (read + written)."""
     import workloads as W
+    if isinstance(case, W.DequantCase):
+        return dequant_bytes(case)
     if isinstance(case, W.DenseCase):
         M, K = case.x.shape
         return int(M * K * bytes_per_element(case.fmt)), M * K
@@ -119,8 +131,8 @@ def algorithmic_bytes(case):
 
 class Runner:
     """Holds NB resident copies of one workload's buffers and launches one
-    step on copy i (the quantizer, or with ``producer`` the NVFP4 tensor-scale
-    producer on the same input)."""
+    step on copy i: the quantizer; with ``producer`` the NVFP4 tensor-scale
+    producer on the same input; for a DequantCase the dequantization."""
 
     def __init__(self, case, nb, producer=False):
         import torch
@@ -128,12 +140,22 @@ class Runner:
         import fp8_quantization_amd as bsq
         import workloads as W
         self.bsq, self.torch, self.case = bsq, torch, case
-        self.grouped = not isinstance(case, W.DenseCase)
+        self.dequant = isinstance(case, W.DequantCase)
+        self.grouped = isinstance(case, W.GroupedCase)
         self.producer = producer
+        self.sets = []
+        if self.dequant:
+            codes, scales = torch.from_numpy(case.codes).cuda(), torch.from_numpy(case.scales).cuda()
+            for i in range(nb):
+                self.sets.append({"q": codes if i == 0 else codes.clone(),
+                                  "s": scales if i == 0 else scales.clone(),
+                                  "out": torch.empty((case.codes.shape[0], case.K),
+                                                     dtype=torch.float32, device="cuda")})
+            torch.cuda.synchronize()
+            return
         xd = torch.from_numpy(np.ascontiguousarray(case.x).view(np.int16)).cuda()
         K = case.x.shape[1]
         bs = bsq.BLOCK_SIZE[case.fmt]
-        self.sets = []
         for i in range(nb):
             s = {"x": xd if i == 0 else xd.clone()}
             if self.grouped:
@@ -166,7 +188,9 @@ class Runner:
     def step(self, i):
         s = self.sets[i % len(self.sets)]
         c = self.case
-        if self.producer and self.grouped:
+        if self.dequant:
+            self.bsq.dequantize_block_scaled(s["q"], s["s"], c.fmt, c.K, c.tensor_sf, out=s["out"])
+        elif self.producer and self.grouped:
             self.bsq.grouped_tensor_scale_nvfp4(s["x"], s["ro"], s["ids"], c.tensor_sf.size,
                                                 c.max_rows, row_indices=s["ri"], out=s["tsf"])
         elif self.producer:
@@ -318,7 +342,8 @@ def main():
     head = summary(args.workload, nbytes, elems, wall, kern, args.steps, nb)
     log("[bench] headline", json.dumps(head))
     achieved = nbytes / (kern * 1e-3) / 1e9
-    if args.workload in PRODUCERS:
+    quantizer = args.workload not in PRODUCERS and not args.workload.startswith("dequant_")
+    if not quantizer:
         traffic, traffic_note = None, "counters are taken on the quantizer only"
     else:
         traffic, traffic_note = traffic_from_counters(nbytes)
@@ -327,7 +352,7 @@ def main():
     if not args.no_secondary:
         for name in ("dense_nvfp4", "grouped_nvfp4", "dense_mxfp4", "grouped_mxfp4_decode",
                      "grouped_mxfp8_decode", "grouped_mxfp8", "grouped_mxfp4",
-                     "tsf_dense_nvfp4", "tsf_grouped_nvfp4"):
+                     "tsf_dense_nvfp4", "tsf_grouped_nvfp4", "dequant_mxfp8", "dequant_nvfp4"):
             if name == args.workload:
                 continue
             c2, r2, nb2, el2, nbs2, w2, k2 = measure(name, args.steps, args.warmup)
@@ -338,12 +363,12 @@ def main():
             torch.cuda.empty_cache()
 
     cpu = None
-    if not args.no_cpu_baseline and args.workload not in PRODUCERS:
+    if not args.no_cpu_baseline and quantizer:
         cpu = cpu_baseline(case, runner)
         log("[bench] cpu_baseline", json.dumps(cpu))
 
     fmt_name = {0: "MXFP4", 1: "MXFP8", 2: "NVFP4"}[case.fmt]
-    K = case.x.shape[1]
+    rows, K = (case.codes.shape[0], case.K) if hasattr(case, "codes") else case.x.shape
     line = {
         "metric": METRIC,
         "value": round(nbytes * args.steps / wall / 1e9, 1),
@@ -357,7 +382,7 @@ def main():
         "vs_baseline": None,
         "dtype": "fp32",
         "data": "synthetic",
-        "config": {"workload": case.name, "format": fmt_name, "rows": int(case.x.shape[0]),
+        "config": {"workload": case.name, "format": fmt_name, "rows": int(rows),
                    "K": int(K), "block": bsq.BLOCK_SIZE[case.fmt],
                    "bytes_per_step": nbytes, "buffer_sets_rotated": nb,
                    "version": bsq.version()},

@@ -43,6 +43,12 @@ _lib.tensor_scale_nvfp4.restype = _i32
 _lib.grouped_tensor_scale_nvfp4.argtypes = [_p, _i64, _i64, _i64, _p, _p, _p, _i64, _i64, _i64, _p,
                                             _p]
 _lib.grouped_tensor_scale_nvfp4.restype = _i32
+_lib.dequantize_block_scaled.argtypes = [_i32, _i32, _i32, _p, _i64, _i64, _i64, _p, _i64, _f32,
+                                         _p, _i64, _p]
+_lib.dequantize_block_scaled.restype = _i32
+_lib.block_scaled_matmul_naive.argtypes = [_i32, _i32, _i32, _p, _i64, _p, _i64, _f32, _p, _i64,
+                                           _p, _i64, _f32, _i64, _i64, _i64, _p, _i64, _p]
+_lib.block_scaled_matmul_naive.restype = _i32
 _lib.bsq_last_error.argtypes = []
 _lib.bsq_last_error.restype = ctypes.c_char_p
 _lib.bsq_version.argtypes = []
@@ -201,4 +207,45 @@ def grouped_tensor_scale_nvfp4(x: torch.Tensor, row_offsets: torch.Tensor,
     _check(_lib.grouped_tensor_scale_nvfp4(
         _ptr(x), S, K, _ld(x), _ptr(row_indices), _ptr(row_offsets), _ptr(expert_ids), G,
         num_experts, max_rows, _ptr(out), _stream_ptr(stream, x.device)))
+    return out
+
+
+def _as_code_matrix(name, t):
+    if t.dtype != torch.uint8 or t.dim() != 2 or t.stride(1) != 1 or not t.is_cuda:
+        raise TypeError(f"{name} must be a 2-D row-major uint8 GPU tensor")
+    return t
+
+
+def dequantize_block_scaled(codes: torch.Tensor, scales: torch.Tensor, fmt, K: int,
+                            tensor_sf: float = 1.0, out=None, stream=None):
+    """fp32 [M, K] values of a quantizer's codes ([M, K/2] FP4 or [M, K] FP8)
+    and block scales ([M, K/block_size]); NVFP4 values include tensor_sf."""
+    f = _fmt(fmt)
+    codes, scales = _as_code_matrix("codes", codes), _as_code_matrix("scales", scales)
+    M = codes.shape[0]
+    if scales.shape[0] != M:
+        raise ValueError("codes and scales must have the same number of rows")
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float32, device=codes.device)
+    _check(_lib.dequantize_block_scaled(f, BLOCK_SIZE.get(f, 0), SCALES_ROW_MAJOR, _ptr(codes), M,
+                                        K, _ld(codes), _ptr(scales), _ld(scales), float(tensor_sf),
+                                        _ptr(out), _ld(out), _stream_ptr(stream, codes.device)))
+    return out
+
+
+def block_scaled_matmul_naive(a_codes, a_scales, b_codes, b_scales, fmt, K: int,
+                              a_tsf: float = 1.0, b_tsf: float = 1.0, out=None, stream=None):
+    """Reference GEMM c = A @ B.T (fp32 [M, N]) over two quantizer outputs of
+    one format, both blocked along K; one thread per output, fp32 sums in
+    ascending k.  Not a fast GEMM."""
+    f = _fmt(fmt)
+    a_codes, a_scales = _as_code_matrix("a_codes", a_codes), _as_code_matrix("a_scales", a_scales)
+    b_codes, b_scales = _as_code_matrix("b_codes", b_codes), _as_code_matrix("b_scales", b_scales)
+    M, N = a_codes.shape[0], b_codes.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
+    _check(_lib.block_scaled_matmul_naive(
+        f, BLOCK_SIZE.get(f, 0), SCALES_ROW_MAJOR, _ptr(a_codes), _ld(a_codes), _ptr(a_scales),
+        _ld(a_scales), float(a_tsf), _ptr(b_codes), _ld(b_codes), _ptr(b_scales), _ld(b_scales),
+        float(b_tsf), M, N, K, _ptr(out), _ld(out), _stream_ptr(stream, a_codes.device)))
     return out

@@ -16,7 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbsq.so")
-SOURCES = [os.path.join(CSRC, "bsq_api.cpp"), os.path.join(CSRC, "bsq_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "bsq_api.cpp"), os.path.join(CSRC, "bsq_kernels.hip"),
+           os.path.join(CSRC, "bsq_consume.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

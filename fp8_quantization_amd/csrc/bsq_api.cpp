@@ -51,7 +51,7 @@ bool log_enabled() {
 
 // Launch-shape knobs, read once from the environment for sweeps (0 / unset:
 // the built-in choice below):
-//   BSQ_TILE_CHUNKS   quantizer: chunks of 512 elements per wave (1, 2, 4)
+//   BSQ_TILE_CHUNKS   quantizer, dequantizer: chunks of 512 elements per wave (1, 2, 4)
 int env_knob(const char* name) {
     const char* s = std::getenv(name);
     return (s && s[0]) ? std::atoi(s) : 0;
@@ -113,9 +113,8 @@ int expected_block(int format) {
 }
 
 // Checks shared by both forms.  rows is M (dense) or the source row count.
-int check_common(int format, int block_size, int scale_layout, const void* x, int64_t rows,
-                 int64_t K, int64_t ldx, const void* codes, int64_t ldq, const void* scales,
-                 int64_t lds, bool has_work) {
+// Format, block size, layout and sizes (every entry point).
+int check_layout(int format, int block_size, int scale_layout, int64_t rows, int64_t K) {
     const int bs = expected_block(format);
     if (bs < 0) return fail(BSQ_ERR_UNSUPPORTED, "unknown format %d", format);
     if (block_size != bs)
@@ -130,26 +129,41 @@ int check_common(int format, int block_size, int scale_layout, const void* x, in
         return fail(BSQ_ERR_INVALID_ARG, "K=%lld is not a multiple of the block size %d",
                     (long long)K, bs);
     if (K > (int64_t(1) << 30)) return fail(BSQ_ERR_INVALID_ARG, "K=%lld too large", (long long)K);
-    if (!has_work) return BSQ_OK;
+    return BSQ_OK;
+}
+
+// A codes + scales operand of K elements per row (`what` names it in errors).
+int check_operand(int format, int64_t K, const void* codes, int64_t ldq, const void* scales,
+                  int64_t lds, const char* what) {
+    const int bs = expected_block(format);
     const int64_t code_row = (format == BSQ_MXFP8) ? K : K / 2;
     const int code_align = (format == BSQ_MXFP8) ? 8 : 4;
-    if (!x || !codes || !scales)
-        return fail(BSQ_ERR_INVALID_ARG, "null pointer (x=%p codes=%p scales=%p)", x, codes,
-                    scales);
+    if (!codes || !scales)
+        return fail(BSQ_ERR_INVALID_ARG, "null pointer (%scodes=%p %sscales=%p)", what, codes,
+                    what, scales);
+    if (!aligned(codes, code_align))
+        return fail(BSQ_ERR_INVALID_ARG, "%scodes must be %d-byte aligned for %s", what,
+                    code_align, fmt_name(format));
+    if (ldq < code_row || ldq % code_align != 0)
+        return fail(BSQ_ERR_INVALID_ARG, "%sldq=%lld must be >= %lld and a multiple of %d", what,
+                    (long long)ldq, (long long)code_row, code_align);
+    if (lds < K / bs)
+        return fail(BSQ_ERR_INVALID_ARG, "%slds=%lld must be >= K/block_size=%lld", what,
+                    (long long)lds, (long long)(K / bs));
+    return BSQ_OK;
+}
+
+int check_common(int format, int block_size, int scale_layout, const void* x, int64_t rows,
+                 int64_t K, int64_t ldx, const void* codes, int64_t ldq, const void* scales,
+                 int64_t lds, bool has_work) {
+    const int st = check_layout(format, block_size, scale_layout, rows, K);
+    if (st != BSQ_OK || !has_work) return st;
+    if (!x) return fail(BSQ_ERR_INVALID_ARG, "null pointer (x)");
     if (!aligned(x, 16)) return fail(BSQ_ERR_INVALID_ARG, "x must be 16-byte aligned");
     if (ldx < K || ldx % 8 != 0)
         return fail(BSQ_ERR_INVALID_ARG, "ldx=%lld must be >= K=%lld and a multiple of 8",
                     (long long)ldx, (long long)K);
-    if (!aligned(codes, code_align))
-        return fail(BSQ_ERR_INVALID_ARG, "codes must be %d-byte aligned for %s", code_align,
-                    fmt_name(format));
-    if (ldq < code_row || ldq % code_align != 0)
-        return fail(BSQ_ERR_INVALID_ARG, "ldq=%lld must be >= %lld and a multiple of %d",
-                    (long long)ldq, (long long)code_row, code_align);
-    if (lds < K / bs)
-        return fail(BSQ_ERR_INVALID_ARG, "lds=%lld must be >= K/block_size=%lld", (long long)lds,
-                    (long long)(K / bs));
-    return BSQ_OK;
+    return check_operand(format, K, codes, ldq, scales, lds, "");
 }
 
 bool tsf_in_domain(float t) {
@@ -162,9 +176,11 @@ bool tsf_in_domain(float t) {
 // Tile geometry for a launch with u chunks per tile: fills chunks_per_row,
 // chunks_per_tile, tiles_per_row, total_tiles, the tile->row magic divisor,
 // and the number of 4-wave workgroups.
-int st_geometry(bsq::KernelArgs& a, int u, int64_t* blocks) {
+// Tiles of u chunks over rows x K: chunks and tiles per row, total tiles
+// (< 2^31), the tile->row magic divisor, and workgroups of kWavesPerBlock.
+template <typename Args>
+int tile_geometry(Args& a, int u, int64_t* blocks) {
     a.chunks_per_row = (int32_t)((a.K + bsq::kChunkElems - 1) / bsq::kChunkElems);
-    a.chunks_per_tile = u;
     a.tiles_per_row = (a.chunks_per_row + u - 1) / u;
     a.total_tiles = a.rows * a.tiles_per_row;
     if (a.total_tiles > 0x7FFFFFFFLL)
@@ -179,6 +195,11 @@ int st_geometry(bsq::KernelArgs& a, int u, int64_t* blocks) {
     }
     *blocks = (a.total_tiles + bsq::kWavesPerBlock - 1) / bsq::kWavesPerBlock;
     return BSQ_OK;
+}
+
+int st_geometry(bsq::KernelArgs& a, int u, int64_t* blocks) {
+    a.chunks_per_tile = u;
+    return tile_geometry(a, u, blocks);
 }
 
 // Tensor-scale reduction: tiles of kTsfChunks chunks, split into contiguous
@@ -402,6 +423,87 @@ int grouped_tensor_scale_nvfp4(const void* x, int64_t num_src_rows, int64_t K, i
     const hipError_t e = bsq::launch_tensor_scale(true, a, blocks, wpb, tpw, tensor_sf_out,
                                                   (int)num_experts,
                                                   static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int dequantize_block_scaled(int format, int block_size, int scale_layout, const void* codes,
+                            int64_t M, int64_t K, int64_t ldq, const void* scales, int64_t lds,
+                            float tensor_sf, float* out, int64_t ldo, void* stream) {
+    int st = check_layout(format, block_size, scale_layout, M, K);
+    if (st != BSQ_OK) return st;
+    if (format == BSQ_NVFP4 && !tsf_in_domain(tensor_sf))
+        return fail(BSQ_ERR_INVALID_ARG,
+                    "tensor_sf=%g must be finite and within [2^-117, 2^100]", (double)tensor_sf);
+    if (M == 0 || K == 0) return ok();
+    st = check_operand(format, K, codes, ldq, scales, lds, "");
+    if (st != BSQ_OK) return st;
+    if (!out || !aligned(out, 16))
+        return fail(BSQ_ERR_INVALID_ARG, "out must be a 16-byte aligned device array");
+    if (ldo < K || ldo % 4 != 0)
+        return fail(BSQ_ERR_INVALID_ARG, "ldo=%lld must be >= K=%lld and a multiple of 4",
+                    (long long)ldo, (long long)K);
+    bsq::DequantArgs a{};
+    a.codes = static_cast<const uint8_t*>(codes);
+    a.ldq = ldq;
+    a.scales = static_cast<const uint8_t*>(scales);
+    a.lds = lds;
+    a.out = out;
+    a.ldo = ldo;
+    a.rows = M;
+    a.K = (int32_t)K;
+    a.tensor_sf = tensor_sf;
+    int64_t blocks = 0;
+    a.chunks_per_tile = tile_knob() ? tile_knob() : bsq::kDequantChunks;
+    if (tile_geometry(a, a.chunks_per_tile, &blocks) != BSQ_OK) return BSQ_ERR_INVALID_ARG;
+    const hipError_t e = bsq::launch_dequantize(format, a, blocks, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int block_scaled_matmul_naive(int format, int block_size, int scale_layout,
+                              const void* a_codes, int64_t lda_q, const void* a_scales,
+                              int64_t lda_s, float a_tsf,
+                              const void* b_codes, int64_t ldb_q, const void* b_scales,
+                              int64_t ldb_s, float b_tsf,
+                              int64_t M, int64_t N, int64_t K, float* c, int64_t ldc,
+                              void* stream) {
+    int st = check_layout(format, block_size, scale_layout, M, K);
+    if (st != BSQ_OK) return st;
+    if (N < 0) return fail(BSQ_ERR_INVALID_ARG, "negative size (N=%lld)", (long long)N);
+    if (format == BSQ_NVFP4 && (!tsf_in_domain(a_tsf) || !tsf_in_domain(b_tsf)))
+        return fail(BSQ_ERR_INVALID_ARG,
+                    "a_tsf=%g and b_tsf=%g must be finite and within [2^-117, 2^100]",
+                    (double)a_tsf, (double)b_tsf);
+    if (M == 0 || N == 0) return ok();
+    if (M * N > (int64_t(1) << 38))
+        return fail(BSQ_ERR_INVALID_ARG, "M*N=%lld too large for one launch", (long long)(M * N));
+    if (K > 0) {
+        st = check_operand(format, K, a_codes, lda_q, a_scales, lda_s, "a_");
+        if (st != BSQ_OK) return st;
+        st = check_operand(format, K, b_codes, ldb_q, b_scales, ldb_s, "b_");
+        if (st != BSQ_OK) return st;
+    }
+    if (!c || !aligned(c, 4)) return fail(BSQ_ERR_INVALID_ARG, "c must be a 4-byte aligned device array");
+    if (ldc < N) return fail(BSQ_ERR_INVALID_ARG, "ldc=%lld must be >= N=%lld", (long long)ldc,
+                             (long long)N);
+    bsq::GemmArgs a{};
+    a.a_codes = static_cast<const uint8_t*>(a_codes);
+    a.lda_q = lda_q;
+    a.a_scales = static_cast<const uint8_t*>(a_scales);
+    a.lda_s = lda_s;
+    a.a_tsf = a_tsf;
+    a.b_codes = static_cast<const uint8_t*>(b_codes);
+    a.ldb_q = ldb_q;
+    a.b_scales = static_cast<const uint8_t*>(b_scales);
+    a.ldb_s = ldb_s;
+    a.b_tsf = b_tsf;
+    a.c = c;
+    a.ldc = ldc;
+    a.M = M;
+    a.N = N;
+    a.K = (int32_t)K;
+    const hipError_t e = bsq::launch_naive_matmul(format, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }

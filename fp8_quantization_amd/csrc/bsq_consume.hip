@@ -1,0 +1,233 @@
+// bsq_consume.hip -- gfx950 kernels that read block-scaled codes back: the
+// dequantization to fp32 and a naive block-scaled GEMM (no MFMA), the
+// consumer-side check of the quantizers' output.  The Modular
+// "block_scaled_quantization" module page lists a naive block-scaled matmul
+// as the reference GEMM over such operands; the decode direction of the
+// scales follows the quantizer's readings: an MX value is code * 2^(b - 127),
+// an NVFP4 value is code * s * tensor_sf.
+//
+// Decoding:
+//  * element codes go through gfx950's v_cvt_scalef32_pk_f32_{fp4,fp8} at
+//    scale 1.0 (two codes per instruction, exact; E4M3 NaN codes give NaN);
+//  * MX: the value is that code times the fp32 2^(b - 127) -- exact (every
+//    such product is an fp32 value or overflows to infinity); b = 0xFF is NaN;
+//  * NVFP4: fl32(fl32(code * s) * tensor_sf), where code * s is exact in fp32
+//    (a 2-bit by 4-bit significand product), so the value is the exact
+//    product rounded once; s keeps its sign bit; 0x7F / 0xFF are NaN.
+// Build flags keep IEEE fp32 semantics (no contraction, no denormal flush).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bsq_internal.h"
+
+namespace bsq {
+namespace {
+
+// the conversion builtins return a GCC vector of two floats
+typedef float f32x2_t __attribute__((vector_size(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int c32x2_t __attribute__((ext_vector_type(2)));
+
+// 2^(b - 127) as fp32; b = 0 is the subnormal 2^-127; b = 0xFF is NaN.
+__device__ __forceinline__ float e8m0_f32(uint32_t b) {
+    if (b == 0xFFu) return __uint_as_float(0x7FC00000u);
+    return __uint_as_float(b == 0u ? 0x00400000u : (b << 23));
+}
+
+// The E4M3 value of byte b (sign kept; 0x7F / 0xFF NaN).
+__device__ __forceinline__ float e4m3_f32(uint32_t b) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(b, 1.0f, false)[0];
+}
+
+// Codes of byte / word `SEL` of v as two floats (low element first).
+template <int SEL>
+__device__ __forceinline__ f32x2_t fp4_pair(uint32_t v) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, SEL);
+}
+template <bool HI>
+__device__ __forceinline__ f32x2_t fp8_pair(uint32_t v) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v, 1.0f, HI);
+}
+
+// Eight codes (one lane's share of a chunk) as floats: FP4 in q0, FP8 in q0, q1.
+template <int FMT>
+__device__ __forceinline__ void decode8(uint32_t q0, uint32_t q1, float (&f)[8]) {
+    f32x2_t p[4];
+    if constexpr (FMT == 1) {
+        p[0] = fp8_pair<false>(q0);
+        p[1] = fp8_pair<true>(q0);
+        p[2] = fp8_pair<false>(q1);
+        p[3] = fp8_pair<true>(q1);
+    } else {
+        p[0] = fp4_pair<0>(q0);
+        p[1] = fp4_pair<1>(q0);
+        p[2] = fp4_pair<2>(q0);
+        p[3] = fp4_pair<3>(q0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = p[j][0];
+        f[2 * j + 1] = p[j][1];
+    }
+}
+
+// Scale one decoded code by its block scale byte (and, NVFP4, the tensor scale).
+template <int FMT>
+__device__ __forceinline__ float apply_scale(float code, float scale, float tsf) {
+    if constexpr (FMT == 2) return (code * scale) * tsf;
+    return code * scale;
+}
+
+template <int FMT>
+__device__ __forceinline__ float scale_value(uint32_t b) {
+    if constexpr (FMT == 2) return e4m3_f32(b);
+    return e8m0_f32(b);
+}
+
+__device__ __forceinline__ uint32_t div_rows(uint32_t t, const DequantArgs& a) {
+    if ((a.tpr_magic_lo | a.tpr_magic_hi) == 0) return t;
+    const uint64_t lo = (uint64_t)t * a.tpr_magic_lo;
+    const uint64_t hi = (uint64_t)t * a.tpr_magic_hi + (lo >> 32);
+    return (uint32_t)(hi >> 32);
+}
+
+// Dequantization: one wave per tile of U chunks of one row (512 elements per
+// chunk, lane l holding elements [8l, 8l + 8)).  All of a tile's code and
+// scale loads are issued first; each lane then writes its 8 floats with two
+// 16-byte stores, so every store instruction covers 1 KiB of the output row.
+// The stores are ordinary ones: for this write-heavy stream (4 of every ~4.6
+// bytes) non-temporal 16-byte stores measured at under half the bandwidth.
+template <int FMT, int U>
+__global__ void __launch_bounds__(kThreadsPerBlock) dequant_kernel(const DequantArgs a) {
+    constexpr int kBlock = FMT == 2 ? 16 : 32;
+    const int lane = (int)(threadIdx.x & (kWaveSize - 1));
+    const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock +
+                                                      (threadIdx.x / kWaveSize));
+    if (t >= (uint32_t)a.total_tiles) return;
+    const uint32_t row = div_rows(t, a);
+    const int c0 = (int)(t - row * (uint32_t)a.tiles_per_row) * U;
+    const uint8_t* crow = a.codes + (int64_t)row * a.ldq;
+    const uint8_t* srow = a.scales + (int64_t)row * a.lds;
+    float* orow = a.out + (int64_t)row * a.ldo;
+
+    uint32_t q0[U], q1[U], sb[U];
+    bool in[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t col = (uint32_t)((c0 + u) * kChunkElems + lane * kElemsPerLane);
+        in[u] = c0 + u < a.chunks_per_row && col < (uint32_t)a.K;
+        q0[u] = q1[u] = sb[u] = 0u;
+        if (in[u]) {
+            if constexpr (FMT == 1) {
+                const c32x2_t v = __builtin_nontemporal_load(
+                    reinterpret_cast<const c32x2_t*>(crow + col));
+                q0[u] = v.x;
+                q1[u] = v.y;
+            } else {
+                q0[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(crow + col / 2));
+            }
+            sb[u] = srow[col / kBlock];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (!in[u]) continue;
+        const uint32_t col = (uint32_t)((c0 + u) * kChunkElems + lane * kElemsPerLane);
+        float f[8];
+        decode8<FMT>(q0[u], q1[u], f);
+        const float s = scale_value<FMT>(sb[u]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = apply_scale<FMT>(f[j], s, a.tensor_sf);
+        f32x4_t* o = reinterpret_cast<f32x4_t*>(orow + col);
+        o[0] = (f32x4_t){f[0], f[1], f[2], f[3]};
+        o[1] = (f32x4_t){f[4], f[5], f[6], f[7]};
+    }
+}
+
+// Two consecutive decoded values (k even) of one operand row.
+template <int FMT>
+__device__ __forceinline__ f32x2_t operand_pair(const uint8_t* codes, int k) {
+    if constexpr (FMT == 1) {
+        const uint32_t w = *reinterpret_cast<const uint16_t*>(codes + k);
+        return fp8_pair<false>(w);
+    } else {
+        return fp4_pair<0>((uint32_t)codes[k / 2]);
+    }
+}
+
+// Naive GEMM: one thread per output c[m, n] = sum over k of A[m, k] * B[n, k]
+// (both operands K-major, dequantized on the fly exactly as above), summed in
+// fp32 in ascending k as acc = acc + a * b.
+template <int FMT>
+__global__ void __launch_bounds__(kThreadsPerBlock) naive_matmul_kernel(const GemmArgs a) {
+    constexpr int kBlock = FMT == 2 ? 16 : 32;
+    const int64_t idx = (int64_t)blockIdx.x * kThreadsPerBlock + threadIdx.x;
+    if (idx >= a.M * a.N) return;
+    const int64_t m = idx / a.N, n = idx - m * a.N;
+    const uint8_t* ac = a.a_codes + m * a.lda_q;
+    const uint8_t* as = a.a_scales + m * a.lda_s;
+    const uint8_t* bc = a.b_codes + n * a.ldb_q;
+    const uint8_t* bs = a.b_scales + n * a.ldb_s;
+    float acc = 0.0f;
+    for (int kb = 0; kb < a.K / kBlock; ++kb) {
+        const float sa = scale_value<FMT>(as[kb]);
+        const float sb = scale_value<FMT>(bs[kb]);
+        for (int k = kb * kBlock; k < (kb + 1) * kBlock; k += 2) {
+            const f32x2_t ca = operand_pair<FMT>(ac, k);
+            const f32x2_t cb = operand_pair<FMT>(bc, k);
+            acc = acc + apply_scale<FMT>(ca[0], sa, a.a_tsf) * apply_scale<FMT>(cb[0], sb, a.b_tsf);
+            acc = acc + apply_scale<FMT>(ca[1], sa, a.a_tsf) * apply_scale<FMT>(cb[1], sb, a.b_tsf);
+        }
+    }
+    a.c[m * a.ldc + n] = acc;
+}
+
+template <int FMT>
+hipError_t launch_dq(const DequantArgs& a, int64_t blocks, hipStream_t stream) {
+    switch (a.chunks_per_tile) {
+        case 1:
+            hipLaunchKernelGGL((dequant_kernel<FMT, 1>), dim3((uint32_t)blocks),
+                               dim3(kThreadsPerBlock), 0, stream, a);
+            break;
+        case 2:
+            hipLaunchKernelGGL((dequant_kernel<FMT, 2>), dim3((uint32_t)blocks),
+                               dim3(kThreadsPerBlock), 0, stream, a);
+            break;
+        case 4:
+            hipLaunchKernelGGL((dequant_kernel<FMT, 4>), dim3((uint32_t)blocks),
+                               dim3(kThreadsPerBlock), 0, stream, a);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_mm(const GemmArgs& a, hipStream_t stream) {
+    const int64_t blocks = (a.M * a.N + kThreadsPerBlock - 1) / kThreadsPerBlock;
+    hipLaunchKernelGGL((naive_matmul_kernel<FMT>), dim3((uint32_t)blocks), dim3(kThreadsPerBlock),
+                       0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dequantize(int fmt, const DequantArgs& a, int64_t blocks, hipStream_t stream) {
+    switch (fmt) {
+        case 0: return launch_dq<0>(a, blocks, stream);
+        case 1: return launch_dq<1>(a, blocks, stream);
+        case 2: return launch_dq<2>(a, blocks, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_naive_matmul(int fmt, const GemmArgs& a, hipStream_t stream) {
+    switch (fmt) {
+        case 0: return launch_mm<0>(a, stream);
+        case 1: return launch_mm<1>(a, stream);
+        case 2: return launch_mm<2>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace bsq

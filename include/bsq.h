@@ -179,6 +179,54 @@ int grouped_tensor_scale_nvfp4(const void* x, int64_t num_src_rows, int64_t K, i
                                int64_t num_groups, int64_t num_experts, int64_t max_rows,
                                float* tensor_sf_out, void* stream);
 
+/*
+ * Dequantization, the decode direction of the formats above: the consumer-
+ * side check that codes and scales are usable as GEMM operands (the
+ * "block_scaled_quantization" module page lists a naive block-scaled matmul
+ * as the reference GEMM over such operands).
+ *
+ *   out[r, k] = fl32(value of code (r, k) times its block scale), where the
+ *   block scale is 2^(b - 127) for MX (b = 0xFF: NaN) and s * tensor_sf for
+ *   NVFP4 (s the E4M3 scale byte with its sign; 0x7F / 0xFF: NaN).  MX values
+ *   are exact (or overflow to infinity for scale bytes no quantizer above
+ *   writes); NVFP4 values are the exact product rounded once.  E4M3 element
+ *   codes 0x7F / 0xFF decode to NaN; FP4 codes keep their sign (0x8 is -0).
+ *
+ *   format, block_size, scale_layout   as for quantize_block_scaled.
+ *   codes, ldq, scales, lds, M, K      a quantizer's output (same layout,
+ *                                      alignment and stride rules).
+ *   tensor_sf                          NVFP4 only, same domain as the quantizer.
+ *   out, ldo                           fp32 [M, ldo], 16-byte aligned,
+ *                                      ldo >= K and ldo % 4 == 0 (elements).
+ *   M == 0 or K == 0 is a no-op.
+ */
+int dequantize_block_scaled(int format, int block_size, int scale_layout,
+                            const void* codes, int64_t M, int64_t K, int64_t ldq,
+                            const void* scales, int64_t lds, float tensor_sf,
+                            float* out, int64_t ldo, void* stream);
+
+/*
+ * Naive block-scaled GEMM (no matrix cores): c[m, n] = sum over k of
+ * A[m, k] * B[n, k], where A ([M, K]) and B ([N, K]) are two quantizer
+ * outputs of one format, both blocked along K (B is K-major, i.e. the GEMM
+ * computes A B^T), dequantized exactly as dequantize_block_scaled does.  Each
+ * thread computes one c[m, n], summing fl32(a * b) into an fp32 accumulator
+ * in ascending k.  A reference consumer, not a fast GEMM.
+ *
+ *   a_codes, lda_q, a_scales, lda_s, a_tsf   operand A (a_tsf: NVFP4 only)
+ *   b_codes, ldb_q, b_scales, ldb_s, b_tsf   operand B
+ *   M, N, K        M, N >= 0; K % block_size == 0; M * N <= 2^38
+ *   c, ldc         fp32 [M, ldc], 4-byte aligned, ldc >= N
+ *   M == 0 or N == 0 is a no-op; K == 0 writes zeros.
+ */
+int block_scaled_matmul_naive(int format, int block_size, int scale_layout,
+                              const void* a_codes, int64_t lda_q, const void* a_scales,
+                              int64_t lda_s, float a_tsf,
+                              const void* b_codes, int64_t ldb_q, const void* b_scales,
+                              int64_t ldb_s, float b_tsf,
+                              int64_t M, int64_t N, int64_t K, float* c, int64_t ldc,
+                              void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if
    none).  The pointer stays valid until the next call on that thread. */
 const char* bsq_last_error(void);

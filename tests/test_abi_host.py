@@ -41,6 +41,11 @@ def lib():
                                                   i64, i64, i64, i64, p, i64, p, i64, p]
     lib.tensor_scale_nvfp4.argtypes = [p, i64, i64, i64, p, p]
     lib.grouped_tensor_scale_nvfp4.argtypes = [p, i64, i64, i64, p, p, p, i64, i64, i64, p, p]
+    lib.dequantize_block_scaled.argtypes = [i32, i32, i32, p, i64, i64, i64, p, i64,
+                                            ctypes.c_float, p, i64, p]
+    lib.block_scaled_matmul_naive.argtypes = [i32, i32, i32, p, i64, p, i64, ctypes.c_float, p,
+                                              i64, p, i64, ctypes.c_float, i64, i64, i64, p, i64,
+                                              p]
     lib.bsq_last_error.restype = ctypes.c_char_p
     lib.bsq_version.restype = ctypes.c_char_p
     return lib
@@ -50,7 +55,9 @@ def test_header_declares_the_abi():
     assert declared_functions() == sorted(["quantize_block_scaled",
                                            "grouped_quantize_block_scaled", "bsq_last_error",
                                            "bsq_version", "tensor_scale_nvfp4",
-                                           "grouped_tensor_scale_nvfp4"])
+                                           "grouped_tensor_scale_nvfp4",
+                                           "dequantize_block_scaled",
+                                           "block_scaled_matmul_naive"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -153,6 +160,55 @@ def test_tensor_scale_validation(lib):
     assert gts(ids=None) == INVALID
     assert gts(max_rows=9) == INVALID                          # no gather: max_rows > S
     assert gts(out=None) == INVALID
+
+
+def test_dequantize_validation(lib):
+    def dq(fmt=MXFP4, bs=32, layout=0, codes=FAKE, M=4, K=64, ldq=None, scales=FAKE, lds=None,
+           tsf=1.0, out=FAKE, ldo=64):
+        ldq = (K if fmt == MXFP8 else K // 2) if ldq is None else ldq
+        lds = K // max(bs, 1) if lds is None else lds
+        return lib.dequantize_block_scaled(fmt, bs, layout, codes, M, K, ldq, scales, lds, tsf,
+                                           out, ldo, None)
+    assert dq(bs=16) == UNSUPPORTED
+    assert dq(layout=1) == UNSUPPORTED
+    assert dq(M=-1) == INVALID
+    assert dq(K=48, ldo=48) == INVALID                         # K % 32
+    assert dq(codes=None) == INVALID
+    assert dq(scales=None) == INVALID
+    assert dq(codes=FAKE + 2) == INVALID                       # FP4 codes 4-byte aligned
+    assert dq(fmt=MXFP8, codes=FAKE + 4) == INVALID            # FP8 codes 8-byte aligned
+    assert dq(ldq=30) == INVALID
+    assert dq(lds=1) == INVALID
+    assert dq(out=None) == INVALID
+    assert dq(out=FAKE + 8) == INVALID                         # 16-byte aligned
+    assert dq(ldo=60) == INVALID                               # ldo < K
+    assert dq(ldo=66) == INVALID                               # ldo % 4
+    assert dq(fmt=NVFP4, bs=16, tsf=0.0) == INVALID
+    assert dq(M=0, codes=None, scales=None, out=None) == OK
+    assert dq(K=0, ldq=0, lds=0, codes=None, scales=None, out=None) == OK
+
+
+def test_naive_matmul_validation(lib):
+    def mm(fmt=MXFP4, bs=32, M=4, N=3, K=64, a=FAKE, b=FAKE, c=FAKE, ldc=3, ta=1.0, tb=1.0,
+           ldq=None):
+        ldq = (K if fmt == MXFP8 else K // 2) if ldq is None else ldq
+        lds = K // max(bs, 1)
+        return lib.block_scaled_matmul_naive(fmt, bs, 0, a, ldq, FAKE, lds, ta, b, ldq, FAKE,
+                                             lds, tb, M, N, K, c, ldc, None)
+    assert mm(bs=16) == UNSUPPORTED
+    assert mm(N=-1) == INVALID
+    assert mm(K=40) == INVALID
+    assert mm(a=None) == INVALID
+    assert mm(b=None) == INVALID
+    assert mm(c=None) == INVALID
+    assert mm(c=FAKE + 2) == INVALID
+    assert mm(ldc=2) == INVALID
+    assert mm(ldq=30) == INVALID
+    assert mm(fmt=NVFP4, bs=16, ta=float("nan")) == INVALID
+    assert mm(fmt=NVFP4, bs=16, tb=2.0 ** 101) == INVALID
+    assert mm(M=1 << 20, N=1 << 19) == INVALID                 # M * N > 2^38
+    assert mm(M=0, a=None, b=None, c=None) == OK
+    assert mm(N=0, a=None, b=None, c=None) == OK
 
 
 def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):

@@ -174,6 +174,29 @@ def grouped_mx_decode(fmt: int = MXFP4, seed: int = 1005, tokens: int = 64, K: i
 
 # ------------------------------------------------------------ sweep inputs
 
+@dataclass
+class DequantCase:
+    """Block-scaled codes and scales to decode (random bytes: every code and
+    scale pattern, NaN and overflow ones included, appears)."""
+    name: str
+    fmt: int
+    codes: np.ndarray                  # uint8 [M, K/2] (FP4) or [M, K] (FP8)
+    scales: np.ndarray                 # uint8 [M, K/block]
+    K: int
+    tensor_sf: float = 1.0
+
+
+def dequant_random_bytes(fmt: int, M: int, K: int, seed: int,
+                         tensor_sf: float = 1.0) -> DequantCase:
+    rng = np.random.default_rng(seed)
+    bs = 16 if fmt == NVFP4 else 32
+    width = K if fmt == MXFP8 else K // 2
+    codes = rng.integers(0, 256, (M, width), dtype=np.uint8)
+    scales = rng.integers(0, 256, (M, K // bs), dtype=np.uint8)
+    name = {MXFP4: "mxfp4", MXFP8: "mxfp8", NVFP4: "nvfp4"}[fmt]
+    return DequantCase(f"dequant_{name}_{M}x{K}", fmt, codes, scales, K, tensor_sf)
+
+
 def sweep_matrix(bs: int, background: str = "zeros", anchor_bits: int = 0,
                  seed: int = 0) -> np.ndarray:
     """[bs * 65536, bs] BF16 patterns.  Row p * 65536 + h holds pattern h at
