@@ -54,6 +54,10 @@ def _load():
     lib.oracle_block_scaled_matmul.argtypes = [i32, i32, p, i64, p, i64, ctypes.c_float,
                                                p, i64, p, i64, ctypes.c_float, i64, i64, i64, p]
     lib.oracle_block_scaled_matmul.restype = i32
+    lib.oracle_mfma16_scale_offset.argtypes = [i64, i64, i64]
+    lib.oracle_mfma16_scale_offset.restype = i64
+    lib.oracle_scales_to_mfma16.argtypes = [p, i64, i64, i64, p, i64]
+    lib.oracle_scales_to_mfma16.restype = i32
     lib.oracle_tensor_scale.argtypes = [p, i64, i64, i64]
     lib.oracle_tensor_scale.restype = ctypes.c_float
     lib.oracle_grouped_tensor_scale.argtypes = [p, i64, i64, i64, p, p, p, i64, i64, p]
@@ -173,6 +177,29 @@ def block_scaled_matmul(a_codes, a_scales, b_codes, b_scales, fmt, K, a_tsf=1.0,
     if rc != 0:
         raise ValueError("oracle_block_scaled_matmul rejected its arguments")
     return c
+
+
+def mfma16_scale_bytes(rows: int, nblk: int) -> int:
+    """Row-group stride (bytes) of the packed MFMA scale layout: 256 bytes per
+    16 rows x 512 elements record."""
+    return ((nblk + 15) // 16) * 256
+
+
+def mfma16_scale_offset(r: int, kb: int, lds: int) -> int:
+    return _load().oracle_mfma16_scale_offset(r, kb, lds)
+
+
+def scales_to_mfma16(scales_rm: np.ndarray, lds_out=None, fill=0) -> np.ndarray:
+    """Row-major scales [rows, nblk] in the MFMA 16x16x128 layout: uint8
+    [ceil(rows / 16), lds_out] (bytes no scale lands in hold ``fill``)."""
+    lib = _load()
+    rows, nblk = scales_rm.shape
+    lds_out = mfma16_scale_bytes(rows, nblk) if lds_out is None else lds_out
+    out = np.full(((rows + 15) // 16, lds_out), fill, np.uint8)
+    src = np.ascontiguousarray(scales_rm)
+    if lib.oracle_scales_to_mfma16(_ptr(src), rows, nblk, nblk, _ptr(out), lds_out) != 0:
+        raise ValueError("oracle_scales_to_mfma16 rejected its arguments")
+    return out
 
 
 def tensor_scale(x_bits: np.ndarray) -> np.float32:

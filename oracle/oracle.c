@@ -379,6 +379,40 @@ int oracle_dequantize(int fmt, int bs, const uint8_t* codes, int64_t M, int64_t 
     return O_OK;
 }
 
+/* Scale layout for the gfx950 scaled matrix instruction
+   v_mfma_scale_f32_16x16x128_f8f6f4 (MX formats; 32-element blocks, E8M0).
+   That instruction takes, in each of the 64 lanes, one 32-bit register of
+   scale bytes and a byte selector: the scale of A row r (0..15) and K-block
+   q (0..3) of its 128-element K step comes from lane r + 16 q.  (Measured on
+   the hardware with one-wave probes of known operands, for FP4 and FP8, both
+   16x16x128 and 32x32x64 shapes; the pages describe only the SM100
+   interleave.)  The layout packs four K steps into each lane's register:
+   rows in groups of 16 and blocks in groups of 16 (512 elements) form one
+   256-byte record, record (r / 16, kb / 16) at byte offset
+   (r / 16) * lds + (kb / 16) * 256, and inside it the byte of (r, kb) at
+   4 * ((r % 16) + 16 * (kb % 4)) + (kb % 16) / 4.  A GEMM wave loads one dword
+   per lane per record and feeds byte t to the t-th of four instructions.
+
+   mfma16_scale_offset gives that byte offset; oracle_scales_to_mfma16 copies
+   row-major scales [rows, nblk] (stride lds_rm) into the layout (row-group
+   stride lds_out bytes); bytes of incomplete records are left untouched. */
+static int64_t mfma16_scale_offset(int64_t r, int64_t kb, int64_t lds) {
+    return (r / 16) * lds + (kb / 16) * 256 + 4 * ((r % 16) + 16 * (kb % 4)) + (kb % 16) / 4;
+}
+
+int64_t oracle_mfma16_scale_offset(int64_t r, int64_t kb, int64_t lds) {
+    return mfma16_scale_offset(r, kb, lds);
+}
+
+int oracle_scales_to_mfma16(const uint8_t* scales_rm, int64_t rows, int64_t nblk, int64_t lds_rm,
+                            uint8_t* out, int64_t lds_out) {
+    if (rows < 0 || nblk < 0 || lds_rm < nblk || lds_out < ((nblk + 15) / 16) * 256) return O_BAD;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t kb = 0; kb < nblk; ++kb)
+            out[mfma16_scale_offset(r, kb, lds_out)] = scales_rm[r * lds_rm + kb];
+    return O_OK;
+}
+
 /* Naive block-scaled GEMM, the consumer-side check (the Modular
    "block_scaled_quantization" module page lists a naive block-scaled matmul
    as the reference GEMM over such operands).  A and B are both quantized

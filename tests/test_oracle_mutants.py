@@ -74,6 +74,11 @@ MUTANTS = [
      "b_codes, N, K, ldb_q, b_scales, ldb_s, a_tsf, B);"),
     ("gemm_skips_last_k", "for (int64_t k = 0; k < K; ++k) sum +=",
      "for (int64_t k = 0; k + 1 < K; ++k) sum +="),
+    # the MFMA scale layout
+    ("mfma_lane_and_byte_swapped",
+     "4 * ((r % 16) + 16 * (kb % 4)) + (kb % 16) / 4;",
+     "4 * ((r % 16) + 16 * ((kb % 16) / 4)) + kb % 4;"),
+    ("mfma_record_stride", "(kb / 16) * 256 +", "(kb / 16) * 128 +"),
     ("grouped_tsf_gather_ignored",
      "int64_t src = row_indices ? (int64_t)row_indices[r] : r;\n                if (src < 0",
      "int64_t src = r;\n                if (src < 0"),
@@ -205,6 +210,20 @@ def run_battery(lib_path, references):
         B = numpy_dequantize(b_c, b_s, 2, K, 3.5).astype(np.float32).astype(np.float64)
         if not np.all(np.abs(got - A @ B.T) <= 2 * K * 2.0 ** -53 * (np.abs(A) @ np.abs(B).T)):
             failed.append("gemm")
+        # MFMA scale layout, seen from the lanes: K step T, lane L holds (L % 16, 4T + L // 16)
+        sc = g.integers(0, 256, (20, 40)).astype(np.uint8)
+        lay = oracle.scales_to_mfma16(sc, fill=0xEE)
+        ok = True
+        for grp in range(lay.shape[0]):
+            for rec in range(lay.shape[1] // 256):
+                dw = lay[grp, rec * 256:(rec + 1) * 256].reshape(64, 4)
+                for L in range(64):
+                    for T in range(4):
+                        r, kb = 16 * grp + L % 16, 16 * rec + 4 * T + L // 16
+                        want = sc[r, kb] if r < 20 and kb < 40 else 0xEE
+                        ok &= bool(dw[L, T] == want)
+        if not ok:
+            failed.append("mfma_layout")
     finally:
         oracle._lib = saved
         oracle._LIB_PATH = real_path
