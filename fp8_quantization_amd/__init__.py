@@ -20,7 +20,7 @@ import torch
 
 MXFP4, MXFP8, NVFP4 = 0, 1, 2
 BLOCK_SIZE = {MXFP4: 32, MXFP8: 32, NVFP4: 16}
-SCALES_ROW_MAJOR = 0
+SCALES_ROW_MAJOR, SCALES_MFMA16 = 0, 1
 FORMAT_NAMES = {"mxfp4": MXFP4, "mxfp8": MXFP8, "nvfp4": NVFP4}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsq.so")
@@ -86,6 +86,17 @@ def code_width(fmt, K: int) -> int:
     return K if _fmt(fmt) == MXFP8 else K // 2
 
 
+def scale_shape(fmt, rows: int, K: int, scale_layout: int = SCALES_ROW_MAJOR):
+    """Shape of a uint8 scales buffer for rows x K: [rows, K/block_size]
+    row-major, or [ceil(rows/16), 256 * ceil(K/512)] in the MFMA layout (one
+    256-byte record per 16 rows x 512 elements)."""
+    f = _fmt(fmt)
+    nblk = K // BLOCK_SIZE[f] if f in BLOCK_SIZE else 0
+    if scale_layout == SCALES_MFMA16:
+        return ((rows + 15) // 16, ((nblk + 15) // 16) * 256)
+    return (rows, nblk)
+
+
 def _stream_ptr(stream, device):
     s = stream if stream is not None else torch.cuda.current_stream(device)
     return ctypes.c_void_p(s.cuda_stream)
@@ -110,11 +121,12 @@ def _as_bf16_matrix(x: torch.Tensor) -> torch.Tensor:
 
 
 def quantize_block_scaled(x: torch.Tensor, fmt, tensor_sf: float = 1.0, codes=None, scales=None,
-                          stream=None):
+                          stream=None, scale_layout: int = SCALES_ROW_MAJOR):
     """Dense form.  x: BF16 [M, K] on the GPU.  Returns (codes, scales):
-    uint8 [M, K/2] (FP4) or [M, K] (FP8), and uint8 [M, K/block_size].
-    ``tensor_sf`` is the fp32 NVFP4 tensor scale (ignored for MX).  Output
-    tensors may be passed in (any row stride the C ABI accepts)."""
+    uint8 [M, K/2] (FP4) or [M, K] (FP8), and the scales in ``scale_layout``
+    (``scale_shape``).  ``tensor_sf`` is the fp32 NVFP4 tensor scale (ignored
+    for MX).  Output tensors may be passed in (any row stride the C ABI
+    accepts)."""
     f = _fmt(fmt)
     x = _as_bf16_matrix(x)
     M, K = x.shape
@@ -122,8 +134,9 @@ def quantize_block_scaled(x: torch.Tensor, fmt, tensor_sf: float = 1.0, codes=No
     if codes is None:
         codes = torch.empty((M, code_width(f, K) if bs else 0), dtype=torch.uint8, device=x.device)
     if scales is None:
-        scales = torch.empty((M, K // bs if bs else 0), dtype=torch.uint8, device=x.device)
-    _check(_lib.quantize_block_scaled(f, bs, SCALES_ROW_MAJOR, _ptr(x), M, K, _ld(x), _ptr(codes),
+        scales = torch.empty(scale_shape(f, M, K, scale_layout) if bs else (M, 0),
+                             dtype=torch.uint8, device=x.device)
+    _check(_lib.quantize_block_scaled(f, bs, scale_layout, _ptr(x), M, K, _ld(x), _ptr(codes),
                                       _ld(codes), _ptr(scales), _ld(scales),
                                       float(tensor_sf), _stream_ptr(stream, x.device)))
     return codes, scales
@@ -133,7 +146,8 @@ def grouped_quantize_block_scaled(x: torch.Tensor, fmt, row_offsets: torch.Tenso
                                   scales_offsets: torch.Tensor, expert_ids: torch.Tensor,
                                   tensor_sf: torch.Tensor | None, max_rows: int,
                                   num_scale_rows: int, row_indices: torch.Tensor | None = None,
-                                  codes=None, scales=None, stream=None):
+                                  codes=None, scales=None, stream=None,
+                                  scale_layout: int = SCALES_ROW_MAJOR):
     """Grouped per-expert form.  x: BF16 [num_src_rows, K]; row_offsets /
     scales_offsets: uint32 (or int32 bit-identical) [G+1]; expert_ids int32
     [G]; tensor_sf fp32 [num_experts] (NVFP4) or None; row_indices int32
@@ -165,10 +179,10 @@ def grouped_quantize_block_scaled(x: torch.Tensor, fmt, row_offsets: torch.Tenso
         codes = torch.empty((max_rows, code_width(f, K) if bs else 0), dtype=torch.uint8,
                             device=x.device)
     if scales is None:
-        scales = torch.empty((num_scale_rows, K // bs if bs else 0), dtype=torch.uint8,
-                             device=x.device)
+        scales = torch.empty(scale_shape(f, num_scale_rows, K, scale_layout) if bs else
+                             (num_scale_rows, 0), dtype=torch.uint8, device=x.device)
     _check(_lib.grouped_quantize_block_scaled(
-        f, bs, SCALES_ROW_MAJOR, _ptr(x), S, K, _ld(x), _ptr(row_indices), _ptr(row_offsets),
+        f, bs, scale_layout, _ptr(x), S, K, _ld(x), _ptr(row_indices), _ptr(row_offsets),
         _ptr(scales_offsets), _ptr(expert_ids), _ptr(tensor_sf), G, E, max_rows, num_scale_rows,
         _ptr(codes), _ld(codes), _ptr(scales), _ld(scales), _stream_ptr(stream, x.device)))
     return codes, scales
@@ -217,24 +231,26 @@ def _as_code_matrix(name, t):
 
 
 def dequantize_block_scaled(codes: torch.Tensor, scales: torch.Tensor, fmt, K: int,
-                            tensor_sf: float = 1.0, out=None, stream=None):
+                            tensor_sf: float = 1.0, out=None, stream=None,
+                            scale_layout: int = SCALES_ROW_MAJOR):
     """fp32 [M, K] values of a quantizer's codes ([M, K/2] FP4 or [M, K] FP8)
     and block scales ([M, K/block_size]); NVFP4 values include tensor_sf."""
     f = _fmt(fmt)
     codes, scales = _as_code_matrix("codes", codes), _as_code_matrix("scales", scales)
     M = codes.shape[0]
-    if scales.shape[0] != M:
-        raise ValueError("codes and scales must have the same number of rows")
+    if scales.shape[0] != scale_shape(f, M, K, scale_layout)[0]:
+        raise ValueError("scales has the wrong number of rows (row groups) for codes")
     if out is None:
         out = torch.empty((M, K), dtype=torch.float32, device=codes.device)
-    _check(_lib.dequantize_block_scaled(f, BLOCK_SIZE.get(f, 0), SCALES_ROW_MAJOR, _ptr(codes), M,
+    _check(_lib.dequantize_block_scaled(f, BLOCK_SIZE.get(f, 0), scale_layout, _ptr(codes), M,
                                         K, _ld(codes), _ptr(scales), _ld(scales), float(tensor_sf),
                                         _ptr(out), _ld(out), _stream_ptr(stream, codes.device)))
     return out
 
 
 def block_scaled_matmul_naive(a_codes, a_scales, b_codes, b_scales, fmt, K: int,
-                              a_tsf: float = 1.0, b_tsf: float = 1.0, out=None, stream=None):
+                              a_tsf: float = 1.0, b_tsf: float = 1.0, out=None, stream=None,
+                              scale_layout: int = SCALES_ROW_MAJOR):
     """Reference GEMM c = A @ B.T (fp32 [M, N]) over two quantizer outputs of
     one format, both blocked along K; one thread per output, fp32 sums in
     ascending k.  Not a fast GEMM."""
@@ -245,7 +261,7 @@ def block_scaled_matmul_naive(a_codes, a_scales, b_codes, b_scales, fmt, K: int,
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
     _check(_lib.block_scaled_matmul_naive(
-        f, BLOCK_SIZE.get(f, 0), SCALES_ROW_MAJOR, _ptr(a_codes), _ld(a_codes), _ptr(a_scales),
+        f, BLOCK_SIZE.get(f, 0), scale_layout, _ptr(a_codes), _ld(a_codes), _ptr(a_scales),
         _ld(a_scales), float(a_tsf), _ptr(b_codes), _ld(b_codes), _ptr(b_scales), _ld(b_scales),
         float(b_tsf), M, N, K, _ptr(out), _ld(out), _stream_ptr(stream, a_codes.device)))
     return out

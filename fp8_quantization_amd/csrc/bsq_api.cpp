@@ -120,9 +120,11 @@ int check_layout(int format, int block_size, int scale_layout, int64_t rows, int
     if (block_size != bs)
         return fail(BSQ_ERR_UNSUPPORTED, "%s uses %d-element blocks, got block_size=%d",
                     fmt_name(format), bs, block_size);
-    if (scale_layout != BSQ_SCALES_ROW_MAJOR)
-        return fail(BSQ_ERR_UNSUPPORTED, "scale layout %d is not provided (only row-major = 0)",
-                    scale_layout);
+    if (scale_layout != BSQ_SCALES_ROW_MAJOR && scale_layout != BSQ_SCALES_MFMA16)
+        return fail(BSQ_ERR_UNSUPPORTED, "scale layout %d is not provided", scale_layout);
+    if (scale_layout == BSQ_SCALES_MFMA16 && format == BSQ_NVFP4)
+        return fail(BSQ_ERR_UNSUPPORTED,
+                    "the MFMA scale layout holds E8M0 scales of 32-element blocks (MX only)");
     if (rows < 0 || K < 0) return fail(BSQ_ERR_INVALID_ARG, "negative size (rows=%lld K=%lld)",
                                        (long long)rows, (long long)K);
     if (K % bs != 0)
@@ -133,8 +135,10 @@ int check_layout(int format, int block_size, int scale_layout, int64_t rows, int
 }
 
 // A codes + scales operand of K elements per row (`what` names it in errors).
+// Row-major scales: lds bytes per row.  MFMA layout: lds bytes per 16-row
+// group, at least one 256-byte record per 512 elements of K.
 int check_operand(int format, int64_t K, const void* codes, int64_t ldq, const void* scales,
-                  int64_t lds, const char* what) {
+                  int64_t lds, const char* what, int scale_layout) {
     const int bs = expected_block(format);
     const int64_t code_row = (format == BSQ_MXFP8) ? K : K / 2;
     const int code_align = (format == BSQ_MXFP8) ? 8 : 4;
@@ -147,6 +151,14 @@ int check_operand(int format, int64_t K, const void* codes, int64_t ldq, const v
     if (ldq < code_row || ldq % code_align != 0)
         return fail(BSQ_ERR_INVALID_ARG, "%sldq=%lld must be >= %lld and a multiple of %d", what,
                     (long long)ldq, (long long)code_row, code_align);
+    if (scale_layout == BSQ_SCALES_MFMA16) {
+        const int64_t need = ((K / bs + 15) / 16) * 256;
+        if (lds < need || lds % 4 != 0)
+            return fail(BSQ_ERR_INVALID_ARG,
+                        "%slds=%lld must be >= %lld (256 bytes per 512 elements of K per 16-row "
+                        "group) and a multiple of 4", what, (long long)lds, (long long)need);
+        return BSQ_OK;
+    }
     if (lds < K / bs)
         return fail(BSQ_ERR_INVALID_ARG, "%slds=%lld must be >= K/block_size=%lld", what,
                     (long long)lds, (long long)(K / bs));
@@ -163,7 +175,7 @@ int check_common(int format, int block_size, int scale_layout, const void* x, in
     if (ldx < K || ldx % 8 != 0)
         return fail(BSQ_ERR_INVALID_ARG, "ldx=%lld must be >= K=%lld and a multiple of 8",
                     (long long)ldx, (long long)K);
-    return check_operand(format, K, codes, ldq, scales, lds, "");
+    return check_operand(format, K, codes, ldq, scales, lds, "", scale_layout);
 }
 
 bool tsf_in_domain(float t) {
@@ -276,6 +288,7 @@ int quantize_block_scaled(int format, int block_size, int scale_layout, const vo
     a.ldq = ldq;
     a.scales = static_cast<uint8_t*>(scales);
     a.lds = lds;
+    a.scale_layout = scale_layout;
     a.rows = M;
     a.K = (int32_t)K;
     a.tensor_sf = tensor_sf;
@@ -326,6 +339,7 @@ int grouped_quantize_block_scaled(int format, int block_size, int scale_layout, 
     a.ldq = ldq;
     a.scales = static_cast<uint8_t*>(scales);
     a.lds = lds;
+    a.scale_layout = scale_layout;
     a.rows = max_rows;
     a.K = (int32_t)K;
     a.tensor_sf = 1.0f;
@@ -436,7 +450,7 @@ int dequantize_block_scaled(int format, int block_size, int scale_layout, const 
         return fail(BSQ_ERR_INVALID_ARG,
                     "tensor_sf=%g must be finite and within [2^-117, 2^100]", (double)tensor_sf);
     if (M == 0 || K == 0) return ok();
-    st = check_operand(format, K, codes, ldq, scales, lds, "");
+    st = check_operand(format, K, codes, ldq, scales, lds, "", scale_layout);
     if (st != BSQ_OK) return st;
     if (!out || !aligned(out, 16))
         return fail(BSQ_ERR_INVALID_ARG, "out must be a 16-byte aligned device array");
@@ -453,6 +467,7 @@ int dequantize_block_scaled(int format, int block_size, int scale_layout, const 
     a.rows = M;
     a.K = (int32_t)K;
     a.tensor_sf = tensor_sf;
+    a.scale_layout = scale_layout;
     int64_t blocks = 0;
     a.chunks_per_tile = tile_knob() ? tile_knob() : bsq::kDequantChunks;
     if (tile_geometry(a, a.chunks_per_tile, &blocks) != BSQ_OK) return BSQ_ERR_INVALID_ARG;
@@ -479,9 +494,9 @@ int block_scaled_matmul_naive(int format, int block_size, int scale_layout,
     if (M * N > (int64_t(1) << 38))
         return fail(BSQ_ERR_INVALID_ARG, "M*N=%lld too large for one launch", (long long)(M * N));
     if (K > 0) {
-        st = check_operand(format, K, a_codes, lda_q, a_scales, lda_s, "a_");
+        st = check_operand(format, K, a_codes, lda_q, a_scales, lda_s, "a_", scale_layout);
         if (st != BSQ_OK) return st;
-        st = check_operand(format, K, b_codes, ldb_q, b_scales, ldb_s, "b_");
+        st = check_operand(format, K, b_codes, ldb_q, b_scales, ldb_s, "b_", scale_layout);
         if (st != BSQ_OK) return st;
     }
     if (!c || !aligned(c, 4)) return fail(BSQ_ERR_INVALID_ARG, "c must be a 4-byte aligned device array");
@@ -503,6 +518,7 @@ int block_scaled_matmul_naive(int format, int block_size, int scale_layout,
     a.M = M;
     a.N = N;
     a.K = (int32_t)K;
+    a.scale_layout = scale_layout;
     const hipError_t e = bsq::launch_naive_matmul(format, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -107,7 +107,10 @@ __global__ void __launch_bounds__(kThreadsPerBlock) dequant_kernel(const Dequant
     const uint32_t row = div_rows(t, a);
     const int c0 = (int)(t - row * (uint32_t)a.tiles_per_row) * U;
     const uint8_t* crow = a.codes + (int64_t)row * a.ldq;
-    const uint8_t* srow = a.scales + (int64_t)row * a.lds;
+    const bool mfma_layout = FMT != 2 && a.scale_layout == 1;
+    // row-major: the scale row; MFMA layout: the row's place in its group
+    const uint8_t* srow = mfma_layout ? a.scales + (int64_t)(row >> 4) * a.lds + 4 * (row & 15)
+                                      : a.scales + (int64_t)row * a.lds;
     float* orow = a.out + (int64_t)row * a.ldo;
 
     uint32_t q0[U], q1[U], sb[U];
@@ -126,7 +129,9 @@ __global__ void __launch_bounds__(kThreadsPerBlock) dequant_kernel(const Dequant
             } else {
                 q0[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(crow + col / 2));
             }
-            sb[u] = srow[col / kBlock];
+            const int b = lane / (kBlock / kElemsPerLane);  // block within the chunk
+            sb[u] = mfma_layout ? srow[(c0 + u) * 256 + 64 * (b & 3) + (b >> 2)]
+                                : srow[col / kBlock];
         }
     }
 #pragma unroll
@@ -165,13 +170,14 @@ __global__ void __launch_bounds__(kThreadsPerBlock) naive_matmul_kernel(const Ge
     if (idx >= a.M * a.N) return;
     const int64_t m = idx / a.N, n = idx - m * a.N;
     const uint8_t* ac = a.a_codes + m * a.lda_q;
-    const uint8_t* as = a.a_scales + m * a.lda_s;
+    const bool mfma_layout = FMT != 2 && a.scale_layout == 1;
+    const uint8_t* as = mfma_layout ? a.a_scales + (m >> 4) * a.lda_s : a.a_scales + m * a.lda_s;
     const uint8_t* bc = a.b_codes + n * a.ldb_q;
-    const uint8_t* bs = a.b_scales + n * a.ldb_s;
+    const uint8_t* bs = mfma_layout ? a.b_scales + (n >> 4) * a.ldb_s : a.b_scales + n * a.ldb_s;
     float acc = 0.0f;
     for (int kb = 0; kb < a.K / kBlock; ++kb) {
-        const float sa = scale_value<FMT>(as[kb]);
-        const float sb = scale_value<FMT>(bs[kb]);
+        const float sa = scale_value<FMT>(mfma_layout ? as[mfma16_scale_offset(m, kb)] : as[kb]);
+        const float sb = scale_value<FMT>(mfma_layout ? bs[mfma16_scale_offset(n, kb)] : bs[kb]);
         for (int k = kb * kBlock; k < (kb + 1) * kBlock; k += 2) {
             const f32x2_t ca = operand_pair<FMT>(ac, k);
             const f32x2_t cb = operand_pair<FMT>(bc, k);

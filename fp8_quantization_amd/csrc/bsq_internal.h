@@ -38,6 +38,7 @@ struct KernelArgs {
     uint32_t tpr_magic_lo;        // ceil(2^64 / tiles_per_row), low and high words:
     uint32_t tpr_magic_hi;        //   t / tiles_per_row = (t * magic) >> 64 for t < 2^32
     float tensor_sf;              // dense NVFP4
+    int32_t scale_layout;         // 0 row-major, 1 MFMA 16x16x128 (MX only)
 
     // grouped form only
     const int32_t* row_indices;   // nullable
@@ -50,6 +51,17 @@ struct KernelArgs {
     int32_t num_groups;
     int32_t num_experts;
 };
+
+// Byte offset, inside a row group's scale records, of the scale of row r
+// (r % 16 is used) and 32-element block kb in the MFMA 16x16x128 layout:
+// 256-byte records of 16 rows x 16 blocks; the scale of (r, kb) sits in the
+// dword of lane (r % 16) + 16 (kb % 4) -- the lane the scaled matrix
+// instruction takes it from for its 128-element K step -- at byte
+// (kb % 16) / 4, so one dword per lane feeds four consecutive K steps.  The
+// row group of r starts at (r / 16) * lds.
+__host__ __device__ inline int64_t mfma16_scale_offset(int64_t r, int64_t kb) {
+    return (kb / 16) * 256 + 4 * ((r % 16) + 16 * (kb % 4)) + (kb % 16) / 4;
+}
 
 // Dequantization to fp32: one wave per chunk (56.4 us against 64.2 with 2
 // chunks and 72.9 with 4 for [8192, 7168] MXFP8).
@@ -70,6 +82,7 @@ struct DequantArgs {
     int64_t total_tiles;    // < 2^31
     uint32_t tpr_magic_lo, tpr_magic_hi;
     float tensor_sf;        // NVFP4
+    int32_t scale_layout;   // as in KernelArgs
 };
 
 // Naive GEMM c = A B^T over two K-major block-scaled operands.
@@ -88,6 +101,7 @@ struct GemmArgs {
     int64_t ldc;
     int64_t M, N;
     int32_t K;
+    int32_t scale_layout;   // as in KernelArgs
 };
 
 hipError_t launch_dequantize(int fmt, const DequantArgs& a, int64_t blocks, hipStream_t stream);

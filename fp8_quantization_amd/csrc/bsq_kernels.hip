@@ -380,7 +380,11 @@ __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const Kernel
         }
     }
     uint8_t* qrow = a.codes + (int64_t)row * a.ldq;
-    uint8_t* srow = a.scales + scale_row * a.lds;
+    // row-major: the scale row; MFMA layout (MX only): the row's place in
+    // its 16-row group, to which each block adds its record and lane offset
+    const bool mfma_layout = FMT != 2 && a.scale_layout == 1;
+    uint8_t* srow = mfma_layout ? a.scales + (scale_row >> 4) * a.lds + 4 * (scale_row & 15)
+                                : a.scales + scale_row * a.lds;
     Nvfp4Wave nw{};
     if constexpr (FMT == 2) nw = nvfp4_wave_setup(tsf, lane);
 
@@ -419,8 +423,12 @@ __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const Kernel
 #pragma unroll
         for (int k = 1; k < L && g + k < U; ++k) v = (j == k) ? sb[g + k] : v;
         const uint32_t col = (uint32_t)((c0 + u) * kChunkElems + (lane - j) * kElemsPerLane);
-        if (u < nch && u < U && col < (uint32_t)a.K)
-            __builtin_nontemporal_store((uint8_t)v, srow + col / T::kBlock);
+        // block b = lane / L of chunk c0 + u; in the MFMA layout a chunk is one
+        // record and block b goes to lane-dword 16 (b % 4), byte b / 4
+        const int b = lane / L;
+        uint8_t* dst = mfma_layout ? srow + (c0 + u) * 256 + 64 * (b & 3) + (b >> 2)
+                                   : srow + col / T::kBlock;
+        if (u < nch && u < U && col < (uint32_t)a.K) __builtin_nontemporal_store((uint8_t)v, dst);
     }
 }
 

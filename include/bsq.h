@@ -56,9 +56,34 @@ extern "C" {
 
 enum bsq_format { BSQ_MXFP4 = 0, BSQ_MXFP8 = 1, BSQ_NVFP4 = 2 };
 
-/* Scale layouts.  Only row-major scales exist in this version; any other
-   value is rejected with BSQ_ERR_UNSUPPORTED. */
-enum bsq_scale_layout { BSQ_SCALES_ROW_MAJOR = 0 };
+/*
+ * Scale layouts (any other value: BSQ_ERR_UNSUPPORTED).
+ *
+ * BSQ_SCALES_ROW_MAJOR  uint8 [rows, lds]: the scale of row r, block kb at
+ *     r * lds + kb.
+ *
+ * BSQ_SCALES_MFMA16     MX formats only (NVFP4: BSQ_ERR_UNSUPPORTED): the
+ *     operand layout of gfx950's v_mfma_scale_f32_16x16x128_f8f6f4, the
+ *     CDNA4 counterpart of the SM100 scale interleave the
+ *     "block_scaled_quantization" module page lists (block_scales_interleave).
+ *     For one 128-element K step that instruction takes the scale of A row r
+ *     (0..15) and 32-element block q (0..3) from lane r + 16 q of a 32-bit
+ *     register, byte selected by opsel.  Rows form groups of 16 and blocks
+ *     groups of 16 (512 elements); each (row group, block group) is a
+ *     256-byte record in which the scale of (r, kb) is byte
+ *         4 * ((r % 16) + 16 * (kb % 4)) + (kb % 16) / 4,
+ *     and record (r / 16, kb / 16) starts at (r / 16) * lds + (kb / 16) * 256.
+ *     So dword L of a record is lane L's register for four consecutive K
+ *     steps (byte t for step t).  lds is the byte stride between 16-row
+ *     groups: a multiple of 4, at least 256 * ceil(K / 512).  The buffer
+ *     holds ceil(rows / 16) groups; bytes of incomplete records (rows past the
+ *     last row, blocks past K) are not written.  In the grouped form, scale
+ *     row so = scales_offsets[g] + (r - row_offsets[g]) goes to row group
+ *     so / 16 (keeping scales_offsets multiples of 16 keeps each group's rows
+ *     in their own records).  Measured on the hardware with one-wave probes
+ *     of known FP4 and FP8 operands.
+ */
+enum bsq_scale_layout { BSQ_SCALES_ROW_MAJOR = 0, BSQ_SCALES_MFMA16 = 1 };
 
 enum bsq_status {
     BSQ_OK = 0,
@@ -72,7 +97,7 @@ enum bsq_status {
  *
  *   format, block_size  (BSQ_MXFP4, 32), (BSQ_MXFP8, 32) or (BSQ_NVFP4, 16);
  *                       any other pair -> BSQ_ERR_UNSUPPORTED.
- *   scale_layout        BSQ_SCALES_ROW_MAJOR.
+ *   scale_layout        BSQ_SCALES_ROW_MAJOR, or BSQ_SCALES_MFMA16 (MX).
  *   x                   BF16 [M, K], row-major, row stride ldx elements.
  *                       16-byte aligned; ldx >= K and ldx % 8 == 0.
  *   M, K                M >= 0, K >= 0, K % block_size == 0.
@@ -80,8 +105,9 @@ enum bsq_status {
  *                       bytes (FP8) of codes.  FP4: 4-byte aligned,
  *                       ldq % 4 == 0, ldq >= K/2.  FP8: 8-byte aligned,
  *                       ldq % 8 == 0, ldq >= K.
- *   scales              uint8 [M, lds]: row r holds the K/block_size block
- *                       scales of row r; lds >= K/block_size.
+ *   scales              row-major: uint8 [M, lds], row r holds the
+ *                       K/block_size block scales of row r; lds >=
+ *                       K/block_size.  MFMA layout: see above.
  *   tensor_sf           NVFP4 only (ignored for MX): finite and within
  *                       [2^-117, 2^100], so that s * tsf is a normal fp32 or
  *                       zero and its reciprocal is finite; else
@@ -123,7 +149,8 @@ int quantize_block_scaled(int format, int block_size, int scale_layout,
  *                    device offsets are never read on the host.  <= 2^32.
  *   num_scale_rows   rows in the scales buffer.
  *   codes, ldq       uint8 [max_rows, ldq], as for the dense form.
- *   scales, lds      uint8 [num_scale_rows, lds].
+ *   scales, lds      uint8 [num_scale_rows, lds] (row-major), or the MFMA
+ *                    layout over num_scale_rows rows.
  * The device-array contents above are preconditions and are not checked on
  * the host.  The kernels still never access memory outside the buffers the
  * sizes describe: a routed row whose group, source row, expert id or scale

@@ -84,8 +84,18 @@ def test_unsupported_pairs(lib, fmt, bs):
 
 
 def test_unsupported_layout(lib):
-    assert dense(lib, layout=1) == UNSUPPORTED
+    assert dense(lib, layout=2) == UNSUPPORTED
     assert b"layout" in lib.bsq_last_error()
+    assert dense(lib, fmt=NVFP4, bs=16, layout=1, tsf=0.5) == UNSUPPORTED   # MFMA layout: MX only
+    assert b"MX only" in lib.bsq_last_error()
+
+
+def test_mfma_layout_row_group_stride(lib):
+    # K = 1024: two 256-byte records per 16-row group
+    assert dense(lib, layout=1, K=1024, ldx=1024, lds=256) == INVALID
+    assert b"lds" in lib.bsq_last_error()
+    assert dense(lib, layout=1, K=1024, ldx=1024, lds=514) == INVALID    # not a multiple of 4
+    assert dense(lib, fmt=MXFP8, layout=1, K=1024, ldx=1024, lds=511) == INVALID
 
 
 @pytest.mark.parametrize("kw", [
@@ -170,7 +180,9 @@ def test_dequantize_validation(lib):
         return lib.dequantize_block_scaled(fmt, bs, layout, codes, M, K, ldq, scales, lds, tsf,
                                            out, ldo, None)
     assert dq(bs=16) == UNSUPPORTED
-    assert dq(layout=1) == UNSUPPORTED
+    assert dq(layout=2) == UNSUPPORTED
+    assert dq(fmt=NVFP4, bs=16, layout=1) == UNSUPPORTED
+    assert dq(layout=1, lds=255) == INVALID
     assert dq(M=-1) == INVALID
     assert dq(K=48, ldo=48) == INVALID                         # K % 32
     assert dq(codes=None) == INVALID
