@@ -49,6 +49,9 @@ _lib.dequantize_block_scaled.restype = _i32
 _lib.block_scaled_matmul_naive.argtypes = [_i32, _i32, _i32, _p, _i64, _p, _i64, _f32, _p, _i64,
                                            _p, _i64, _f32, _i64, _i64, _i64, _p, _i64, _p]
 _lib.block_scaled_matmul_naive.restype = _i32
+_lib.block_scaled_matmul_mfma.argtypes = [_i32, _i32, _i32, _p, _i64, _p, _i64, _p, _i64, _p,
+                                          _i64, _i64, _i64, _i64, _p, _i64, _p]
+_lib.block_scaled_matmul_mfma.restype = _i32
 _lib.bsq_last_error.argtypes = []
 _lib.bsq_last_error.restype = ctypes.c_char_p
 _lib.bsq_version.argtypes = []
@@ -264,4 +267,22 @@ def block_scaled_matmul_naive(a_codes, a_scales, b_codes, b_scales, fmt, K: int,
         f, BLOCK_SIZE.get(f, 0), scale_layout, _ptr(a_codes), _ld(a_codes), _ptr(a_scales),
         _ld(a_scales), float(a_tsf), _ptr(b_codes), _ld(b_codes), _ptr(b_scales), _ld(b_scales),
         float(b_tsf), M, N, K, _ptr(out), _ld(out), _stream_ptr(stream, a_codes.device)))
+    return out
+
+
+def block_scaled_matmul_mfma(a_codes, a_scales, b_codes, b_scales, fmt, K: int, out=None,
+                             stream=None):
+    """c = A @ B.T (fp32 [M, N]) on the matrix cores, over two MX quantizer
+    outputs with scales in the MFMA layout (``scale_layout=SCALES_MFMA16``);
+    K % 128 == 0."""
+    f = _fmt(fmt)
+    a_codes, a_scales = _as_code_matrix("a_codes", a_codes), _as_code_matrix("a_scales", a_scales)
+    b_codes, b_scales = _as_code_matrix("b_codes", b_codes), _as_code_matrix("b_scales", b_scales)
+    M, N = a_codes.shape[0], b_codes.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
+    _check(_lib.block_scaled_matmul_mfma(
+        f, BLOCK_SIZE.get(f, 0), SCALES_MFMA16, _ptr(a_codes), _ld(a_codes), _ptr(a_scales),
+        _ld(a_scales), _ptr(b_codes), _ld(b_codes), _ptr(b_scales), _ld(b_scales), M, N, K,
+        _ptr(out), _ld(out), _stream_ptr(stream, a_codes.device)))
     return out

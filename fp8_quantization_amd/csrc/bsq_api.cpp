@@ -524,6 +524,60 @@ int block_scaled_matmul_naive(int format, int block_size, int scale_layout,
     return ok();
 }
 
+int block_scaled_matmul_mfma(int format, int block_size, int scale_layout,
+                             const void* a_codes, int64_t lda_q, const void* a_scales,
+                             int64_t lda_s,
+                             const void* b_codes, int64_t ldb_q, const void* b_scales,
+                             int64_t ldb_s,
+                             int64_t M, int64_t N, int64_t K, float* c, int64_t ldc,
+                             void* stream) {
+    int st = check_layout(format, block_size, scale_layout, M, K);
+    if (st != BSQ_OK) return st;
+    if (format == BSQ_NVFP4)
+        return fail(BSQ_ERR_UNSUPPORTED, "the scaled matrix instruction takes MX formats only");
+    if (scale_layout != BSQ_SCALES_MFMA16)
+        return fail(BSQ_ERR_UNSUPPORTED, "the MFMA GEMM reads scales in the MFMA layout only");
+    if (N < 0) return fail(BSQ_ERR_INVALID_ARG, "negative size (N=%lld)", (long long)N);
+    if (K % 128 != 0)
+        return fail(BSQ_ERR_INVALID_ARG, "K=%lld must be a multiple of 128 (one K step)",
+                    (long long)K);
+    if (M == 0 || N == 0) return ok();
+    if (M * N > (int64_t(1) << 38))
+        return fail(BSQ_ERR_INVALID_ARG, "M*N=%lld too large for one launch", (long long)(M * N));
+    if (K > 0) {
+        st = check_operand(format, K, a_codes, lda_q, a_scales, lda_s, "a_", scale_layout);
+        if (st != BSQ_OK) return st;
+        st = check_operand(format, K, b_codes, ldb_q, b_scales, ldb_s, "b_", scale_layout);
+        if (st != BSQ_OK) return st;
+        if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || lda_q % 16 != 0 || ldb_q % 16 != 0)
+            return fail(BSQ_ERR_INVALID_ARG,
+                        "code rows must be 16-byte aligned (codes and ldq multiples of 16)");
+        if (!aligned(a_scales, 4) || !aligned(b_scales, 4))
+            return fail(BSQ_ERR_INVALID_ARG, "scales must be 4-byte aligned");
+    }
+    if (!c || !aligned(c, 4)) return fail(BSQ_ERR_INVALID_ARG, "c must be a 4-byte aligned device array");
+    if (ldc < N) return fail(BSQ_ERR_INVALID_ARG, "ldc=%lld must be >= N=%lld", (long long)ldc,
+                             (long long)N);
+    bsq::GemmArgs a{};
+    a.a_codes = static_cast<const uint8_t*>(a_codes);
+    a.lda_q = lda_q;
+    a.a_scales = static_cast<const uint8_t*>(a_scales);
+    a.lda_s = lda_s;
+    a.b_codes = static_cast<const uint8_t*>(b_codes);
+    a.ldb_q = ldb_q;
+    a.b_scales = static_cast<const uint8_t*>(b_scales);
+    a.ldb_s = ldb_s;
+    a.c = c;
+    a.ldc = ldc;
+    a.M = M;
+    a.N = N;
+    a.K = (int32_t)K;
+    a.scale_layout = scale_layout;
+    const hipError_t e = bsq::launch_mfma_matmul(format, a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 const char* bsq_last_error(void) { return g_last_error.c_str(); }
 
 const char* bsq_version(void) { return "1.0.0"; }

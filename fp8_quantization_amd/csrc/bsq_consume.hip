@@ -188,6 +188,96 @@ __global__ void __launch_bounds__(kThreadsPerBlock) naive_matmul_kernel(const Ge
     a.c[m * a.ldc + n] = acc;
 }
 
+// ------------------------------------------------------------ MFMA consumer
+//
+// c = A B^T with gfx950's scaled matrix instruction
+// v_mfma_scale_f32_16x16x128_f8f6f4, reading the quantizers' MX output as
+// is: codes row-major, scales in the MFMA layout.  One wave per 16 x 16 tile
+// of c; per 128-element K step each lane loads its operand fragments
+// straight from the code rows, and per 512 elements one scale dword per lane
+// per operand, whose byte t feeds step t (opsel = t).
+//
+// Operand fragments (measured with one-wave probes of known operands):
+// lane l serves row l % 16 of its operand and group g = l / 16;
+//  * FP4 (E2M1): the 32 consecutive elements [32 g, 32 g + 32) of the step,
+//    16 bytes, in the first four registers;
+//  * FP8 (E4M3): elements [16 g, 16 g + 16) and [64 + 16 g, 64 + 16 g + 16),
+//    two 16-byte pieces.
+// c tile: lane l holds rows 4 (l / 16) .. 4 (l / 16) + 3, column l % 16.
+typedef int mfma_v8i __attribute__((ext_vector_type(8)));
+typedef float mfma_v4f __attribute__((ext_vector_type(4)));
+
+template <int FMT>
+__device__ __forceinline__ mfma_v8i load_fragment(const uint8_t* row, int k0, int g, bool valid) {
+    mfma_v8i v = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (!valid) return v;
+    if constexpr (FMT == 1) {
+        const int4 lo = *reinterpret_cast<const int4*>(row + k0 + 16 * g);
+        const int4 hi = *reinterpret_cast<const int4*>(row + k0 + 64 + 16 * g);
+        v = (mfma_v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    } else {
+        const int4 q = *reinterpret_cast<const int4*>(row + (k0 + 32 * g) / 2);
+        v = (mfma_v8i){q.x, q.y, q.z, q.w, 0, 0, 0, 0};
+    }
+    return v;
+}
+
+template <int FMT, int T>
+__device__ __forceinline__ mfma_v4f mfma_step(const uint8_t* arow, const uint8_t* brow, int k0,
+                                             int g, bool va, bool vb, uint32_t sa, uint32_t sb,
+                                             mfma_v4f acc) {
+    constexpr int kFmt = FMT == 1 ? 0 : 4;  // instruction format codes: 0 E4M3, 4 E2M1
+    const mfma_v8i fa = load_fragment<FMT>(arow, k0, g, va);
+    const mfma_v8i fb = load_fragment<FMT>(brow, k0, g, vb);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb, acc, kFmt, kFmt, T, (int)sa, T,
+                                                            (int)sb);
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(kThreadsPerBlock) mfma_matmul_kernel(const GemmArgs a,
+                                                                         int64_t tiles_n,
+                                                                         int64_t tiles) {
+    const int lane = (int)(threadIdx.x & (kWaveSize - 1));
+    const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWaveSize;
+    if (t >= tiles) return;
+    const int64_t m0 = (t / tiles_n) * 16, n0 = (t % tiles_n) * 16;
+    const int r = lane & 15, g = lane >> 4;
+    const bool va = m0 + r < a.M, vb = n0 + r < a.N;
+    const uint8_t* arow = a.a_codes + (m0 + r) * a.lda_q;
+    const uint8_t* brow = a.b_codes + (n0 + r) * a.ldb_q;
+    // this lane's dword of each 256-byte scale record of the tile's row groups
+    const uint8_t* as = a.a_scales + (m0 >> 4) * a.lda_s + 4 * lane;
+    const uint8_t* bs = a.b_scales + (n0 >> 4) * a.ldb_s + 4 * lane;
+    mfma_v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k0 = 0; k0 < a.K; k0 += 512) {
+        // rows past M / N: zero codes under scale 2^0, so no unwritten byte enters
+        const uint32_t sa = va ? *reinterpret_cast<const uint32_t*>(as + (k0 / 512) * 256)
+                               : 0x7F7F7F7Fu;
+        const uint32_t sb = vb ? *reinterpret_cast<const uint32_t*>(bs + (k0 / 512) * 256)
+                               : 0x7F7F7F7Fu;
+        acc = mfma_step<FMT, 0>(arow, brow, k0, g, va, vb, sa, sb, acc);
+        if (k0 + 128 < a.K) acc = mfma_step<FMT, 1>(arow, brow, k0 + 128, g, va, vb, sa, sb, acc);
+        if (k0 + 256 < a.K) acc = mfma_step<FMT, 2>(arow, brow, k0 + 256, g, va, vb, sa, sb, acc);
+        if (k0 + 384 < a.K) acc = mfma_step<FMT, 3>(arow, brow, k0 + 384, g, va, vb, sa, sb, acc);
+    }
+    const int64_t col = n0 + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t row = m0 + 4 * g + i;
+        if (row < a.M && col < a.N) a.c[row * a.ldc + col] = acc[i];
+    }
+}
+
+template <int FMT>
+hipError_t launch_mfma_mm(const GemmArgs& a, hipStream_t stream) {
+    const int64_t tiles_n = (a.N + 15) / 16;
+    const int64_t tiles = ((a.M + 15) / 16) * tiles_n;
+    const int64_t blocks = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL((mfma_matmul_kernel<FMT>), dim3((uint32_t)blocks), dim3(kThreadsPerBlock), 0,
+                       stream, a, tiles_n, tiles);
+    return hipGetLastError();
+}
+
 template <int FMT>
 hipError_t launch_dq(const DequantArgs& a, int64_t blocks, hipStream_t stream) {
     switch (a.chunks_per_tile) {
@@ -223,6 +313,14 @@ hipError_t launch_dequantize(int fmt, const DequantArgs& a, int64_t blocks, hipS
         case 0: return launch_dq<0>(a, blocks, stream);
         case 1: return launch_dq<1>(a, blocks, stream);
         case 2: return launch_dq<2>(a, blocks, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_mfma_matmul(int fmt, const GemmArgs& a, hipStream_t stream) {
+    switch (fmt) {
+        case 0: return launch_mfma_mm<0>(a, stream);
+        case 1: return launch_mfma_mm<1>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }

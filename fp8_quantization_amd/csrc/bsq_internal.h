@@ -106,6 +106,8 @@ struct GemmArgs {
 
 hipError_t launch_dequantize(int fmt, const DequantArgs& a, int64_t blocks, hipStream_t stream);
 hipError_t launch_naive_matmul(int fmt, const GemmArgs& a, hipStream_t stream);
+// MX formats, scales in the MFMA layout, K % 128 == 0, 16-byte aligned code rows.
+hipError_t launch_mfma_matmul(int fmt, const GemmArgs& a, hipStream_t stream);
 
 // Launch the dense (grouped = false) or grouped kernel for format fmt
 // (0 MXFP4, 1 MXFP8, 2 NVFP4).  Returns the launch status.

@@ -254,6 +254,38 @@ int block_scaled_matmul_naive(int format, int block_size, int scale_layout,
                               int64_t M, int64_t N, int64_t K, float* c, int64_t ldc,
                               void* stream);
 
+/*
+ * Block-scaled GEMM on the matrix cores: c = A B^T with gfx950's
+ * v_mfma_scale_f32_16x16x128_f8f6f4, reading two MX quantizer outputs as
+ * they are -- codes row-major, scales in BSQ_SCALES_MFMA16 -- the CDNA4
+ * counterpart of the block-scaled matmuls the "block_scaled_quantization"
+ * module page lists.  One wave per 16 x 16 tile of c, no LDS staging: a
+ * consumer of the layout, not a tuned GEMM.  The instruction's own
+ * arithmetic sets the accuracy: FP4 products and their sums come out as
+ * exact fp32 sums would; FP8 products are summed inside each 128-element
+ * K step at reduced precision (measured error up to about 2^-12 of the
+ * largest product of the step); steps are accumulated in fp32.
+ *
+ *   format, block_size   (BSQ_MXFP4, 32) or (BSQ_MXFP8, 32); NVFP4 ->
+ *                        BSQ_ERR_UNSUPPORTED.
+ *   scale_layout         BSQ_SCALES_MFMA16 (anything else ->
+ *                        BSQ_ERR_UNSUPPORTED).
+ *   a_codes, lda_q       operand A [M, K]: code rows 16-byte aligned (base
+ *                        and lda_q multiples of 16); a_scales, lda_s its
+ *                        scales in the MFMA layout, 4-byte aligned.
+ *   b_codes, ...         operand B [N, K], likewise.
+ *   M, N, K              K % 128 == 0; M * N <= 2^38.
+ *   c, ldc               fp32 [M, ldc], 4-byte aligned, ldc >= N.
+ *   M == 0 or N == 0 is a no-op; K == 0 writes zeros.
+ */
+int block_scaled_matmul_mfma(int format, int block_size, int scale_layout,
+                             const void* a_codes, int64_t lda_q, const void* a_scales,
+                             int64_t lda_s,
+                             const void* b_codes, int64_t ldb_q, const void* b_scales,
+                             int64_t ldb_s,
+                             int64_t M, int64_t N, int64_t K, float* c, int64_t ldc,
+                             void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if
    none).  The pointer stays valid until the next call on that thread. */
 const char* bsq_last_error(void);

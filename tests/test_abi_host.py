@@ -46,6 +46,8 @@ def lib():
     lib.block_scaled_matmul_naive.argtypes = [i32, i32, i32, p, i64, p, i64, ctypes.c_float, p,
                                               i64, p, i64, ctypes.c_float, i64, i64, i64, p, i64,
                                               p]
+    lib.block_scaled_matmul_mfma.argtypes = [i32, i32, i32, p, i64, p, i64, p, i64, p, i64, i64,
+                                             i64, i64, p, i64, p]
     lib.bsq_last_error.restype = ctypes.c_char_p
     lib.bsq_version.restype = ctypes.c_char_p
     return lib
@@ -57,7 +59,8 @@ def test_header_declares_the_abi():
                                            "bsq_version", "tensor_scale_nvfp4",
                                            "grouped_tensor_scale_nvfp4",
                                            "dequantize_block_scaled",
-                                           "block_scaled_matmul_naive"])
+                                           "block_scaled_matmul_naive",
+                                           "block_scaled_matmul_mfma"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -221,6 +224,24 @@ def test_naive_matmul_validation(lib):
     assert mm(M=1 << 20, N=1 << 19) == INVALID                 # M * N > 2^38
     assert mm(M=0, a=None, b=None, c=None) == OK
     assert mm(N=0, a=None, b=None, c=None) == OK
+
+
+def test_mfma_matmul_validation(lib):
+    def mm(fmt=MXFP4, bs=32, layout=1, M=32, N=16, K=512, a=FAKE, b=FAKE, sa=FAKE, c=FAKE, ldc=16,
+           ldq=None, lds=256):
+        ldq = (K if fmt == MXFP8 else K // 2) if ldq is None else ldq
+        return lib.block_scaled_matmul_mfma(fmt, bs, layout, a, ldq, sa, lds, b, ldq, FAKE, lds, M,
+                                            N, K, c, ldc, None)
+    assert mm(fmt=NVFP4, bs=16) == UNSUPPORTED
+    assert mm(layout=0) == UNSUPPORTED
+    assert mm(K=96) == INVALID                                  # K % 128
+    assert mm(a=FAKE + 8) == INVALID                            # code rows 16-byte aligned
+    assert mm(ldq=264) == INVALID                               # ldq % 16 (FP4: >= 256)
+    assert mm(sa=FAKE + 2) == INVALID                           # scales 4-byte aligned
+    assert mm(lds=128) == INVALID                               # one record per 512 of K
+    assert mm(c=None) == INVALID
+    assert mm(ldc=8) == INVALID
+    assert mm(M=0, a=None, b=None, c=None) == OK
 
 
 def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):

@@ -1,0 +1,101 @@
+"""The MFMA consumer: c = A B^T on gfx950's scaled matrix instruction, reading
+MX codes row-major and scales in the MFMA layout -- the check that the
+layout is what the hardware takes.
+
+Against the oracle's exact GEMM, the error bound follows the instruction's
+arithmetic as measured on the hardware: E2M1 products and sums are exact
+until the fp32 accumulation across K steps; E4M3 products are summed inside
+each 128-element step at reduced precision (about 2^-12 of the step's
+largest product at worst in one-wave probes).  The bound used,
+|c - c_exact| <= 2^-10 * sum_k |a_k b_k|, holds both with a margin (the
+worst ratio seen is printed)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+NTHREADS = max(1, min(16, os.cpu_count() or 1))
+MXFP4, MXFP8 = oracle.MXFP4, oracle.MXFP8
+REL_BOUND = 2.0 ** -10
+
+
+@pytest.fixture(scope="module")
+def bsq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp8_quantization_amd as m
+    return m
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def operand(fmt, rows, K, seed, span=(-8, 8)):
+    x = W.random_bf16((rows, K), seed=seed, scale_log2_range=span)
+    q, s = oracle.quantize(x, fmt, 1.0, nthreads=NTHREADS)
+    return x, q, s
+
+
+def magnitude_sum(qa, sa, qb, sb, fmt, K):
+    A = oracle.dequantize(qa, sa, fmt, K).astype(np.float32).astype(np.float64)
+    B = oracle.dequantize(qb, sb, fmt, K).astype(np.float32).astype(np.float64)
+    return np.abs(A) @ np.abs(B).T
+
+
+@pytest.mark.parametrize("fmt", [MXFP4, MXFP8])
+@pytest.mark.parametrize("M,N,K", [(16, 16, 128), (37, 45, 1024), (128, 96, 2048),
+                                   (33, 130, 7168), (1, 300, 640)])
+def test_mfma_matmul_matches_oracle(bsq, fmt, M, N, K):
+    _, qa, sa = operand(fmt, M, K, seed=M + K + fmt)
+    _, qb, sb = operand(fmt, N, K, seed=N + K + fmt + 1)
+    got = bsq.block_scaled_matmul_mfma(dev(qa), dev(oracle.scales_to_mfma16(sa)), dev(qb),
+                                       dev(oracle.scales_to_mfma16(sb)), fmt, K)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy().astype(np.float64)
+    want = oracle.block_scaled_matmul(qa, sa, qb, sb, fmt, K)
+    S = magnitude_sum(qa, sa, qb, sb, fmt, K)
+    ratio = np.max(np.abs(got - want) / np.maximum(S, 1e-300))
+    print(f"format {fmt} {M}x{N}x{K}: max |err| / sum|ab| = {ratio:.3e}")
+    assert ratio <= REL_BOUND
+
+
+@pytest.mark.parametrize("fmt", [MXFP4, MXFP8])
+def test_pipeline_quantize_into_layout_then_mfma(bsq, fmt):
+    """BF16 -> GPU quantizer writing the MFMA layout -> MFMA GEMM, against the
+    exact GEMM of the oracle's quantization (and the end-to-end error against
+    the BF16 GEMM, which must match the naive pipeline's)."""
+    K = 2048
+    xa = W.random_bf16((128, K), seed=1, scale_log2_range=(-4, 4))
+    xb = W.random_bf16((96, K), seed=11, scale_log2_range=(-4, 4))
+    L = bsq.SCALES_MFMA16
+    qa, la = bsq.quantize_block_scaled(dev(xa.view(np.int16)), fmt, scale_layout=L)
+    qb, lb = bsq.quantize_block_scaled(dev(xb.view(np.int16)), fmt, scale_layout=L)
+    c = bsq.block_scaled_matmul_mfma(qa, la, qb, lb, fmt, K)
+    torch.cuda.synchronize()
+    qa_h, sa_h = oracle.quantize(xa, fmt, 1.0, nthreads=NTHREADS)
+    qb_h, sb_h = oracle.quantize(xb, fmt, 1.0, nthreads=NTHREADS)
+    want = oracle.block_scaled_matmul(qa_h, sa_h, qb_h, sb_h, fmt, K)
+    S = magnitude_sum(qa_h, sa_h, qb_h, sb_h, fmt, K)
+    got = c.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - want) <= REL_BOUND * S)
+    ref = W.bf16_to_f32(xa).astype(np.float64) @ W.bf16_to_f32(xb).astype(np.float64).T
+    err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    err_exact = np.linalg.norm(want - ref) / np.linalg.norm(ref)
+    print(f"format {fmt}: end-to-end relative error {err:.4f} (exact sums {err_exact:.4f})")
+    assert abs(err - err_exact) <= 1e-3 * err_exact
+
+
+def test_zero_k_and_empty(bsq):
+    z = bsq.block_scaled_matmul_mfma(torch.zeros((5, 0), dtype=torch.uint8, device="cuda"),
+                                     torch.zeros((1, 0), dtype=torch.uint8, device="cuda"),
+                                     torch.zeros((7, 0), dtype=torch.uint8, device="cuda"),
+                                     torch.zeros((1, 0), dtype=torch.uint8, device="cuda"),
+                                     MXFP8, 0)
+    torch.cuda.synchronize()
+    assert z.shape == (5, 7) and torch.all(z == 0)
