@@ -68,6 +68,9 @@ def load_workload(name):
         "dequant_mxfp8": lambda: W.dequant_random_bytes(W.MXFP8, 8192, 7168, seed=1102),
         "dequant_nvfp4": lambda: W.dequant_random_bytes(W.NVFP4, 16384, 7168, seed=1103,
                                                         tensor_sf=0.0123),
+        # the matrix-core consumer of the MFMA scale layout
+        "mfma_gemm_mxfp8": lambda: W.gemm_random_operands(W.MXFP8, 4096, 4096, 7168, seed=1202),
+        "mfma_gemm_mxfp4": lambda: W.gemm_random_operands(W.MXFP4, 4096, 4096, 7168, seed=1201),
     }
     return table[name]()
 
@@ -98,6 +101,14 @@ def producer_bytes(case):
     return int(src * K * 2 + meta), (hi - lo) * K
 
 
+# dense matrix-core peaks of MI355X (TFLOP/s) for the GEMM's operand format
+PEAK_MFMA_TFLOPS = {0: 10100.0, 1: 5000.0}
+
+
+def gemm_flops(case):
+    return 2 * case.a_codes.shape[0] * case.b_codes.shape[0] * case.K
+
+
 def dequant_bytes(case):
     """Codes and scales read, fp32 values written."""
     M = case.codes.shape[0]
@@ -109,6 +120,10 @@ def algorithmic_bytes(case):
     import workloads as W
     if isinstance(case, W.DequantCase):
         return dequant_bytes(case)
+    if isinstance(case, W.GemmCase):    # operands read once + c written
+        M, N = case.a_codes.shape[0], case.b_codes.shape[0]
+        return int(case.a_codes.nbytes + case.a_scales.nbytes + case.b_codes.nbytes +
+                   case.b_scales.nbytes + 4 * M * N), M * N
     if isinstance(case, W.DenseCase):
         M, K = case.x.shape
         return int(M * K * bytes_per_element(case.fmt)), M * K
@@ -141,9 +156,18 @@ class Runner:
         import workloads as W
         self.bsq, self.torch, self.case = bsq, torch, case
         self.dequant = isinstance(case, W.DequantCase)
+        self.gemm = isinstance(case, W.GemmCase)
         self.grouped = isinstance(case, W.GroupedCase)
         self.producer = producer
         self.sets = []
+        if self.gemm:
+            t = lambda a: torch.from_numpy(a).cuda()
+            self.sets.append({"aq": t(case.a_codes), "as": t(case.a_scales),
+                              "bq": t(case.b_codes), "bs": t(case.b_scales),
+                              "c": torch.empty((case.a_codes.shape[0], case.b_codes.shape[0]),
+                                               dtype=torch.float32, device="cuda")})
+            torch.cuda.synchronize()
+            return
         if self.dequant:
             codes, scales = torch.from_numpy(case.codes).cuda(), torch.from_numpy(case.scales).cuda()
             for i in range(nb):
@@ -188,7 +212,10 @@ class Runner:
     def step(self, i):
         s = self.sets[i % len(self.sets)]
         c = self.case
-        if self.dequant:
+        if self.gemm:
+            self.bsq.block_scaled_matmul_mfma(s["aq"], s["as"], s["bq"], s["bs"], c.fmt, c.K,
+                                              out=s["c"])
+        elif self.dequant:
             self.bsq.dequantize_block_scaled(s["q"], s["s"], c.fmt, c.K, c.tensor_sf, out=s["out"])
         elif self.producer and self.grouped:
             self.bsq.grouped_tensor_scale_nvfp4(s["x"], s["ro"], s["ids"], c.tensor_sf.size,
@@ -224,9 +251,11 @@ def time_steps(runner, steps, warmup):
 
 
 def measure(name, steps, warmup, rotate=True):
+    import workloads as W
     producer = name in PRODUCERS
     case = load_workload(PRODUCERS.get(name, name))
     nbytes, elems = producer_bytes(case) if producer else algorithmic_bytes(case)
+    rotate = rotate and not isinstance(case, W.GemmCase)   # a GEMM's operand reuse is its point
     nb = max(2, -(-3 * MALL_BYTES // max(nbytes, 1)) + 1) if rotate else 1
     nb = min(nb, 64)
     runner = Runner(case, nb, producer)
@@ -251,9 +280,11 @@ def summary(name, nbytes, elems, wall, launch_ms, steps, nb):
 
 # ------------------------------------------------------------------ CPU baseline
 
-def cpu_baseline(case, runner, target_seconds=8.0):
-    """Time the oracle (as it stands) on the first rows of the same input on
-    the host's cores; check the GPU's output for those rows."""
+def cpu_baseline(case, runner, target_cpu_seconds=12.0, max_wall_seconds=20.0):
+    """Time the oracle (as it stands) on the same input on the host's cores:
+    whole passes over the leading rows (all of them when the input is small)
+    until about target_cpu_seconds of CPU work (wall x threads) are done;
+    check the GPU's output for those rows."""
     import oracle
     torch = runner.torch
     threads = max(1, min(16, os.cpu_count() or 1))
@@ -261,12 +292,17 @@ def cpu_baseline(case, runner, target_seconds=8.0):
     probe = min(M, 64)
     t = time.perf_counter()
     oracle.quantize(case.x[:probe], case.fmt, case.tensor_sf, nthreads=threads)
-    per_row = (time.perf_counter() - t) / probe
-    rows = int(min(M, max(probe, target_seconds / max(per_row, 1e-9))))
-    t = time.perf_counter()
-    qh, sh = oracle.quantize(case.x[:rows], case.fmt, case.tensor_sf, nthreads=threads)
-    dt = time.perf_counter() - t
-    nbytes = rows * K * bytes_per_element(case.fmt)
+    per_row = (time.perf_counter() - t) / probe           # wall seconds per row
+    want_rows = target_cpu_seconds / threads / max(per_row, 1e-9)
+    rows = int(min(M, max(probe, want_rows)))
+    # whole passes over those rows until the CPU work (wall x threads) reaches the target
+    reps, dt = 0, 0.0
+    while reps == 0 or (dt * threads < target_cpu_seconds and dt < max_wall_seconds):
+        t = time.perf_counter()
+        qh, sh = oracle.quantize(case.x[:rows], case.fmt, case.tensor_sf, nthreads=threads)
+        dt += time.perf_counter() - t
+        reps += 1
+    nbytes = reps * rows * K * bytes_per_element(case.fmt)
     runner.step(0)
     torch.cuda.synchronize()
     s0 = runner.sets[0]
@@ -277,9 +313,9 @@ def cpu_baseline(case, runner, target_seconds=8.0):
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"first {rows} of {M} rows of the {case.name} input ({rows * K} elements, "
-                  f"{nbytes / 1e6:.1f} MB algorithmic), {dt:.2f} s wall on {threads} "
-                  f"thread(s)",
+        "sample": f"first {rows} of {M} rows of the {case.name} input, {reps} pass(es) "
+                  f"({reps * rows * K} elements, {nbytes / 1e6:.1f} MB algorithmic), "
+                  f"{dt:.2f} s wall on {threads} thread(s)",
         "parity_of_sample": "identical" if ok else "MISMATCH",
     }
 
@@ -342,7 +378,8 @@ def main():
     head = summary(args.workload, nbytes, elems, wall, kern, args.steps, nb)
     log("[bench] headline", json.dumps(head))
     achieved = nbytes / (kern * 1e-3) / 1e9
-    quantizer = args.workload not in PRODUCERS and not args.workload.startswith("dequant_")
+    quantizer = args.workload not in PRODUCERS and not args.workload.startswith(
+        ("dequant_", "mfma_gemm"))
     if not quantizer:
         traffic, traffic_note = None, "counters are taken on the quantizer only"
     else:
@@ -352,11 +389,17 @@ def main():
     if not args.no_secondary:
         for name in ("dense_nvfp4", "grouped_nvfp4", "dense_mxfp4", "grouped_mxfp4_decode",
                      "grouped_mxfp8_decode", "grouped_mxfp8", "grouped_mxfp4",
-                     "tsf_dense_nvfp4", "tsf_grouped_nvfp4", "dequant_mxfp8", "dequant_nvfp4"):
+                     "tsf_dense_nvfp4", "tsf_grouped_nvfp4", "dequant_mxfp8", "dequant_nvfp4",
+                     "mfma_gemm_mxfp8", "mfma_gemm_mxfp4"):
             if name == args.workload:
                 continue
             c2, r2, nb2, el2, nbs2, w2, k2 = measure(name, args.steps, args.warmup)
             s = summary(name, nb2, el2, w2, k2, args.steps, nbs2)
+            if name.startswith("mfma_gemm"):
+                tf = gemm_flops(c2) / (k2 * 1e-3) / 1e12
+                s.update({"bound": "mfma", "TFLOPs": round(tf, 1),
+                          "peak_TFLOPs": PEAK_MFMA_TFLOPS[c2.fmt],
+                          "frac_of_peak": round(tf / PEAK_MFMA_TFLOPS[c2.fmt], 4)})
             log("[bench] secondary", json.dumps(s))
             secondary.append(s)
             del r2, c2
@@ -368,7 +411,12 @@ def main():
         log("[bench] cpu_baseline", json.dumps(cpu))
 
     fmt_name = {0: "MXFP4", 1: "MXFP8", 2: "NVFP4"}[case.fmt]
-    rows, K = (case.codes.shape[0], case.K) if hasattr(case, "codes") else case.x.shape
+    if hasattr(case, "a_codes"):
+        rows, K = case.a_codes.shape[0], case.K
+    elif hasattr(case, "codes"):
+        rows, K = case.codes.shape[0], case.K
+    else:
+        rows, K = case.x.shape
     line = {
         "metric": METRIC,
         "value": round(nbytes * args.steps / wall / 1e9, 1),

@@ -197,6 +197,40 @@ def dequant_random_bytes(fmt: int, M: int, K: int, seed: int,
     return DequantCase(f"dequant_{name}_{M}x{K}", fmt, codes, scales, K, tensor_sf)
 
 
+@dataclass
+class GemmCase:
+    """Two MX operands for c = A B^T: codes row-major, scales already in the
+    MFMA 16x16x128 layout (random bytes)."""
+    name: str
+    fmt: int
+    a_codes: np.ndarray
+    a_scales: np.ndarray               # uint8 [ceil(M/16), 256 * ceil(K/512)]
+    b_codes: np.ndarray
+    b_scales: np.ndarray
+    K: int
+
+
+def gemm_random_operands(fmt: int, M: int, N: int, K: int, seed: int) -> GemmCase:
+    """Random codes (E4M3 NaN codes replaced by 1.0) and scale bytes in
+    [120, 134] (2^-7 .. 2^7) for both operands."""
+    rng = np.random.default_rng(seed)
+    width = K if fmt == MXFP8 else K // 2
+
+    def codes(rows):
+        c = rng.integers(0, 256, (rows, width), dtype=np.uint8)
+        if fmt == MXFP8:
+            c[(c & 0x7F) == 0x7F] = 0x38
+        return c
+
+    def scales(rows):
+        return rng.integers(120, 135, ((rows + 15) // 16, ((K // 32 + 15) // 16) * 256),
+                            dtype=np.uint8)
+
+    name = {MXFP4: "mxfp4", MXFP8: "mxfp8"}[fmt]
+    return GemmCase(f"mfma_gemm_{name}_{M}x{N}x{K}", fmt, codes(M), scales(M), codes(N),
+                    scales(N), K)
+
+
 def sweep_matrix(bs: int, background: str = "zeros", anchor_bits: int = 0,
                  seed: int = 0) -> np.ndarray:
     """[bs * 65536, bs] BF16 patterns.  Row p * 65536 + h holds pattern h at
