@@ -91,6 +91,29 @@ def test_pipeline_quantize_into_layout_then_mfma(bsq, fmt):
     assert abs(err - err_exact) <= 1e-3 * err_exact
 
 
+@pytest.mark.parametrize("fmt", [MXFP4, MXFP8])
+def test_nan_scale_and_nan_code(bsq, fmt):
+    """A block holding NaN or Inf gets the NaN scale 0xFF (and zero codes):
+    the instruction must turn its row of c into NaN, as the oracle does."""
+    K = 512
+    x = W.random_bf16((20, K), seed=9 + fmt, scale_log2_range=(-4, 4))
+    x[3, 100] = 0x7FC0                      # NaN in A row 3
+    y = W.random_bf16((18, K), seed=10 + fmt, scale_log2_range=(-4, 4))
+    y[7, 300] = 0xFF80                      # -Inf in B row 7
+    qa, sa = oracle.quantize(x, fmt, 1.0)
+    qb, sb = oracle.quantize(y, fmt, 1.0)
+    got = bsq.block_scaled_matmul_mfma(dev(qa), dev(oracle.scales_to_mfma16(sa)), dev(qb),
+                                       dev(oracle.scales_to_mfma16(sb)), fmt, K)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    want = oracle.block_scaled_matmul(qa, sa, qb, sb, fmt, K)
+    assert np.isnan(want[3]).all() and np.isnan(want[:, 7]).all()
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    S = magnitude_sum(qa, sa, qb, sb, fmt, K)
+    assert np.all(np.abs(got[ok] - want[ok]) <= REL_BOUND * S[ok])
+
+
 def test_zero_k_and_empty(bsq):
     z = bsq.block_scaled_matmul_mfma(torch.zeros((5, 0), dtype=torch.uint8, device="cuda"),
                                      torch.zeros((1, 0), dtype=torch.uint8, device="cuda"),
