@@ -63,6 +63,11 @@ int tile_knob() {
     }();
     return v;
 }
+//   BSQ_MFMA_TILED           matrix-core GEMM: 1 LDS-tiled (default), 2 one wave per 16 x 16 tile
+int mfma_tiled_knob() {
+    static const int v = env_knob("BSQ_MFMA_TILED");
+    return v;
+}
 //   BSQ_TSF_WAVES_PER_CU     tensor-scale reduction: resident waves per CU
 //   BSQ_TSF_WAVES_PER_BLOCK  tensor-scale reduction: waves per workgroup (4, 8, 16)
 constexpr int kTsfWavesPerCu = 16;
@@ -573,6 +578,7 @@ int block_scaled_matmul_mfma(int format, int block_size, int scale_layout,
     a.N = N;
     a.K = (int32_t)K;
     a.scale_layout = scale_layout;
+    a.tiled = mfma_tiled_knob() == 2 ? 0 : 1;
     const hipError_t e = bsq::launch_mfma_matmul(format, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

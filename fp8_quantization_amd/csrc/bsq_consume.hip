@@ -268,6 +268,170 @@ __global__ void __launch_bounds__(kThreadsPerBlock) mfma_matmul_kernel(const Gem
     }
 }
 
+// Tiled form: a workgroup of 4 waves computes a 128 x 128 tile of c, each
+// wave a 64 x 64 quarter as 4 x 4 instructions' 16 x 16 tiles.  Per stage
+// the workgroup stages 128 bytes of K of its 128 A rows and 128 B rows in LDS
+// (rows padded to 144 bytes so the 16 rows a fragment read touches fall in
+// different banks); the next stage's global loads are in flight while the
+// current stage's instructions run.  A stage is one 128-element K step for
+// E4M3 and two for E2M1; scale dwords are read once per 512 elements.
+constexpr int kTileM = 128, kTileN = 128;
+
+template <int FMT, int SB>
+struct TiledGemm {
+    static constexpr int kStageBytes = SB;                     // bytes of K per row per stage
+    static constexpr int kLdsRow = SB + 16;                    // padded LDS row
+    static constexpr int kStepBytes = FMT == 1 ? 128 : 64;      // bytes of one K step
+    static constexpr int kSteps = SB / kStepBytes;              // K steps per stage
+    static constexpr int kStageElems = kSteps * 128;
+    static constexpr int kStagesPer512 = kStageElems >= 512 ? 1 : 512 / kStageElems;
+    static constexpr int kPieces = SB / 32;                     // 16-byte pieces per thread
+};
+
+// 16 bytes of row `row` of an operand at byte `kb` of its codes, or zeros past
+// the rows or the row's bytes.
+__device__ __forceinline__ int4 load_piece(const uint8_t* codes, int64_t ldq, int64_t row,
+                                           int64_t rows, int kb, int row_bytes) {
+    if (row >= rows || kb >= row_bytes) return make_int4(0, 0, 0, 0);
+    return *reinterpret_cast<const int4*>(codes + row * ldq + kb);
+}
+
+template <int FMT, int SB>
+__global__ void __launch_bounds__(kThreadsPerBlock) mfma_gemm_tiled_kernel(const GemmArgs a,
+                                                                             int64_t tiles_n) {
+    using TG = TiledGemm<FMT, SB>;
+    constexpr int kFmt = FMT == 1 ? 0 : 4;
+    constexpr int kLdsRow = TG::kLdsRow;
+    static_assert(TG::kSteps * TG::kStagesPer512 <= 4 || TG::kStageElems == 512,
+                  "a stage spans at most one 512-element scale record");
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[kTileM * kLdsRow];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_b[kTileN * kLdsRow];
+    const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * kTileM;
+    const int64_t n0 = (int64_t)(blockIdx.x % tiles_n) * kTileN;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int row_bytes = FMT == 1 ? a.K : a.K / 2;
+    const int64_t groups_a = (a.M + 15) / 16, groups_b = (a.N + 15) / 16;
+
+    // global -> LDS: thread t moves row t / 2, bytes [SB/2 (t % 2), +SB/2) of the stage
+    const int lrow = tid >> 1, lcol = (tid & 1) * (SB / 2);
+    int4 pa[TG::kPieces], pb[TG::kPieces];
+    auto fetch = [&](int kb0) {
+#pragma unroll
+        for (int i = 0; i < TG::kPieces; ++i) {
+            pa[i] = load_piece(a.a_codes, a.lda_q, m0 + lrow, a.M, kb0 + lcol + 16 * i, row_bytes);
+            pb[i] = load_piece(a.b_codes, a.ldb_q, n0 + lrow, a.N, kb0 + lcol + 16 * i, row_bytes);
+        }
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int i = 0; i < TG::kPieces; ++i) {
+            *reinterpret_cast<int4*>(lds_a + lrow * kLdsRow + lcol + 16 * i) = pa[i];
+            *reinterpret_cast<int4*>(lds_b + lrow * kLdsRow + lcol + 16 * i) = pb[i];
+        }
+    };
+    // this lane's fragment of the 16-row subtile starting at LDS row r0, K step j of the stage
+    const int fr = lane & 15, fg = lane >> 4;
+    auto fragment = [&](const uint8_t* lds, int r0, int j) {
+        const uint8_t* row = lds + (r0 + fr) * kLdsRow + j * TG::kStepBytes;
+        mfma_v8i v;
+        if constexpr (FMT == 1) {
+            const int4 lo = *reinterpret_cast<const int4*>(row + 16 * fg);
+            const int4 hi = *reinterpret_cast<const int4*>(row + 64 + 16 * fg);
+            v = (mfma_v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        } else {
+            const int4 q = *reinterpret_cast<const int4*>(row + 16 * fg);
+            v = (mfma_v8i){q.x, q.y, q.z, q.w, 0, 0, 0, 0};
+        }
+        return v;
+    };
+    // scale dword of this lane for the 16-row group g of an operand, record k / 512
+    auto scale_dword = [&](const uint8_t* scales, int64_t lds_s, int64_t g, int64_t groups,
+                           int k512) -> uint32_t {
+        if (g >= groups) return 0x7F7F7F7Fu;   // rows past the operand: 2^0, zero codes
+        return *reinterpret_cast<const uint32_t*>(scales + g * lds_s + (int64_t)k512 * 256 +
+                                                  4 * lane);
+    };
+
+    mfma_v4f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = (mfma_v4f){0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int nstages = (a.K + TG::kStageElems - 1) / TG::kStageElems;
+    fetch(0);
+    int stage = 0;
+    for (int k512 = 0; k512 * 512 < a.K; ++k512) {
+        uint32_t sa[4], sb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sa[i] = scale_dword(a.a_scales, a.lda_s, (m0 >> 4) + 4 * wm + i, groups_a, k512);
+            sb[i] = scale_dword(a.b_scales, a.ldb_s, (n0 >> 4) + 4 * wn + i, groups_b, k512);
+        }
+#pragma unroll
+        for (int st = 0; st < TG::kStagesPer512; ++st, ++stage) {
+            if (stage >= nstages) break;
+            __syncthreads();                       // everyone is done reading the last stage
+            stash();
+            __syncthreads();
+            if (stage + 1 < nstages) fetch((stage + 1) * SB);
+#pragma unroll
+            for (int j = 0; j < TG::kSteps; ++j) {
+                if ((int64_t)stage * TG::kStageElems + j * 128 >= a.K) break;
+                const int t = st * TG::kSteps + j;  // K step within the 512: the opsel byte
+                mfma_v8i fb[4];
+#pragma unroll
+                for (int jn = 0; jn < 4; ++jn) fb[jn] = fragment(lds_b, 64 * wn + 16 * jn, j);
+#pragma unroll
+                for (int im = 0; im < 4; ++im) {
+                    const mfma_v8i fa = fragment(lds_a, 64 * wm + 16 * im, j);
+#pragma unroll
+                    for (int jn = 0; jn < 4; ++jn) {
+                        switch (t) {
+                            case 0: acc[im][jn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                        fa, fb[jn], acc[im][jn], kFmt, kFmt, 0, (int)sa[im], 0,
+                                        (int)sb[jn]); break;
+                            case 1: acc[im][jn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                        fa, fb[jn], acc[im][jn], kFmt, kFmt, 1, (int)sa[im], 1,
+                                        (int)sb[jn]); break;
+                            case 2: acc[im][jn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                        fa, fb[jn], acc[im][jn], kFmt, kFmt, 2, (int)sa[im], 2,
+                                        (int)sb[jn]); break;
+                            default: acc[im][jn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                        fa, fb[jn], acc[im][jn], kFmt, kFmt, 3, (int)sa[im], 3,
+                                        (int)sb[jn]); break;
+                        }
+                    }
+                }
+            }
+        }
+    }
+    // c: lane l holds rows 4 (l / 16) + e, column l % 16 of each 16 x 16 tile
+#pragma unroll
+    for (int im = 0; im < 4; ++im)
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn) {
+            const int64_t col = n0 + 64 * wn + 16 * jn + fr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t row = m0 + 64 * wm + 16 * im + 4 * fg + e;
+                if (row < a.M && col < a.N) a.c[row * a.ldc + col] = acc[im][jn][e];
+            }
+        }
+}
+
+template <int FMT>
+hipError_t launch_mfma_tiled(const GemmArgs& a, hipStream_t stream) {
+    const int64_t tiles_n = (a.N + kTileN - 1) / kTileN;
+    const int64_t tiles = ((a.M + kTileM - 1) / kTileM) * tiles_n;
+    // 128-byte stages: 256-byte ones (2 x the work per barrier) measured twice as slow, their
+    // registers and LDS leaving one workgroup per CU to hide the loads' latency
+    hipLaunchKernelGGL((mfma_gemm_tiled_kernel<FMT, 128>), dim3((uint32_t)tiles),
+                       dim3(kThreadsPerBlock), 0, stream, a, tiles_n);
+    return hipGetLastError();
+}
+
 template <int FMT>
 hipError_t launch_mfma_mm(const GemmArgs& a, hipStream_t stream) {
     const int64_t tiles_n = (a.N + 15) / 16;
@@ -318,9 +482,10 @@ hipError_t launch_dequantize(int fmt, const DequantArgs& a, int64_t blocks, hipS
 }
 
 hipError_t launch_mfma_matmul(int fmt, const GemmArgs& a, hipStream_t stream) {
+    const bool tiled = a.tiled != 0;
     switch (fmt) {
-        case 0: return launch_mfma_mm<0>(a, stream);
-        case 1: return launch_mfma_mm<1>(a, stream);
+        case 0: return tiled ? launch_mfma_tiled<0>(a, stream) : launch_mfma_mm<0>(a, stream);
+        case 1: return tiled ? launch_mfma_tiled<1>(a, stream) : launch_mfma_mm<1>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
