@@ -52,6 +52,10 @@ _lib.block_scaled_matmul_naive.restype = _i32
 _lib.block_scaled_matmul_mfma.argtypes = [_i32, _i32, _i32, _p, _i64, _p, _i64, _p, _i64, _p,
                                           _i64, _i64, _i64, _i64, _p, _i64, _p]
 _lib.block_scaled_matmul_mfma.restype = _i32
+_lib.grouped_block_scaled_matmul_mfma.argtypes = [_i32, _i32, _i32, _p, _i64, _p, _i64, _p, _p,
+                                                  _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _i64,
+                                                  _i64, _i64, _p, _i64, _p]
+_lib.grouped_block_scaled_matmul_mfma.restype = _i32
 _lib.bsq_last_error.argtypes = []
 _lib.bsq_last_error.restype = ctypes.c_char_p
 _lib.bsq_version.argtypes = []
@@ -285,4 +289,30 @@ def block_scaled_matmul_mfma(a_codes, a_scales, b_codes, b_scales, fmt, K: int, 
         f, BLOCK_SIZE.get(f, 0), SCALES_MFMA16, _ptr(a_codes), _ld(a_codes), _ptr(a_scales),
         _ld(a_scales), _ptr(b_codes), _ld(b_codes), _ptr(b_scales), _ld(b_scales), M, N, K,
         _ptr(out), _ld(out), _stream_ptr(stream, a_codes.device)))
+    return out
+
+
+def grouped_block_scaled_matmul_mfma(a_codes, a_scales, row_offsets, scales_offsets, expert_ids,
+                                     max_rows: int, num_scale_rows: int, b_codes, b_scales,
+                                     num_experts: int, fmt, K: int, out=None, stream=None):
+    """Per-expert c[r] = A[r] @ B[expert_ids[g]].T for the routed rows r of each
+    group g, on the matrix cores.  A: the grouped quantizer's MX output with
+    MFMA-layout scales (scales_offsets multiples of 16); B: [num_experts * N,
+    K/2 or K] codes and their MFMA-layout scales ([num_experts *
+    ceil(N/16), ...]).  Returns fp32 [max_rows, N]; rows no group owns are
+    left as they were (uninitialised in a new output)."""
+    f = _fmt(fmt)
+    a_codes, a_scales = _as_code_matrix("a_codes", a_codes), _as_code_matrix("a_scales", a_scales)
+    b_codes, b_scales = _as_code_matrix("b_codes", b_codes), _as_code_matrix("b_scales", b_scales)
+    if b_codes.shape[0] % num_experts:
+        raise ValueError("b_codes must hold num_experts * N rows")
+    N = b_codes.shape[0] // num_experts
+    G = expert_ids.shape[0]
+    if out is None:
+        out = torch.empty((max_rows, N), dtype=torch.float32, device=a_codes.device)
+    _check(_lib.grouped_block_scaled_matmul_mfma(
+        f, BLOCK_SIZE.get(f, 0), SCALES_MFMA16, _ptr(a_codes), _ld(a_codes), _ptr(a_scales),
+        _ld(a_scales), _ptr(row_offsets), _ptr(scales_offsets), _ptr(expert_ids), G, max_rows,
+        num_scale_rows, _ptr(b_codes), _ld(b_codes), _ptr(b_scales), _ld(b_scales), num_experts,
+        N, K, _ptr(out), _ld(out), _stream_ptr(stream, a_codes.device)))
     return out

@@ -584,6 +584,84 @@ int block_scaled_matmul_mfma(int format, int block_size, int scale_layout,
     return ok();
 }
 
+int grouped_block_scaled_matmul_mfma(int format, int block_size, int scale_layout,
+                                     const void* a_codes, int64_t lda_q, const void* a_scales,
+                                     int64_t lda_s,
+                                     const uint32_t* row_offsets, const uint32_t* scales_offsets,
+                                     const int32_t* expert_ids, int64_t num_groups,
+                                     int64_t max_rows, int64_t num_scale_rows,
+                                     const void* b_codes, int64_t ldb_q, const void* b_scales,
+                                     int64_t ldb_s, int64_t num_experts,
+                                     int64_t N, int64_t K, float* c, int64_t ldc, void* stream) {
+    int st = check_layout(format, block_size, scale_layout, max_rows, K);
+    if (st != BSQ_OK) return st;
+    if (format == BSQ_NVFP4)
+        return fail(BSQ_ERR_UNSUPPORTED, "the scaled matrix instruction takes MX formats only");
+    if (scale_layout != BSQ_SCALES_MFMA16)
+        return fail(BSQ_ERR_UNSUPPORTED, "the MFMA GEMM reads scales in the MFMA layout only");
+    if (N < 0 || num_groups < 0 || num_scale_rows < 0)
+        return fail(BSQ_ERR_INVALID_ARG, "negative size");
+    if (num_experts < 1 || num_experts > (1 << 24))
+        return fail(BSQ_ERR_INVALID_ARG, "num_experts=%lld must be in [1, 2^24]",
+                    (long long)num_experts);
+    if (num_groups > (1 << 24))
+        return fail(BSQ_ERR_INVALID_ARG, "num_groups=%lld too large", (long long)num_groups);
+    if (max_rows > (int64_t(1) << 32))
+        return fail(BSQ_ERR_INVALID_ARG, "max_rows=%lld exceeds the uint32 offset range",
+                    (long long)max_rows);
+    if (K % 128 != 0)
+        return fail(BSQ_ERR_INVALID_ARG, "K=%lld must be a multiple of 128 (one K step)",
+                    (long long)K);
+    if (num_groups == 0 || max_rows == 0 || N == 0) return ok();
+    if (!row_offsets || !scales_offsets || !expert_ids)
+        return fail(BSQ_ERR_INVALID_ARG, "row_offsets, scales_offsets and expert_ids are required");
+    if (K > 0) {
+        st = check_operand(format, K, a_codes, lda_q, a_scales, lda_s, "a_", scale_layout);
+        if (st != BSQ_OK) return st;
+        st = check_operand(format, K, b_codes, ldb_q, b_scales, ldb_s, "b_", scale_layout);
+        if (st != BSQ_OK) return st;
+        if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || lda_q % 16 != 0 || ldb_q % 16 != 0)
+            return fail(BSQ_ERR_INVALID_ARG,
+                        "code rows must be 16-byte aligned (codes and ldq multiples of 16)");
+        if (!aligned(a_scales, 4) || !aligned(b_scales, 4))
+            return fail(BSQ_ERR_INVALID_ARG, "scales must be 4-byte aligned");
+    }
+    if (!c || !aligned(c, 4)) return fail(BSQ_ERR_INVALID_ARG, "c must be a 4-byte aligned device array");
+    if (ldc < N) return fail(BSQ_ERR_INVALID_ARG, "ldc=%lld must be >= N=%lld", (long long)ldc,
+                             (long long)N);
+    bsq::GroupedGemmArgs g{};
+    g.row_offsets = row_offsets;
+    g.scales_offsets = scales_offsets;
+    g.expert_ids = expert_ids;
+    g.num_groups = (int32_t)num_groups;
+    g.num_experts = (int32_t)num_experts;
+    g.max_rows = max_rows;
+    g.num_scale_rows = num_scale_rows;
+    g.m_tiles = (max_rows + 127) / 128 + num_groups;   // each group adds at most one partial tile
+    if (g.m_tiles > 0x7FFFFFFFLL || (N + 127) / 128 > 65535)
+        return fail(BSQ_ERR_INVALID_ARG, "problem too large for one launch");
+    bsq::GemmArgs a{};
+    a.a_codes = static_cast<const uint8_t*>(a_codes);
+    a.lda_q = lda_q;
+    a.a_scales = static_cast<const uint8_t*>(a_scales);
+    a.lda_s = lda_s;
+    a.b_codes = static_cast<const uint8_t*>(b_codes);
+    a.ldb_q = ldb_q;
+    a.b_scales = static_cast<const uint8_t*>(b_scales);
+    a.ldb_s = ldb_s;
+    a.c = c;
+    a.ldc = ldc;
+    a.M = max_rows;
+    a.N = N;
+    a.K = (int32_t)K;
+    a.scale_layout = scale_layout;
+    a.tiled = 1;
+    const hipError_t e = bsq::launch_mfma_grouped_matmul(format, a, g,
+                                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 const char* bsq_last_error(void) { return g_last_error.c_str(); }
 
 const char* bsq_version(void) { return "1.0.0"; }

@@ -296,22 +296,32 @@ __device__ __forceinline__ int4 load_piece(const uint8_t* codes, int64_t ldq, in
     return *reinterpret_cast<const int4*>(codes + row * ldq + kb);
 }
 
+// One 128 x 128 tile of c: operand rows and scale groups relative to the
+// tile's first row, valid-row counts, and the output window.
+struct GemmTile {
+    const uint8_t* a;          // A codes, first row of the tile
+    int64_t lda_q, a_rows;     // row stride; rows that exist from here on
+    const uint8_t* as;         // A scales (MFMA layout), first row group of the tile
+    int64_t lda_s, a_groups;   // row-group stride; row groups that exist from here on
+    const uint8_t* b;
+    int64_t ldb_q, b_rows;
+    const uint8_t* bs;
+    int64_t ldb_s, b_groups;
+    float* c;                  // c[0, 0] of the tile
+    int64_t ldc, c_rows, c_cols;
+    int K;
+};
+
 template <int FMT, int SB>
-__global__ void __launch_bounds__(kThreadsPerBlock) mfma_gemm_tiled_kernel(const GemmArgs a,
-                                                                             int64_t tiles_n) {
+__device__ __forceinline__ void gemm_tile(const GemmTile& d, uint8_t* lds_a, uint8_t* lds_b) {
     using TG = TiledGemm<FMT, SB>;
     constexpr int kFmt = FMT == 1 ? 0 : 4;
     constexpr int kLdsRow = TG::kLdsRow;
     static_assert(TG::kSteps * TG::kStagesPer512 <= 4 || TG::kStageElems == 512,
                   "a stage spans at most one 512-element scale record");
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[kTileM * kLdsRow];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_b[kTileN * kLdsRow];
     const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * kTileM;
-    const int64_t n0 = (int64_t)(blockIdx.x % tiles_n) * kTileN;
     const int wm = wave >> 1, wn = wave & 1;
-    const int row_bytes = FMT == 1 ? a.K : a.K / 2;
-    const int64_t groups_a = (a.M + 15) / 16, groups_b = (a.N + 15) / 16;
+    const int row_bytes = FMT == 1 ? d.K : d.K / 2;
 
     // global -> LDS: thread t moves row t / 2, bytes [SB/2 (t % 2), +SB/2) of the stage
     const int lrow = tid >> 1, lcol = (tid & 1) * (SB / 2);
@@ -319,8 +329,8 @@ __global__ void __launch_bounds__(kThreadsPerBlock) mfma_gemm_tiled_kernel(const
     auto fetch = [&](int kb0) {
 #pragma unroll
         for (int i = 0; i < TG::kPieces; ++i) {
-            pa[i] = load_piece(a.a_codes, a.lda_q, m0 + lrow, a.M, kb0 + lcol + 16 * i, row_bytes);
-            pb[i] = load_piece(a.b_codes, a.ldb_q, n0 + lrow, a.N, kb0 + lcol + 16 * i, row_bytes);
+            pa[i] = load_piece(d.a, d.lda_q, lrow, d.a_rows, kb0 + lcol + 16 * i, row_bytes);
+            pb[i] = load_piece(d.b, d.ldb_q, lrow, d.b_rows, kb0 + lcol + 16 * i, row_bytes);
         }
     };
     auto stash = [&]() {
@@ -359,15 +369,15 @@ __global__ void __launch_bounds__(kThreadsPerBlock) mfma_gemm_tiled_kernel(const
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = (mfma_v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int nstages = (a.K + TG::kStageElems - 1) / TG::kStageElems;
+    const int nstages = (d.K + TG::kStageElems - 1) / TG::kStageElems;
     fetch(0);
     int stage = 0;
-    for (int k512 = 0; k512 * 512 < a.K; ++k512) {
+    for (int k512 = 0; k512 * 512 < d.K; ++k512) {
         uint32_t sa[4], sb[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            sa[i] = scale_dword(a.a_scales, a.lda_s, (m0 >> 4) + 4 * wm + i, groups_a, k512);
-            sb[i] = scale_dword(a.b_scales, a.ldb_s, (n0 >> 4) + 4 * wn + i, groups_b, k512);
+            sa[i] = scale_dword(d.as, d.lda_s, 4 * wm + i, d.a_groups, k512);
+            sb[i] = scale_dword(d.bs, d.ldb_s, 4 * wn + i, d.b_groups, k512);
         }
 #pragma unroll
         for (int st = 0; st < TG::kStagesPer512; ++st, ++stage) {
@@ -378,7 +388,7 @@ __global__ void __launch_bounds__(kThreadsPerBlock) mfma_gemm_tiled_kernel(const
             if (stage + 1 < nstages) fetch((stage + 1) * SB);
 #pragma unroll
             for (int j = 0; j < TG::kSteps; ++j) {
-                if ((int64_t)stage * TG::kStageElems + j * 128 >= a.K) break;
+                if ((int64_t)stage * TG::kStageElems + j * 128 >= d.K) break;
                 const int t = st * TG::kSteps + j;  // K step within the 512: the opsel byte
                 mfma_v8i fb[4];
 #pragma unroll
@@ -412,13 +422,99 @@ __global__ void __launch_bounds__(kThreadsPerBlock) mfma_gemm_tiled_kernel(const
     for (int im = 0; im < 4; ++im)
 #pragma unroll
         for (int jn = 0; jn < 4; ++jn) {
-            const int64_t col = n0 + 64 * wn + 16 * jn + fr;
+            const int64_t col = 64 * wn + 16 * jn + fr;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int64_t row = m0 + 64 * wm + 16 * im + 4 * fg + e;
-                if (row < a.M && col < a.N) a.c[row * a.ldc + col] = acc[im][jn][e];
+                const int64_t row = 64 * wm + 16 * im + 4 * fg + e;
+                if (row < d.c_rows && col < d.c_cols) d.c[row * d.ldc + col] = acc[im][jn][e];
             }
         }
+}
+
+
+template <int FMT, int SB>
+__global__ void __launch_bounds__(kThreadsPerBlock) mfma_gemm_tiled_kernel(const GemmArgs a,
+                                                                             int64_t tiles_n) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[kTileM * TiledGemm<FMT, SB>::kLdsRow];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_b[kTileN * TiledGemm<FMT, SB>::kLdsRow];
+    const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * kTileM;
+    const int64_t n0 = (int64_t)(blockIdx.x % tiles_n) * kTileN;
+    GemmTile d;
+    d.a = a.a_codes + m0 * a.lda_q;
+    d.lda_q = a.lda_q;
+    d.a_rows = a.M - m0;
+    d.as = a.a_scales + (m0 >> 4) * a.lda_s;
+    d.lda_s = a.lda_s;
+    d.a_groups = (a.M + 15) / 16 - (m0 >> 4);
+    d.b = a.b_codes + n0 * a.ldb_q;
+    d.ldb_q = a.ldb_q;
+    d.b_rows = a.N - n0;
+    d.bs = a.b_scales + (n0 >> 4) * a.ldb_s;
+    d.ldb_s = a.ldb_s;
+    d.b_groups = (a.N + 15) / 16 - (n0 >> 4);
+    d.c = a.c + m0 * a.ldc + n0;
+    d.ldc = a.ldc;
+    d.c_rows = a.M - m0;
+    d.c_cols = a.N - n0;
+    d.K = a.K;
+    gemm_tile<FMT, SB>(d, lds_a, lds_b);
+}
+
+// Grouped per-expert form: blockIdx.y is the 128-column tile of c, blockIdx.x
+// a 128-row tile counted across the groups in order (group g has
+// ceil(m_g / 128) of them); each workgroup finds its group by scanning the
+// offsets.  Group g multiplies its routed rows (codes row r, scale row
+// scales_offsets[g] + r - row_offsets[g]) by the B of expert expert_ids[g]
+// ([N, K] codes from row e N, scales from row group e ceil(N / 16)).  A group
+// whose metadata falls outside the buffers, or whose scale offset is not a
+// multiple of 16 (the layout's row groups), is skipped.
+template <int FMT, int SB>
+__global__ void __launch_bounds__(kThreadsPerBlock)
+mfma_gemm_grouped_kernel(const GemmArgs a, const GroupedGemmArgs g) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[kTileM * TiledGemm<FMT, SB>::kLdsRow];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_b[kTileN * TiledGemm<FMT, SB>::kLdsRow];
+    const int64_t n0 = (int64_t)blockIdx.y * kTileN;
+    int64_t t = blockIdx.x;
+    int grp = -1;
+    int64_t lo = 0, hi = 0;
+    for (int h = 0; h < g.num_groups; ++h) {
+        const int64_t l = g.row_offsets[h], u = g.row_offsets[h + 1];
+        const int64_t tiles = u > l ? (u - l + kTileM - 1) / kTileM : 0;
+        if (t < tiles) {
+            grp = h;
+            lo = l;
+            hi = u;
+            break;
+        }
+        t -= tiles;
+    }
+    if (grp < 0) return;                                     // past the last group's tiles
+    const int e = g.expert_ids[grp];
+    const int64_t so = g.scales_offsets[grp];
+    const int64_t r0 = lo + t * kTileM;
+    if (hi > g.max_rows || e < 0 || e >= g.num_experts || so % 16 != 0 ||
+        so + (hi - lo) > g.num_scale_rows)
+        return;
+    const int64_t groups_n = (a.N + 15) / 16;
+    GemmTile d;
+    d.a = a.a_codes + r0 * a.lda_q;
+    d.lda_q = a.lda_q;
+    d.a_rows = hi - r0;
+    d.as = a.a_scales + ((so + t * kTileM) >> 4) * a.lda_s;
+    d.lda_s = a.lda_s;
+    d.a_groups = (hi - r0 + 15) / 16;
+    d.b = a.b_codes + ((int64_t)e * a.N + n0) * a.ldb_q;
+    d.ldb_q = a.ldb_q;
+    d.b_rows = a.N - n0;
+    d.bs = a.b_scales + ((int64_t)e * groups_n + (n0 >> 4)) * a.ldb_s;
+    d.ldb_s = a.ldb_s;
+    d.b_groups = groups_n - (n0 >> 4);
+    d.c = a.c + r0 * a.ldc + n0;
+    d.ldc = a.ldc;
+    d.c_rows = hi - r0;
+    d.c_cols = a.N - n0;
+    d.K = a.K;
+    gemm_tile<FMT, SB>(d, lds_a, lds_b);
 }
 
 template <int FMT>
@@ -477,6 +573,25 @@ hipError_t launch_dequantize(int fmt, const DequantArgs& a, int64_t blocks, hipS
         case 0: return launch_dq<0>(a, blocks, stream);
         case 1: return launch_dq<1>(a, blocks, stream);
         case 2: return launch_dq<2>(a, blocks, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+namespace {
+template <int FMT>
+hipError_t launch_mfma_grouped(const GemmArgs& a, const GroupedGemmArgs& g, hipStream_t stream) {
+    const dim3 grid((uint32_t)g.m_tiles, (uint32_t)((a.N + kTileN - 1) / kTileN));
+    hipLaunchKernelGGL((mfma_gemm_grouped_kernel<FMT, 128>), grid, dim3(kThreadsPerBlock), 0,
+                       stream, a, g);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_mfma_grouped_matmul(int fmt, const GemmArgs& a, const GroupedGemmArgs& g,
+                                      hipStream_t stream) {
+    switch (fmt) {
+        case 0: return launch_mfma_grouped<0>(a, g, stream);
+        case 1: return launch_mfma_grouped<1>(a, g, stream);
         default: return hipErrorInvalidValue;
     }
 }

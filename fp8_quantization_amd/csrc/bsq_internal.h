@@ -110,6 +110,21 @@ hipError_t launch_naive_matmul(int fmt, const GemmArgs& a, hipStream_t stream);
 // MX formats, scales in the MFMA layout, K % 128 == 0, 16-byte aligned code rows.
 hipError_t launch_mfma_matmul(int fmt, const GemmArgs& a, hipStream_t stream);
 
+// Grouped per-expert GEMM: A rows grouped by row_offsets (scale rows by
+// scales_offsets), B = num_experts stacked [N, K] operands; GemmArgs.M unused.
+struct GroupedGemmArgs {
+    const uint32_t* row_offsets;     // [num_groups + 1]
+    const uint32_t* scales_offsets;  // [num_groups + 1]
+    const int32_t* expert_ids;       // [num_groups]
+    int32_t num_groups;
+    int32_t num_experts;
+    int64_t max_rows;                // rows of A codes and of c
+    int64_t num_scale_rows;          // scale rows of A
+    int64_t m_tiles;                 // grid bound on 128-row tiles over all groups
+};
+hipError_t launch_mfma_grouped_matmul(int fmt, const GemmArgs& a, const GroupedGemmArgs& g,
+                                      hipStream_t stream);
+
 // Launch the dense (grouped = false) or grouped kernel for format fmt
 // (0 MXFP4, 1 MXFP8, 2 NVFP4).  Returns the launch status.
 hipError_t launch_quantize(int fmt, bool grouped, const KernelArgs& a, int64_t blocks,

@@ -286,6 +286,43 @@ int block_scaled_matmul_mfma(int format, int block_size, int scale_layout,
                              int64_t M, int64_t N, int64_t K, float* c, int64_t ldc,
                              void* stream);
 
+/*
+ * Grouped per-expert block-scaled GEMM on the matrix cores (the counterpart
+ * of the grouped per-expert MXFP4 matmul the "block_scaled_quantization"
+ * module page lists for CDNA4): for each group g with expert e =
+ * expert_ids[g], the routed rows r in [row_offsets[g], row_offsets[g+1]) get
+ *     c[r, n] = sum over k of A[r, k] * B_e[n, k],
+ * A being the grouped quantizer's output (codes row r; scales in the MFMA
+ * layout at scale row scales_offsets[g] + r - row_offsets[g]) and B_e
+ * expert e's weights.  Rows of c no group owns are not written.  Accuracy
+ * as for block_scaled_matmul_mfma.
+ *
+ *   format, block_size, scale_layout   as for block_scaled_matmul_mfma.
+ *   a_codes, lda_q       [max_rows, K] codes (routed order), 16-byte aligned rows.
+ *   a_scales, lda_s      MFMA-layout scales over num_scale_rows rows.
+ *   row_offsets, scales_offsets, expert_ids, num_groups   as for the grouped
+ *                        quantizer; each scales_offsets[g] must be a multiple
+ *                        of 16 (the layout's row groups) -- a group that is
+ *                        not, or whose rows or scale rows fall outside
+ *                        max_rows / num_scale_rows, or whose expert id is out
+ *                        of range, is skipped.
+ *   b_codes, ldb_q       [num_experts * N, K] codes: expert e's rows e*N .. e*N+N-1.
+ *   b_scales, ldb_s      MFMA-layout scales of those rows, expert e's row
+ *                        groups starting at e * ceil(N / 16).
+ *   num_experts          >= 1.   N, K: K % 128 == 0.
+ *   c, ldc               fp32 [max_rows, ldc], ldc >= N.
+ *   num_groups == 0, max_rows == 0 or N == 0 is a no-op.
+ */
+int grouped_block_scaled_matmul_mfma(int format, int block_size, int scale_layout,
+                                     const void* a_codes, int64_t lda_q, const void* a_scales,
+                                     int64_t lda_s,
+                                     const uint32_t* row_offsets, const uint32_t* scales_offsets,
+                                     const int32_t* expert_ids, int64_t num_groups,
+                                     int64_t max_rows, int64_t num_scale_rows,
+                                     const void* b_codes, int64_t ldb_q, const void* b_scales,
+                                     int64_t ldb_s, int64_t num_experts,
+                                     int64_t N, int64_t K, float* c, int64_t ldc, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if
    none).  The pointer stays valid until the next call on that thread. */
 const char* bsq_last_error(void);

@@ -60,7 +60,8 @@ def test_header_declares_the_abi():
                                            "grouped_tensor_scale_nvfp4",
                                            "dequantize_block_scaled",
                                            "block_scaled_matmul_naive",
-                                           "block_scaled_matmul_mfma"])
+                                           "block_scaled_matmul_mfma",
+                                           "grouped_block_scaled_matmul_mfma"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -242,6 +243,30 @@ def test_mfma_matmul_validation(lib):
     assert mm(c=None) == INVALID
     assert mm(ldc=8) == INVALID
     assert mm(M=0, a=None, b=None, c=None) == OK
+
+
+def test_grouped_mfma_matmul_validation(lib):
+    i64, i32, p = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    f = lib.grouped_block_scaled_matmul_mfma
+    f.argtypes = [i32, i32, i32, p, i64, p, i64, p, p, p, i64, i64, i64, p, i64, p, i64, i64, i64,
+                  i64, p, i64, p]
+
+    def gm(fmt=MXFP4, bs=32, layout=1, G=2, max_rows=64, nsr=64, E=2, N=32, K=512, ro=FAKE,
+           a=FAKE, c=FAKE, ldc=32):
+        ldq = K if fmt == MXFP8 else K // 2
+        return f(fmt, bs, layout, a, ldq, FAKE, 256, ro, FAKE, FAKE, G, max_rows, nsr, FAKE, ldq,
+                 FAKE, 256, E, N, K, c, ldc, None)
+    assert gm(fmt=NVFP4, bs=16) == UNSUPPORTED
+    assert gm(layout=0) == UNSUPPORTED
+    assert gm(E=0) == INVALID
+    assert gm(K=96) == INVALID
+    assert gm(ro=None) == INVALID
+    assert gm(a=FAKE + 8) == INVALID
+    assert gm(c=None) == INVALID
+    assert gm(ldc=16) == INVALID
+    assert gm(max_rows=(1 << 32) + 1) == INVALID
+    assert gm(G=0, ro=None, a=None, c=None) == OK
+    assert gm(N=0, ro=None, a=None, c=None) == OK
 
 
 def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):

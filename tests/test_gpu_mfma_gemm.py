@@ -114,6 +114,78 @@ def test_nan_scale_and_nan_code(bsq, fmt):
     assert np.all(np.abs(got[ok] - want[ok]) <= REL_BOUND * S[ok])
 
 
+def grouped_case(fmt, G, E, N, K, rows, seed, misaligned=None):
+    """Routed activations quantized by the oracle's grouped quantizer (scales
+    then mapped into the MFMA layout) and E experts' [N, K] weights (one
+    layout per expert, stacked)."""
+    rng = np.random.default_rng(seed)
+    S = rows + 10
+    x = W.random_bf16((S, K), seed=seed, scale_log2_range=(-6, 6))
+    w = rng.random(G) * (rng.random(G) > 0.3)
+    w[0] += 1e-3
+    counts = rng.multinomial(rows, w / w.sum())
+    ro = np.concatenate([[0], np.cumsum(counts)]).astype(np.uint32)
+    pads = -(-counts // 16) * 16 + 16 * rng.integers(0, 2, G)          # some extra padding
+    so = np.concatenate([[0], np.cumsum(pads)]).astype(np.uint32)
+    if misaligned is not None:                                          # shift one group's scales
+        so[misaligned] += 8
+    ids = rng.integers(0, E, G).astype(np.int32)
+    max_rows, nsr = int(ro[-1]) + 7, int(so[-1]) + 16
+    width = K if fmt == MXFP8 else K // 2
+    qa, sa = oracle.grouped_quantize(x, fmt, ro, so, ids, None, max_rows, nsr,
+                                     codes=np.zeros((max_rows, width), np.uint8),
+                                     scales=np.zeros((nsr, K // 32), np.uint8), nthreads=NTHREADS)
+    wb = W.random_bf16((E * N, K), seed=seed + 1, scale_log2_range=(-6, 6))
+    qb, sb = oracle.quantize(wb, fmt, 1.0, nthreads=NTHREADS)
+    lb = np.concatenate([oracle.scales_to_mfma16(sb[e * N:(e + 1) * N]) for e in range(E)])
+    return dict(qa=qa, sa=sa, la=oracle.scales_to_mfma16(sa), ro=ro, so=so, ids=ids,
+                max_rows=max_rows, nsr=nsr, qb=qb, sb=sb, lb=lb, counts=counts)
+
+
+@pytest.mark.parametrize("fmt", [MXFP4, MXFP8])
+@pytest.mark.parametrize("G,E,N,K,rows", [(1, 1, 128, 256, 128), (5, 3, 100, 512, 300),
+                                          (40, 16, 160, 1024, 900), (9, 4, 256, 7168, 700)])
+def test_grouped_mfma_matches_oracle(bsq, fmt, G, E, N, K, rows):
+    d = grouped_case(fmt, G, E, N, K, rows, seed=G + N + K + fmt)
+    out = torch.full((d["max_rows"], N), 7.0, dtype=torch.float32, device="cuda")
+    bsq.grouped_block_scaled_matmul_mfma(
+        dev(d["qa"]), dev(d["la"]), dev(d["ro"].view(np.int32)), dev(d["so"].view(np.int32)),
+        dev(d["ids"]), d["max_rows"], d["nsr"], dev(d["qb"]), dev(d["lb"]), E, fmt, K, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    owned = np.zeros(d["max_rows"], bool)
+    worst = 0.0
+    for g in range(G):
+        lo, hi, so, e = int(d["ro"][g]), int(d["ro"][g + 1]), int(d["so"][g]), int(d["ids"][g])
+        if hi == lo:
+            continue
+        owned[lo:hi] = True
+        qa, sa = d["qa"][lo:hi], d["sa"][so:so + hi - lo]
+        qb, sb = d["qb"][e * N:(e + 1) * N], d["sb"][e * N:(e + 1) * N]
+        want = oracle.block_scaled_matmul(qa, sa, qb, sb, fmt, K)
+        S = magnitude_sum(qa, sa, qb, sb, fmt, K)
+        err = np.abs(got[lo:hi] - want)
+        assert np.all(err <= REL_BOUND * S), g
+        worst = max(worst, float(np.max(err / np.maximum(S, 1e-300))))
+    assert np.all(got[~owned] == 7.0)              # rows no group owns are not written
+    print(f"format {fmt} G={G} N={N} K={K}: max |err| / sum|ab| = {worst:.3e}")
+
+
+def test_grouped_mfma_skips_a_misaligned_group(bsq):
+    fmt, G, E, N, K = MXFP8, 6, 3, 64, 512
+    d = grouped_case(fmt, G, E, N, K, 400, seed=77, misaligned=2)
+    out = torch.full((d["max_rows"], N), 7.0, dtype=torch.float32, device="cuda")
+    bsq.grouped_block_scaled_matmul_mfma(
+        dev(d["qa"]), dev(d["la"]), dev(d["ro"].view(np.int32)), dev(d["so"].view(np.int32)),
+        dev(d["ids"]), d["max_rows"], d["nsr"], dev(d["qb"]), dev(d["lb"]), E, fmt, K, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    lo, hi = int(d["ro"][2]), int(d["ro"][3])
+    assert hi > lo and np.all(got[lo:hi] == 7.0)    # scale offset not a multiple of 16: skipped
+    lo1, hi1 = int(d["ro"][1]), int(d["ro"][2])
+    assert hi1 == lo1 or np.all(got[lo1:hi1] != 7.0)
+
+
 def test_zero_k_and_empty(bsq):
     z = bsq.block_scaled_matmul_mfma(torch.zeros((5, 0), dtype=torch.uint8, device="cuda"),
                                      torch.zeros((1, 0), dtype=torch.uint8, device="cuda"),
