@@ -71,6 +71,7 @@ def load_workload(name):
         # the matrix-core consumer of the MFMA scale layout
         "mfma_gemm_mxfp8": lambda: W.gemm_random_operands(W.MXFP8, 4096, 4096, 7168, seed=1202),
         "mfma_gemm_mxfp4": lambda: W.gemm_random_operands(W.MXFP4, 4096, 4096, 7168, seed=1201),
+        "mfma_grouped_gemm_mxfp4": lambda: W.grouped_gemm_prefill(W.MXFP4),
     }
     return table[name]()
 
@@ -106,6 +107,10 @@ PEAK_MFMA_TFLOPS = {0: 10100.0, 1: 5000.0}
 
 
 def gemm_flops(case):
+    import workloads as W
+    if isinstance(case, W.GroupedGemmCase):
+        routed = int(case.row_offsets[-1]) - int(case.row_offsets[0])
+        return 2 * routed * (case.b_codes.shape[0] // case.num_experts) * case.K
     return 2 * case.a_codes.shape[0] * case.b_codes.shape[0] * case.K
 
 
@@ -120,6 +125,11 @@ def algorithmic_bytes(case):
     import workloads as W
     if isinstance(case, W.DequantCase):
         return dequant_bytes(case)
+    if isinstance(case, W.GroupedGemmCase):   # operands and metadata read once + c written
+        N = case.b_codes.shape[0] // case.num_experts
+        meta = 4 * (case.row_offsets.size + case.scales_offsets.size + case.expert_ids.size)
+        return int(case.a_codes.nbytes + case.a_scales.nbytes + case.b_codes.nbytes +
+                   case.b_scales.nbytes + meta + 4 * case.max_rows * N), case.max_rows * N
     if isinstance(case, W.GemmCase):    # operands read once + c written
         M, N = case.a_codes.shape[0], case.b_codes.shape[0]
         return int(case.a_codes.nbytes + case.a_scales.nbytes + case.b_codes.nbytes +
@@ -156,16 +166,23 @@ class Runner:
         import workloads as W
         self.bsq, self.torch, self.case = bsq, torch, case
         self.dequant = isinstance(case, W.DequantCase)
-        self.gemm = isinstance(case, W.GemmCase)
+        self.gemm = isinstance(case, (W.GemmCase, W.GroupedGemmCase))
+        self.grouped_gemm = isinstance(case, W.GroupedGemmCase)
         self.grouped = isinstance(case, W.GroupedCase)
         self.producer = producer
         self.sets = []
         if self.gemm:
-            t = lambda a: torch.from_numpy(a).cuda()
-            self.sets.append({"aq": t(case.a_codes), "as": t(case.a_scales),
-                              "bq": t(case.b_codes), "bs": t(case.b_scales),
-                              "c": torch.empty((case.a_codes.shape[0], case.b_codes.shape[0]),
-                                               dtype=torch.float32, device="cuda")})
+            t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+            n_out = case.b_codes.shape[0] // (case.num_experts if self.grouped_gemm else 1)
+            s = {"aq": t(case.a_codes), "as": t(case.a_scales), "bq": t(case.b_codes),
+                 "bs": t(case.b_scales),
+                 "c": torch.empty((case.a_codes.shape[0], n_out), dtype=torch.float32,
+                                  device="cuda")}
+            if self.grouped_gemm:
+                s["ro"] = t(case.row_offsets.view(np.int32))
+                s["so"] = t(case.scales_offsets.view(np.int32))
+                s["ids"] = t(case.expert_ids)
+            self.sets.append(s)
             torch.cuda.synchronize()
             return
         if self.dequant:
@@ -212,7 +229,11 @@ class Runner:
     def step(self, i):
         s = self.sets[i % len(self.sets)]
         c = self.case
-        if self.gemm:
+        if self.grouped_gemm:
+            self.bsq.grouped_block_scaled_matmul_mfma(
+                s["aq"], s["as"], s["ro"], s["so"], s["ids"], c.max_rows, c.num_scale_rows,
+                s["bq"], s["bs"], c.num_experts, c.fmt, c.K, out=s["c"])
+        elif self.gemm:
             self.bsq.block_scaled_matmul_mfma(s["aq"], s["as"], s["bq"], s["bs"], c.fmt, c.K,
                                               out=s["c"])
         elif self.dequant:
@@ -255,7 +276,7 @@ def measure(name, steps, warmup, rotate=True):
     producer = name in PRODUCERS
     case = load_workload(PRODUCERS.get(name, name))
     nbytes, elems = producer_bytes(case) if producer else algorithmic_bytes(case)
-    rotate = rotate and not isinstance(case, W.GemmCase)   # a GEMM's operand reuse is its point
+    rotate = rotate and not isinstance(case, (W.GemmCase, W.GroupedGemmCase))  # reuse is the point
     nb = max(2, -(-3 * MALL_BYTES // max(nbytes, 1)) + 1) if rotate else 1
     nb = min(nb, 64)
     runner = Runner(case, nb, producer)
@@ -379,7 +400,7 @@ def main():
     log("[bench] headline", json.dumps(head))
     achieved = nbytes / (kern * 1e-3) / 1e9
     quantizer = args.workload not in PRODUCERS and not args.workload.startswith(
-        ("dequant_", "mfma_gemm"))
+        ("dequant_", "mfma_gemm", "mfma_grouped_gemm"))
     if not quantizer:
         traffic, traffic_note = None, "counters are taken on the quantizer only"
     else:
@@ -390,16 +411,18 @@ def main():
         for name in ("dense_nvfp4", "grouped_nvfp4", "dense_mxfp4", "grouped_mxfp4_decode",
                      "grouped_mxfp8_decode", "grouped_mxfp8", "grouped_mxfp4",
                      "tsf_dense_nvfp4", "tsf_grouped_nvfp4", "dequant_mxfp8", "dequant_nvfp4",
-                     "mfma_gemm_mxfp8", "mfma_gemm_mxfp4"):
+                     "mfma_gemm_mxfp8", "mfma_gemm_mxfp4", "mfma_grouped_gemm_mxfp4"):
             if name == args.workload:
                 continue
             c2, r2, nb2, el2, nbs2, w2, k2 = measure(name, args.steps, args.warmup)
             s = summary(name, nb2, el2, w2, k2, args.steps, nbs2)
-            if name.startswith("mfma_gemm"):
+            if name.startswith(("mfma_gemm", "mfma_grouped_gemm")):
                 tf = gemm_flops(c2) / (k2 * 1e-3) / 1e12
-                s.update({"bound": "mfma", "TFLOPs": round(tf, 1),
-                          "peak_TFLOPs": PEAK_MFMA_TFLOPS[c2.fmt],
-                          "frac_of_peak": round(tf / PEAK_MFMA_TFLOPS[c2.fmt], 4)})
+                peak = PEAK_MFMA_TFLOPS[c2.fmt]
+                # the bound is whichever ideal time is longer: flops at the peak or bytes at 8 TB/s
+                hbm_bound = nb2 / PEAK_HBM_GBS / 1e9 > gemm_flops(c2) / peak / 1e12
+                s.update({"bound": "hbm" if hbm_bound else "mfma", "TFLOPs": round(tf, 1),
+                          "peak_TFLOPs": peak, "frac_of_peak": round(tf / peak, 4)})
             log("[bench] secondary", json.dumps(s))
             secondary.append(s)
             del r2, c2

@@ -231,6 +231,51 @@ def gemm_random_operands(fmt: int, M: int, N: int, K: int, seed: int) -> GemmCas
                     scales(N), K)
 
 
+@dataclass
+class GroupedGemmCase:
+    """Routed MX activations (codes in routed order, MFMA-layout scales at
+    padded scale rows) and per-expert MX weights [num_experts * N, K]."""
+    name: str
+    fmt: int
+    a_codes: np.ndarray
+    a_scales: np.ndarray
+    row_offsets: np.ndarray
+    scales_offsets: np.ndarray
+    expert_ids: np.ndarray
+    max_rows: int
+    num_scale_rows: int
+    b_codes: np.ndarray
+    b_scales: np.ndarray
+    num_experts: int
+    K: int
+
+
+def grouped_gemm_prefill(fmt: int = MXFP4, seed: int = 1203, rows: int = 16384, K: int = 7168,
+                         N: int = 512, experts: int = 128, alpha: float = 0.3) -> GroupedGemmCase:
+    """The prefill routing (multinomial over Dirichlet(alpha) per-expert
+    counts, scale rows padded to 128 per expert) with random codes and scale
+    bytes in [120, 134] for the activations and for E experts' [N, K] weights."""
+    rng = np.random.default_rng(seed)
+    counts = rng.multinomial(rows, rng.dirichlet([alpha] * experts))
+    ro, so = offsets_from_counts(counts, 128)
+    width = K if fmt == MXFP8 else K // 2
+    rec = ((K // 32 + 15) // 16) * 256
+
+    def codes(n):
+        c = rng.integers(0, 256, (n, width), dtype=np.uint8)
+        if fmt == MXFP8:
+            c[(c & 0x7F) == 0x7F] = 0x38
+        return c
+
+    nsr = int(so[-1])
+    a_scales = rng.integers(120, 135, ((nsr + 15) // 16, rec), dtype=np.uint8)
+    b_scales = rng.integers(120, 135, (experts * ((N + 15) // 16), rec), dtype=np.uint8)
+    name = {MXFP4: "mxfp4", MXFP8: "mxfp8"}[fmt]
+    return GroupedGemmCase(f"mfma_grouped_gemm_{name}_{rows}x{N}x{K}_e{experts}", fmt,
+                           codes(rows), a_scales, ro, so, np.arange(experts, dtype=np.int32),
+                           rows, nsr, codes(experts * N), b_scales, experts, K)
+
+
 def sweep_matrix(bs: int, background: str = "zeros", anchor_bits: int = 0,
                  seed: int = 0) -> np.ndarray:
     """[bs * 65536, bs] BF16 patterns.  Row p * 65536 + h holds pattern h at
