@@ -63,7 +63,9 @@ int tile_knob() {
     }();
     return v;
 }
-//   BSQ_MFMA_TILED           matrix-core GEMM: 1 LDS-tiled (default), 2 one wave per 16 x 16 tile
+//   BSQ_MFMA_TILED           matrix-core GEMM: 128 x 128 tiles with two LDS stage buffers
+//                            (default); 2 one wave per 16 x 16 tile (dense); 3 three stage
+//                            buffers
 int mfma_tiled_knob() {
     static const int v = env_knob("BSQ_MFMA_TILED");
     return v;
@@ -578,7 +580,7 @@ int block_scaled_matmul_mfma(int format, int block_size, int scale_layout,
     a.N = N;
     a.K = (int32_t)K;
     a.scale_layout = scale_layout;
-    a.tiled = mfma_tiled_knob() == 2 ? 0 : 1;
+    a.tiled = mfma_tiled_knob() == 2 ? 0 : mfma_tiled_knob() == 3 ? 3 : 1;
     const hipError_t e = bsq::launch_mfma_matmul(format, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -655,7 +657,7 @@ int grouped_block_scaled_matmul_mfma(int format, int block_size, int scale_layou
     a.N = N;
     a.K = (int32_t)K;
     a.scale_layout = scale_layout;
-    a.tiled = 1;
+    a.tiled = mfma_tiled_knob() == 3 ? 3 : 1;
     const hipError_t e = bsq::launch_mfma_grouped_matmul(format, a, g,
                                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

@@ -1,6 +1,7 @@
 // bsq_consume.hip -- gfx950 kernels that read block-scaled codes back: the
-// dequantization to fp32 and a naive block-scaled GEMM (no MFMA), the
-// consumer-side check of the quantizers' output.  The Modular
+// dequantization to fp32, a naive block-scaled GEMM (no MFMA) as the
+// consumer-side check of the quantizers' output, and the dense and grouped
+// block-scaled GEMMs on the matrix cores.  The Modular
 // "block_scaled_quantization" module page lists a naive block-scaled matmul
 // as the reference GEMM over such operands; the decode direction of the
 // scales follows the quantizer's readings: an MX value is code * 2^(b - 127),
@@ -269,32 +270,11 @@ __global__ void __launch_bounds__(kThreadsPerBlock) mfma_matmul_kernel(const Gem
 }
 
 // Tiled form: a workgroup of 4 waves computes a 128 x 128 tile of c, each
-// wave a 64 x 64 quarter as 4 x 4 instructions' 16 x 16 tiles.  Per stage
-// the workgroup stages 128 bytes of K of its 128 A rows and 128 B rows in LDS
-// (rows padded to 144 bytes so the 16 rows a fragment read touches fall in
-// different banks); the next stage's global loads are in flight while the
-// current stage's instructions run.  A stage is one 128-element K step for
-// E4M3 and two for E2M1; scale dwords are read once per 512 elements.
+// wave a 64 x 64 quarter as 4 x 4 instructions' 16 x 16 tiles, stepping
+// through K in stages of 128 bytes per operand row (one 128-element K step of
+// E4M3, two of E2M1) that are staged in LDS; its scale bytes come from the
+// 512-element records of the MFMA layout, staged beside them.
 constexpr int kTileM = 128, kTileN = 128;
-
-template <int FMT, int SB>
-struct TiledGemm {
-    static constexpr int kStageBytes = SB;                     // bytes of K per row per stage
-    static constexpr int kLdsRow = SB + 16;                    // padded LDS row
-    static constexpr int kStepBytes = FMT == 1 ? 128 : 64;      // bytes of one K step
-    static constexpr int kSteps = SB / kStepBytes;              // K steps per stage
-    static constexpr int kStageElems = kSteps * 128;
-    static constexpr int kStagesPer512 = kStageElems >= 512 ? 1 : 512 / kStageElems;
-    static constexpr int kPieces = SB / 32;                     // 16-byte pieces per thread
-};
-
-// 16 bytes of row `row` of an operand at byte `kb` of its codes, or zeros past
-// the rows or the row's bytes.
-__device__ __forceinline__ int4 load_piece(const uint8_t* codes, int64_t ldq, int64_t row,
-                                           int64_t rows, int kb, int row_bytes) {
-    if (row >= rows || kb >= row_bytes) return make_int4(0, 0, 0, 0);
-    return *reinterpret_cast<const int4*>(codes + row * ldq + kb);
-}
 
 // One 128 x 128 tile of c: operand rows and scale groups relative to the
 // tile's first row, valid-row counts, and the output window.
@@ -312,134 +292,10 @@ struct GemmTile {
     int K;
 };
 
-template <int FMT, int SB>
-__device__ __forceinline__ void gemm_tile(const GemmTile& d, uint8_t* lds_a, uint8_t* lds_b) {
-    using TG = TiledGemm<FMT, SB>;
-    constexpr int kFmt = FMT == 1 ? 0 : 4;
-    constexpr int kLdsRow = TG::kLdsRow;
-    static_assert(TG::kSteps * TG::kStagesPer512 <= 4 || TG::kStageElems == 512,
-                  "a stage spans at most one 512-element scale record");
-    const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int row_bytes = FMT == 1 ? d.K : d.K / 2;
-
-    // global -> LDS: thread t moves row t / 2, bytes [SB/2 (t % 2), +SB/2) of the stage
-    const int lrow = tid >> 1, lcol = (tid & 1) * (SB / 2);
-    int4 pa[TG::kPieces], pb[TG::kPieces];
-    auto fetch = [&](int kb0) {
-#pragma unroll
-        for (int i = 0; i < TG::kPieces; ++i) {
-            pa[i] = load_piece(d.a, d.lda_q, lrow, d.a_rows, kb0 + lcol + 16 * i, row_bytes);
-            pb[i] = load_piece(d.b, d.ldb_q, lrow, d.b_rows, kb0 + lcol + 16 * i, row_bytes);
-        }
-    };
-    auto stash = [&]() {
-#pragma unroll
-        for (int i = 0; i < TG::kPieces; ++i) {
-            *reinterpret_cast<int4*>(lds_a + lrow * kLdsRow + lcol + 16 * i) = pa[i];
-            *reinterpret_cast<int4*>(lds_b + lrow * kLdsRow + lcol + 16 * i) = pb[i];
-        }
-    };
-    // this lane's fragment of the 16-row subtile starting at LDS row r0, K step j of the stage
-    const int fr = lane & 15, fg = lane >> 4;
-    auto fragment = [&](const uint8_t* lds, int r0, int j) {
-        const uint8_t* row = lds + (r0 + fr) * kLdsRow + j * TG::kStepBytes;
-        mfma_v8i v;
-        if constexpr (FMT == 1) {
-            const int4 lo = *reinterpret_cast<const int4*>(row + 16 * fg);
-            const int4 hi = *reinterpret_cast<const int4*>(row + 64 + 16 * fg);
-            v = (mfma_v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        } else {
-            const int4 q = *reinterpret_cast<const int4*>(row + 16 * fg);
-            v = (mfma_v8i){q.x, q.y, q.z, q.w, 0, 0, 0, 0};
-        }
-        return v;
-    };
-    // scale dword of this lane for the 16-row group g of an operand, record k / 512
-    auto scale_dword = [&](const uint8_t* scales, int64_t lds_s, int64_t g, int64_t groups,
-                           int k512) -> uint32_t {
-        if (g >= groups) return 0x7F7F7F7Fu;   // rows past the operand: 2^0, zero codes
-        return *reinterpret_cast<const uint32_t*>(scales + g * lds_s + (int64_t)k512 * 256 +
-                                                  4 * lane);
-    };
-
-    mfma_v4f acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = (mfma_v4f){0.0f, 0.0f, 0.0f, 0.0f};
-
-    const int nstages = (d.K + TG::kStageElems - 1) / TG::kStageElems;
-    fetch(0);
-    int stage = 0;
-    for (int k512 = 0; k512 * 512 < d.K; ++k512) {
-        uint32_t sa[4], sb[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sa[i] = scale_dword(d.as, d.lda_s, 4 * wm + i, d.a_groups, k512);
-            sb[i] = scale_dword(d.bs, d.ldb_s, 4 * wn + i, d.b_groups, k512);
-        }
-#pragma unroll
-        for (int st = 0; st < TG::kStagesPer512; ++st, ++stage) {
-            if (stage >= nstages) break;
-            __syncthreads();                       // everyone is done reading the last stage
-            stash();
-            __syncthreads();
-            if (stage + 1 < nstages) fetch((stage + 1) * SB);
-#pragma unroll
-            for (int j = 0; j < TG::kSteps; ++j) {
-                if ((int64_t)stage * TG::kStageElems + j * 128 >= d.K) break;
-                const int t = st * TG::kSteps + j;  // K step within the 512: the opsel byte
-                mfma_v8i fb[4];
-#pragma unroll
-                for (int jn = 0; jn < 4; ++jn) fb[jn] = fragment(lds_b, 64 * wn + 16 * jn, j);
-#pragma unroll
-                for (int im = 0; im < 4; ++im) {
-                    const mfma_v8i fa = fragment(lds_a, 64 * wm + 16 * im, j);
-#pragma unroll
-                    for (int jn = 0; jn < 4; ++jn) {
-                        switch (t) {
-                            case 0: acc[im][jn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                        fa, fb[jn], acc[im][jn], kFmt, kFmt, 0, (int)sa[im], 0,
-                                        (int)sb[jn]); break;
-                            case 1: acc[im][jn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                        fa, fb[jn], acc[im][jn], kFmt, kFmt, 1, (int)sa[im], 1,
-                                        (int)sb[jn]); break;
-                            case 2: acc[im][jn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                        fa, fb[jn], acc[im][jn], kFmt, kFmt, 2, (int)sa[im], 2,
-                                        (int)sb[jn]); break;
-                            default: acc[im][jn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                        fa, fb[jn], acc[im][jn], kFmt, kFmt, 3, (int)sa[im], 3,
-                                        (int)sb[jn]); break;
-                        }
-                    }
-                }
-            }
-        }
-    }
-    // c: lane l holds rows 4 (l / 16) + e, column l % 16 of each 16 x 16 tile
-#pragma unroll
-    for (int im = 0; im < 4; ++im)
-#pragma unroll
-        for (int jn = 0; jn < 4; ++jn) {
-            const int64_t col = 64 * wn + 16 * jn + fr;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t row = 64 * wm + 16 * im + 4 * fg + e;
-                if (row < d.c_rows && col < d.c_cols) d.c[row * d.ldc + col] = acc[im][jn][e];
-            }
-        }
-}
-
-
-template <int FMT, int SB>
-__global__ void __launch_bounds__(kThreadsPerBlock) mfma_gemm_tiled_kernel(const GemmArgs a,
-                                                                             int64_t tiles_n) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[kTileM * TiledGemm<FMT, SB>::kLdsRow];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_b[kTileN * TiledGemm<FMT, SB>::kLdsRow];
+// Tile descriptors.  Dense: workgroup -> 128 x 128 tile, row-major.
+__device__ __forceinline__ void dense_desc(const GemmArgs& a, int64_t tiles_n, GemmTile& d) {
     const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * kTileM;
     const int64_t n0 = (int64_t)(blockIdx.x % tiles_n) * kTileN;
-    GemmTile d;
     d.a = a.a_codes + m0 * a.lda_q;
     d.lda_q = a.lda_q;
     d.a_rows = a.M - m0;
@@ -457,7 +313,6 @@ __global__ void __launch_bounds__(kThreadsPerBlock) mfma_gemm_tiled_kernel(const
     d.c_rows = a.M - m0;
     d.c_cols = a.N - n0;
     d.K = a.K;
-    gemm_tile<FMT, SB>(d, lds_a, lds_b);
 }
 
 // Grouped per-expert form: blockIdx.y is the 128-column tile of c, blockIdx.x
@@ -467,12 +322,9 @@ __global__ void __launch_bounds__(kThreadsPerBlock) mfma_gemm_tiled_kernel(const
 // scales_offsets[g] + r - row_offsets[g]) by the B of expert expert_ids[g]
 // ([N, K] codes from row e N, scales from row group e ceil(N / 16)).  A group
 // whose metadata falls outside the buffers, or whose scale offset is not a
-// multiple of 16 (the layout's row groups), is skipped.
-template <int FMT, int SB>
-__global__ void __launch_bounds__(kThreadsPerBlock)
-mfma_gemm_grouped_kernel(const GemmArgs a, const GroupedGemmArgs g) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[kTileM * TiledGemm<FMT, SB>::kLdsRow];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_b[kTileN * TiledGemm<FMT, SB>::kLdsRow];
+// multiple of 16 (the layout's row groups), is skipped: returns false.
+__device__ __forceinline__ bool grouped_desc(const GemmArgs& a, const GroupedGemmArgs& g,
+                                             GemmTile& d) {
     const int64_t n0 = (int64_t)blockIdx.y * kTileN;
     int64_t t = blockIdx.x;
     int grp = -1;
@@ -488,15 +340,14 @@ mfma_gemm_grouped_kernel(const GemmArgs a, const GroupedGemmArgs g) {
         }
         t -= tiles;
     }
-    if (grp < 0) return;                                     // past the last group's tiles
+    if (grp < 0) return false;                               // past the last group's tiles
     const int e = g.expert_ids[grp];
     const int64_t so = g.scales_offsets[grp];
     const int64_t r0 = lo + t * kTileM;
     if (hi > g.max_rows || e < 0 || e >= g.num_experts || so % 16 != 0 ||
         so + (hi - lo) > g.num_scale_rows)
-        return;
+        return false;
     const int64_t groups_n = (a.N + 15) / 16;
-    GemmTile d;
     d.a = a.a_codes + r0 * a.lda_q;
     d.lda_q = a.lda_q;
     d.a_rows = hi - r0;
@@ -514,17 +365,228 @@ mfma_gemm_grouped_kernel(const GemmArgs a, const GroupedGemmArgs g) {
     d.c_rows = hi - r0;
     d.c_cols = a.N - n0;
     d.K = a.K;
-    gemm_tile<FMT, SB>(d, lds_a, lds_b);
+    return true;
+}
+
+// Pipelined form of the tile: the stages of A and B go straight from global
+// memory to LDS (global_load_lds_dwordx4, 1 KiB per wave instruction), NBUF
+// stages deep, so NBUF - 1 stages of loads are in flight while one is being
+// multiplied, with no registers holding them.  A stage buffer holds the 128 A
+// rows and 128 B rows of 128 bytes each, unpadded; logical 16-byte piece c
+// of row R sits at piece c ^ (R % 8) (each lane chooses which global piece it
+// fetches for its LDS slot), so the 8 rows a fragment read serves at once
+// fall in distinct banks.  After the rows, the buffer holds the scale records
+// of the stage's 512 elements (8 A row groups, 8 B row groups, 256 bytes
+// each): every wave issues the same 9 loads per stage, so the wait for a
+// stage is a fixed count of the loads issued after it.
+constexpr int kDmaStageBytes = 2 * 128 * 128 + 16 * 256;   // rows of A and B, then scale records
+
+__device__ __forceinline__ void dma16(const void* g, uint8_t* lds) {
+    __builtin_amdgcn_global_load_lds(const_cast<void*>(g), lds, 16, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    // s_waitcnt with vmcnt <= N and the other counters unconstrained
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+template <int FMT, int NBUF>
+__device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const (&bufs)[NBUF]) {
+    constexpr int kFmt = FMT == 1 ? 0 : 4;
+    constexpr int kStepBytes = FMT == 1 ? 128 : 64;
+    constexpr int kSteps = 128 / kStepBytes;                 // K steps per stage
+    constexpr int kStageElems = kSteps * 128;
+    constexpr int kPerWave = 9;                              // load instructions per wave per stage
+    constexpr int kPerRecord = 4 / kSteps;                   // stages per 512-element scale record
+    // the stage loop is unrolled by a multiple of both the buffer count and the stages per
+    // record, so each unrolled stage's buffer and opsel byte are constants
+    constexpr int kUnroll = NBUF % kPerRecord == 0 ? NBUF
+                          : kPerRecord % NBUF == 0 ? kPerRecord : NBUF * kPerRecord;
+    const int tid = (int)threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
+    const int wm = wave >> 1, wn = wave & 1;
+    const int row_bytes = FMT == 1 ? d.K : d.K / 2;
+    const int nstages = (d.K + kStageElems - 1) / kStageElems;
+
+    // this lane's slot in a 1 KiB chunk: row 8 c + lane / 8, physical piece lane % 8
+    const int crow = lane >> 3, cpiece = lane & 7;
+    // stage s goes to buffer s % NBUF; the caller passes that index as a constant, so
+    // every LDS access names one buffer (distinct LDS objects keep the compiler's
+    // waits for the in-flight loads to the buffer actually read)
+    auto issue = [&](int s, uint8_t* buf) {
+        const int kb0 = s * 128;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int chunk = wave + 4 * i, row = 8 * chunk + crow;
+            const int piece = cpiece ^ (row & 7);
+            int kb = kb0 + 16 * piece;
+            kb = kb < row_bytes ? kb : 0;                     // past K: any in-row bytes, never used
+            const int64_t ra = row < d.a_rows ? row : d.a_rows - 1;
+            const int64_t rb = row < d.b_rows ? row : d.b_rows - 1;
+            dma16(d.a + ra * d.lda_q + kb, buf + chunk * 1024);
+            dma16(d.b + rb * d.ldb_q + kb, buf + 128 * 128 + chunk * 1024);
+        }
+        // scale records of the stage's 512 elements (A row groups 0..7, B row groups
+        // 0..7): wave w moves records 4 w .. 4 w + 3, lane L bytes 16 (L % 16) of
+        // record 4 w + L / 16
+        const int rec = 4 * wave + (lane >> 4);              // 0..15
+        const int k512 = (s * kStageElems) / 512;
+        const bool is_a = rec < 8;
+        const int g = rec & 7;
+        const int64_t groups = is_a ? d.a_groups : d.b_groups;
+        const int64_t gg = g < groups ? g : groups - 1;
+        const uint8_t* src = (is_a ? d.as + gg * d.lda_s : d.bs + gg * d.ldb_s) +
+                             (int64_t)k512 * 256 + 16 * (lane & 15);
+        dma16(src, buf + 2 * 128 * 128 + wave * 1024);
+    };
+
+    mfma_v4f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = (mfma_v4f){0.0f, 0.0f, 0.0f, 0.0f};
+
+#pragma unroll
+    for (int s = 0; s < NBUF - 1; ++s)
+        if (s < nstages) issue(s, bufs[s]);
+    const int fr = lane & 15, fg = lane >> 4;
+    for (int s0 = 0; s0 < nstages; s0 += kUnroll) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int s = s0 + u;
+        if (s >= nstages) break;
+        // this wave's loads of stage s are done once at most the later-issued stages'
+        // loads are outstanding; after the barrier every wave's are, and every wave has
+        // finished reading stage s - 1 (its MFMAs consumed those reads), so its buffer
+        // can be refilled.  No fence: the loads write LDS directly and the explicit
+        // count is the wait they need.
+        if (s + NBUF - 2 < nstages) wait_vm<kPerWave * (NBUF - 2)>();
+        else wait_vm<0>();
+        asm volatile("s_barrier" ::: "memory");
+        if (s + NBUF - 1 < nstages) issue(s + NBUF - 1, bufs[(u + NBUF - 1) % NBUF]);
+        const uint8_t* buf = bufs[u % NBUF];
+        // row groups past the operand's end hold the last group's record (their
+        // outputs are never stored), so every read is unconditional
+        constexpr int sc = 2 * 128 * 128;
+        uint32_t sa[4], sb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sa[i] = *reinterpret_cast<const uint32_t*>(buf + (sc + (4 * wm + i) * 256 + 4 * lane));
+            sb[i] = *reinterpret_cast<const uint32_t*>(buf + (sc + (8 + 4 * wn + i) * 256 + 4 * lane));
+        }
+        // every LDS address is the buffer plus one integer offset: a single step from
+        // the LDS object keeps the compiler's knowledge of which buffer is read
+        auto fragment = [&](int region, int r0, int j) {
+            const int r = r0 + fr;
+            const int row = region + r * 128;
+            mfma_v8i v;
+            if constexpr (FMT == 1) {
+                const int4 lo = *reinterpret_cast<const int4*>(buf + (row + 16 * (fg ^ (r & 7))));
+                const int4 hi =
+                    *reinterpret_cast<const int4*>(buf + (row + 16 * ((4 + fg) ^ (r & 7))));
+                v = (mfma_v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            } else {
+                const int4 q =
+                    *reinterpret_cast<const int4*>(buf + (row + 16 * ((4 * j + fg) ^ (r & 7))));
+                v = (mfma_v8i){q.x, q.y, q.z, q.w, 0, 0, 0, 0};
+            }
+            return v;
+        };
+#pragma unroll
+        for (int j = 0; j < kSteps; ++j) {
+            const int k = s * kStageElems + j * 128;
+            if (k >= d.K) break;
+            const int t = (u * kSteps + j) & 3;              // opsel byte: (k / 128) mod 4
+            mfma_v8i fb[4];
+#pragma unroll
+            for (int jn = 0; jn < 4; ++jn) fb[jn] = fragment(128 * 128, 64 * wn + 16 * jn, j);
+#pragma unroll
+            for (int im = 0; im < 4; ++im) {
+                const mfma_v8i fa = fragment(0, 64 * wm + 16 * im, j);
+#pragma unroll
+                for (int jn = 0; jn < 4; ++jn) {
+                    switch (t) {
+                        case 0: acc[im][jn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                    fa, fb[jn], acc[im][jn], kFmt, kFmt, 0, (int)sa[im], 0,
+                                    (int)sb[jn]); break;
+                        case 1: acc[im][jn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                    fa, fb[jn], acc[im][jn], kFmt, kFmt, 1, (int)sa[im], 1,
+                                    (int)sb[jn]); break;
+                        case 2: acc[im][jn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                    fa, fb[jn], acc[im][jn], kFmt, kFmt, 2, (int)sa[im], 2,
+                                    (int)sb[jn]); break;
+                        default: acc[im][jn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                    fa, fb[jn], acc[im][jn], kFmt, kFmt, 3, (int)sa[im], 3,
+                                    (int)sb[jn]); break;
+                    }
+                }
+            }
+        }
+    }
+    }
+#pragma unroll
+    for (int im = 0; im < 4; ++im)
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn) {
+            const int64_t col = 64 * wn + 16 * jn + fr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t row = 64 * wm + 16 * im + 4 * fg + e;
+                if (row < d.c_rows && col < d.c_cols) d.c[row * d.ldc + col] = acc[im][jn][e];
+            }
+        }
+}
+
+// The stage buffers are separate LDS objects: the compiler then knows which
+// buffer each LDS read and each direct load touches, and waits only for the
+// loads into the buffer being read.
+#define BSQ_STAGE_BUFFERS(NBUF)                                                            \
+    __shared__ __attribute__((aligned(16))) uint8_t stage0[kDmaStageBytes];                \
+    __shared__ __attribute__((aligned(16))) uint8_t stage1[kDmaStageBytes];                \
+    __shared__ __attribute__((aligned(16))) uint8_t stage2[(NBUF) >= 3 ? kDmaStageBytes : 16];
+
+template <int FMT, int NBUF>
+__device__ __forceinline__ void run_tile(const GemmTile& d, uint8_t* b0, uint8_t* b1,
+                                         uint8_t* b2) {
+    if constexpr (NBUF == 2) {
+        uint8_t* const bufs[2] = {b0, b1};
+        gemm_tile_dma<FMT, 2>(d, bufs);
+    } else {
+        uint8_t* const bufs[3] = {b0, b1, b2};
+        gemm_tile_dma<FMT, 3>(d, bufs);
+    }
+}
+
+template <int FMT, int NBUF>
+__global__ void __launch_bounds__(kThreadsPerBlock) mfma_gemm_tiled_kernel(const GemmArgs a,
+                                                                             int64_t tiles_n) {
+    BSQ_STAGE_BUFFERS(NBUF)
+    GemmTile d;
+    dense_desc(a, tiles_n, d);
+    run_tile<FMT, NBUF>(d, stage0, stage1, stage2);
+}
+
+template <int FMT, int NBUF>
+__global__ void __launch_bounds__(kThreadsPerBlock)
+mfma_gemm_grouped_kernel(const GemmArgs a, const GroupedGemmArgs g) {
+    BSQ_STAGE_BUFFERS(NBUF)
+    GemmTile d;
+    if (!grouped_desc(a, g, d)) return;
+    run_tile<FMT, NBUF>(d, stage0, stage1, stage2);
 }
 
 template <int FMT>
 hipError_t launch_mfma_tiled(const GemmArgs& a, hipStream_t stream) {
     const int64_t tiles_n = (a.N + kTileN - 1) / kTileN;
     const int64_t tiles = ((a.M + kTileM - 1) / kTileM) * tiles_n;
-    // 128-byte stages: 256-byte ones (2 x the work per barrier) measured twice as slow, their
-    // registers and LDS leaving one workgroup per CU to hide the loads' latency
-    hipLaunchKernelGGL((mfma_gemm_tiled_kernel<FMT, 128>), dim3((uint32_t)tiles),
-                       dim3(kThreadsPerBlock), 0, stream, a, tiles_n);
+    const dim3 grid((uint32_t)tiles), block(kThreadsPerBlock);
+    // two stage buffers (72 KiB, two workgroups per CU) by default; three (108 KiB)
+    // leave one workgroup per CU and measured slower
+    if (a.tiled == 3)
+        hipLaunchKernelGGL((mfma_gemm_tiled_kernel<FMT, 3>), grid, block, 0, stream, a, tiles_n);
+    else
+        hipLaunchKernelGGL((mfma_gemm_tiled_kernel<FMT, 2>), grid, block, 0, stream, a, tiles_n);
     return hipGetLastError();
 }
 
@@ -581,8 +643,11 @@ namespace {
 template <int FMT>
 hipError_t launch_mfma_grouped(const GemmArgs& a, const GroupedGemmArgs& g, hipStream_t stream) {
     const dim3 grid((uint32_t)g.m_tiles, (uint32_t)((a.N + kTileN - 1) / kTileN));
-    hipLaunchKernelGGL((mfma_gemm_grouped_kernel<FMT, 128>), grid, dim3(kThreadsPerBlock), 0,
-                       stream, a, g);
+    const dim3 block(kThreadsPerBlock);
+    if (a.tiled == 3)
+        hipLaunchKernelGGL((mfma_gemm_grouped_kernel<FMT, 3>), grid, block, 0, stream, a, g);
+    else
+        hipLaunchKernelGGL((mfma_gemm_grouped_kernel<FMT, 2>), grid, block, 0, stream, a, g);
     return hipGetLastError();
 }
 }  // namespace
