@@ -63,9 +63,10 @@ int tile_knob() {
     }();
     return v;
 }
-//   BSQ_MFMA_TILED           matrix-core GEMM: 128 x 128 tiles with two LDS stage buffers
-//                            (default); 2 one wave per 16 x 16 tile (dense); 3 three stage
-//                            buffers
+//   BSQ_MFMA_TILED           matrix-core GEMM: two LDS stage buffers, 256 x 256 tiles where
+//                            they fill the chip and 128 x 128 otherwise (default); 2 one wave
+//                            per 16 x 16 tile (dense); 3 128 x 128 tiles, three stage
+//                            buffers; 4 128 x 128 tiles (dense)
 int mfma_tiled_knob() {
     static const int v = env_knob("BSQ_MFMA_TILED");
     return v;
@@ -580,7 +581,7 @@ int block_scaled_matmul_mfma(int format, int block_size, int scale_layout,
     a.N = N;
     a.K = (int32_t)K;
     a.scale_layout = scale_layout;
-    a.tiled = mfma_tiled_knob() == 2 ? 0 : mfma_tiled_knob() == 3 ? 3 : 1;
+    a.tiled = mfma_tiled_knob() == 2 ? 0 : mfma_tiled_knob() == 3 ? 3 : mfma_tiled_knob() == 4 ? 4 : 1;
     const hipError_t e = bsq::launch_mfma_matmul(format, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

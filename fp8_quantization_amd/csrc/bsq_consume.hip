@@ -269,12 +269,28 @@ __global__ void __launch_bounds__(kThreadsPerBlock) mfma_matmul_kernel(const Gem
     }
 }
 
-// Tiled form: a workgroup of 4 waves computes a 128 x 128 tile of c, each
-// wave a 64 x 64 quarter as 4 x 4 instructions' 16 x 16 tiles, stepping
-// through K in stages of 128 bytes per operand row (one 128-element K step of
-// E4M3, two of E2M1) that are staged in LDS; its scale bytes come from the
-// 512-element records of the MFMA layout, staged beside them.
-constexpr int kTileM = 128, kTileN = 128;
+// Tiled form: a workgroup computes a TM x TN tile of c with a WAVES_M x
+// WAVES_N grid of waves, each wave a (16 IM) x (16 JN) block of instructions'
+// 16 x 16 tiles, stepping through K in stages of 128 bytes per operand row
+// (one 128-element K step of E4M3, two of E2M1) that are staged in LDS; its
+// scale bytes come from the 512-element records of the MFMA layout, staged
+// beside them.
+template <int TM_, int TN_, int WAVES_M_, int WAVES_N_>
+struct TileCfg {
+    static constexpr int TM = TM_, TN = TN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int NW = WAVES_M * WAVES_N;              // waves per workgroup
+    static constexpr int IM = TM / WAVES_M / 16, JN = TN / WAVES_N / 16;
+    static constexpr int kChunksA = TM / 8 / NW;               // 1 KiB row chunks per wave
+    static constexpr int kChunksB = TN / 8 / NW;
+    static constexpr int kPerWave = kChunksA + kChunksB + 1;   // direct loads per wave per stage
+    static constexpr int kRecords = (TM + TN) / 16;            // scale records per stage
+    static constexpr int kStageBytes = (TM + TN) * 128 + kRecords * 256;
+    // every wave moves the same rows and one 1 KiB run of records per stage
+    static_assert(TM % (8 * NW) == 0 && TN % (8 * NW) == 0 && kRecords == 4 * NW, "tile shape");
+};
+using Tile128 = TileCfg<128, 128, 2, 2>;   // 4 waves of 64 x 64
+using Tile256 = TileCfg<256, 256, 2, 4>;   // 8 waves of 128 x 64
+constexpr int kTileM = 128, kTileN = 128;  // grouped form
 
 // One 128 x 128 tile of c: operand rows and scale groups relative to the
 // tile's first row, valid-row counts, and the output window.
@@ -292,10 +308,11 @@ struct GemmTile {
     int K;
 };
 
-// Tile descriptors.  Dense: workgroup -> 128 x 128 tile, row-major.
+// Tile descriptors.  Dense: workgroup -> TM x TN tile, row-major.
+template <int TM, int TN>
 __device__ __forceinline__ void dense_desc(const GemmArgs& a, int64_t tiles_n, GemmTile& d) {
-    const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * kTileM;
-    const int64_t n0 = (int64_t)(blockIdx.x % tiles_n) * kTileN;
+    const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * TM;
+    const int64_t n0 = (int64_t)(blockIdx.x % tiles_n) * TN;
     d.a = a.a_codes + m0 * a.lda_q;
     d.lda_q = a.lda_q;
     d.a_rows = a.M - m0;
@@ -371,15 +388,14 @@ __device__ __forceinline__ bool grouped_desc(const GemmArgs& a, const GroupedGem
 // Pipelined form of the tile: the stages of A and B go straight from global
 // memory to LDS (global_load_lds_dwordx4, 1 KiB per wave instruction), NBUF
 // stages deep, so NBUF - 1 stages of loads are in flight while one is being
-// multiplied, with no registers holding them.  A stage buffer holds the 128 A
-// rows and 128 B rows of 128 bytes each, unpadded; logical 16-byte piece c
+// multiplied, with no registers holding them.  A stage buffer holds the TM A
+// rows and TN B rows of 128 bytes each, unpadded; logical 16-byte piece c
 // of row R sits at piece c ^ (R % 8) (each lane chooses which global piece it
 // fetches for its LDS slot), so the 8 rows a fragment read serves at once
 // fall in distinct banks.  After the rows, the buffer holds the scale records
-// of the stage's 512 elements (8 A row groups, 8 B row groups, 256 bytes
-// each): every wave issues the same 9 loads per stage, so the wait for a
-// stage is a fixed count of the loads issued after it.
-constexpr int kDmaStageBytes = 2 * 128 * 128 + 16 * 256;   // rows of A and B, then scale records
+// of the stage's 512 elements (TM / 16 A row groups, then TN / 16 B row
+// groups, 256 bytes each): every wave issues the same loads per stage, so the
+// wait for a stage is a fixed count of the loads issued after it.
 
 __device__ __forceinline__ void dma16(const void* g, uint8_t* lds) {
     __builtin_amdgcn_global_load_lds(const_cast<void*>(g), lds, 16, 0, 0);
@@ -391,13 +407,14 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-template <int FMT, int NBUF>
+template <int FMT, int NBUF, class Cfg>
 __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const (&bufs)[NBUF]) {
     constexpr int kFmt = FMT == 1 ? 0 : 4;
     constexpr int kStepBytes = FMT == 1 ? 128 : 64;
     constexpr int kSteps = 128 / kStepBytes;                 // K steps per stage
     constexpr int kStageElems = kSteps * 128;
-    constexpr int kPerWave = 9;                              // load instructions per wave per stage
+    constexpr int kPerWave = Cfg::kPerWave;
+    constexpr int TM = Cfg::TM, IM = Cfg::IM, JN = Cfg::JN;
     constexpr int kPerRecord = 4 / kSteps;                   // stages per 512-element scale record
     // the stage loop is unrolled by a multiple of both the buffer count and the stages per
     // record, so each unrolled stage's buffer and opsel byte are constants
@@ -405,7 +422,7 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const 
                           : kPerRecord % NBUF == 0 ? kPerRecord : NBUF * kPerRecord;
     const int tid = (int)threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
     const int row_bytes = FMT == 1 ? d.K : d.K / 2;
     const int nstages = (d.K + kStageElems - 1) / kStageElems;
 
@@ -415,37 +432,43 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const 
     // every LDS access names one buffer (distinct LDS objects keep the compiler's
     // waits for the in-flight loads to the buffer actually read)
     auto issue = [&](int s, uint8_t* buf) {
+        // row chunk c (rows 8 c .. 8 c + 7) of an operand goes to 1 KiB at c;
+        // rows past the operand load its last row, bytes past K any in-row
+        // bytes: their products are never stored
         const int kb0 = s * 128;
+        int kb = kb0 + 16 * (cpiece ^ crow);
+        kb = kb < row_bytes ? kb : 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int chunk = wave + 4 * i, row = 8 * chunk + crow;
-            const int piece = cpiece ^ (row & 7);
-            int kb = kb0 + 16 * piece;
-            kb = kb < row_bytes ? kb : 0;                     // past K: any in-row bytes, never used
+        for (int i = 0; i < Cfg::kChunksA; ++i) {
+            const int chunk = wave + Cfg::NW * i, row = 8 * chunk + crow;
             const int64_t ra = row < d.a_rows ? row : d.a_rows - 1;
-            const int64_t rb = row < d.b_rows ? row : d.b_rows - 1;
             dma16(d.a + ra * d.lda_q + kb, buf + chunk * 1024);
-            dma16(d.b + rb * d.ldb_q + kb, buf + 128 * 128 + chunk * 1024);
         }
-        // scale records of the stage's 512 elements (A row groups 0..7, B row groups
-        // 0..7): wave w moves records 4 w .. 4 w + 3, lane L bytes 16 (L % 16) of
+#pragma unroll
+        for (int i = 0; i < Cfg::kChunksB; ++i) {
+            const int chunk = wave + Cfg::NW * i, row = 8 * chunk + crow;
+            const int64_t rb = row < d.b_rows ? row : d.b_rows - 1;
+            dma16(d.b + rb * d.ldb_q + kb, buf + TM * 128 + chunk * 1024);
+        }
+        // scale records of the stage's 512 elements (A row groups, then B row
+        // groups): wave w moves records 4 w .. 4 w + 3, lane L bytes 16 (L % 16) of
         // record 4 w + L / 16
-        const int rec = 4 * wave + (lane >> 4);              // 0..15
+        const int rec = 4 * wave + (lane >> 4);
         const int k512 = (s * kStageElems) / 512;
-        const bool is_a = rec < 8;
-        const int g = rec & 7;
+        const bool is_a = rec < TM / 16;
+        const int g = is_a ? rec : rec - TM / 16;
         const int64_t groups = is_a ? d.a_groups : d.b_groups;
         const int64_t gg = g < groups ? g : groups - 1;
         const uint8_t* src = (is_a ? d.as + gg * d.lda_s : d.bs + gg * d.ldb_s) +
                              (int64_t)k512 * 256 + 16 * (lane & 15);
-        dma16(src, buf + 2 * 128 * 128 + wave * 1024);
+        dma16(src, buf + (TM + Cfg::TN) * 128 + wave * 1024);
     };
 
-    mfma_v4f acc[4][4];
+    mfma_v4f acc[IM][JN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < IM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = (mfma_v4f){0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < JN; ++j) acc[i][j] = (mfma_v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
 #pragma unroll
     for (int s = 0; s < NBUF - 1; ++s)
@@ -468,13 +491,15 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const 
         const uint8_t* buf = bufs[u % NBUF];
         // row groups past the operand's end hold the last group's record (their
         // outputs are never stored), so every read is unconditional
-        constexpr int sc = 2 * 128 * 128;
-        uint32_t sa[4], sb[4];
+        constexpr int sc = (TM + Cfg::TN) * 128;
+        uint32_t sa[IM], sb[JN];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sa[i] = *reinterpret_cast<const uint32_t*>(buf + (sc + (4 * wm + i) * 256 + 4 * lane));
-            sb[i] = *reinterpret_cast<const uint32_t*>(buf + (sc + (8 + 4 * wn + i) * 256 + 4 * lane));
-        }
+        for (int i = 0; i < IM; ++i)
+            sa[i] = *reinterpret_cast<const uint32_t*>(buf + (sc + (IM * wm + i) * 256 + 4 * lane));
+#pragma unroll
+        for (int i = 0; i < JN; ++i)
+            sb[i] = *reinterpret_cast<const uint32_t*>(
+                buf + (sc + (TM / 16 + JN * wn + i) * 256 + 4 * lane));
         // every LDS address is the buffer plus one integer offset: a single step from
         // the LDS object keeps the compiler's knowledge of which buffer is read
         auto fragment = [&](int region, int r0, int j) {
@@ -498,14 +523,14 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const 
             const int k = s * kStageElems + j * 128;
             if (k >= d.K) break;
             const int t = (u * kSteps + j) & 3;              // opsel byte: (k / 128) mod 4
-            mfma_v8i fb[4];
+            mfma_v8i fb[JN];
 #pragma unroll
-            for (int jn = 0; jn < 4; ++jn) fb[jn] = fragment(128 * 128, 64 * wn + 16 * jn, j);
+            for (int jn = 0; jn < JN; ++jn) fb[jn] = fragment(TM * 128, 16 * (JN * wn + jn), j);
 #pragma unroll
-            for (int im = 0; im < 4; ++im) {
-                const mfma_v8i fa = fragment(0, 64 * wm + 16 * im, j);
+            for (int im = 0; im < IM; ++im) {
+                const mfma_v8i fa = fragment(0, 16 * (IM * wm + im), j);
 #pragma unroll
-                for (int jn = 0; jn < 4; ++jn) {
+                for (int jn = 0; jn < JN; ++jn) {
                     switch (t) {
                         case 0: acc[im][jn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                                     fa, fb[jn], acc[im][jn], kFmt, kFmt, 0, (int)sa[im], 0,
@@ -526,13 +551,13 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const 
     }
     }
 #pragma unroll
-    for (int im = 0; im < 4; ++im)
+    for (int im = 0; im < IM; ++im)
 #pragma unroll
-        for (int jn = 0; jn < 4; ++jn) {
-            const int64_t col = 64 * wn + 16 * jn + fr;
+        for (int jn = 0; jn < JN; ++jn) {
+            const int64_t col = 16 * (JN * wn + jn) + fr;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int64_t row = 64 * wm + 16 * im + 4 * fg + e;
+                const int64_t row = 16 * (IM * wm + im) + 4 * fg + e;
                 if (row < d.c_rows && col < d.c_cols) d.c[row * d.ldc + col] = acc[im][jn][e];
             }
         }
@@ -541,53 +566,66 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const 
 // The stage buffers are separate LDS objects: the compiler then knows which
 // buffer each LDS read and each direct load touches, and waits only for the
 // loads into the buffer being read.
-#define BSQ_STAGE_BUFFERS(NBUF)                                                            \
-    __shared__ __attribute__((aligned(16))) uint8_t stage0[kDmaStageBytes];                \
-    __shared__ __attribute__((aligned(16))) uint8_t stage1[kDmaStageBytes];                \
-    __shared__ __attribute__((aligned(16))) uint8_t stage2[(NBUF) >= 3 ? kDmaStageBytes : 16];
+#define BSQ_STAGE_BUFFERS(NBUF, BYTES)                                                     \
+    __shared__ __attribute__((aligned(16))) uint8_t stage0[BYTES];                         \
+    __shared__ __attribute__((aligned(16))) uint8_t stage1[BYTES];                         \
+    __shared__ __attribute__((aligned(16))) uint8_t stage2[(NBUF) >= 3 ? (BYTES) : 16];
 
-template <int FMT, int NBUF>
+template <int FMT, int NBUF, class Cfg>
 __device__ __forceinline__ void run_tile(const GemmTile& d, uint8_t* b0, uint8_t* b1,
                                          uint8_t* b2) {
     if constexpr (NBUF == 2) {
         uint8_t* const bufs[2] = {b0, b1};
-        gemm_tile_dma<FMT, 2>(d, bufs);
+        gemm_tile_dma<FMT, 2, Cfg>(d, bufs);
     } else {
         uint8_t* const bufs[3] = {b0, b1, b2};
-        gemm_tile_dma<FMT, 3>(d, bufs);
+        gemm_tile_dma<FMT, 3, Cfg>(d, bufs);
     }
 }
 
-template <int FMT, int NBUF>
-__global__ void __launch_bounds__(kThreadsPerBlock) mfma_gemm_tiled_kernel(const GemmArgs a,
-                                                                             int64_t tiles_n) {
-    BSQ_STAGE_BUFFERS(NBUF)
+template <int FMT, int NBUF, class Cfg>
+__global__ void __launch_bounds__(64 * Cfg::NW) mfma_gemm_tiled_kernel(const GemmArgs a,
+                                                                        int64_t tiles_n) {
+    BSQ_STAGE_BUFFERS(NBUF, Cfg::kStageBytes)
     GemmTile d;
-    dense_desc(a, tiles_n, d);
-    run_tile<FMT, NBUF>(d, stage0, stage1, stage2);
+    dense_desc<Cfg::TM, Cfg::TN>(a, tiles_n, d);
+    run_tile<FMT, NBUF, Cfg>(d, stage0, stage1, stage2);
 }
 
 template <int FMT, int NBUF>
-__global__ void __launch_bounds__(kThreadsPerBlock)
+__global__ void __launch_bounds__(64 * Tile128::NW)
 mfma_gemm_grouped_kernel(const GemmArgs a, const GroupedGemmArgs g) {
-    BSQ_STAGE_BUFFERS(NBUF)
+    BSQ_STAGE_BUFFERS(NBUF, Tile128::kStageBytes)
     GemmTile d;
     if (!grouped_desc(a, g, d)) return;
-    run_tile<FMT, NBUF>(d, stage0, stage1, stage2);
+    run_tile<FMT, NBUF, Tile128>(d, stage0, stage1, stage2);
 }
 
+template <int FMT, class Cfg>
+hipError_t launch_tiles(const GemmArgs& a, hipStream_t stream) {
+    const int64_t tiles_n = (a.N + Cfg::TN - 1) / Cfg::TN;
+    const int64_t tiles = ((a.M + Cfg::TM - 1) / Cfg::TM) * tiles_n;
+    const dim3 grid((uint32_t)tiles), block(64 * Cfg::NW);
+    // two stage buffers; three (128 x 128 only) leave one workgroup per CU and
+    // measured slower
+    if constexpr (Cfg::kStageBytes * 3 <= 160 * 1024) {
+        if (a.tiled == 3) {
+            hipLaunchKernelGGL((mfma_gemm_tiled_kernel<FMT, 3, Cfg>), grid, block, 0, stream, a,
+                               tiles_n);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((mfma_gemm_tiled_kernel<FMT, 2, Cfg>), grid, block, 0, stream, a, tiles_n);
+    return hipGetLastError();
+}
+
+// 256 x 256 tiles (8 waves, 144 KiB of LDS in two stages, one workgroup per
+// CU) once they alone fill the chip; 128 x 128 ones otherwise, or on request
 template <int FMT>
 hipError_t launch_mfma_tiled(const GemmArgs& a, hipStream_t stream) {
-    const int64_t tiles_n = (a.N + kTileN - 1) / kTileN;
-    const int64_t tiles = ((a.M + kTileM - 1) / kTileM) * tiles_n;
-    const dim3 grid((uint32_t)tiles), block(kThreadsPerBlock);
-    // two stage buffers (72 KiB, two workgroups per CU) by default; three (108 KiB)
-    // leave one workgroup per CU and measured slower
-    if (a.tiled == 3)
-        hipLaunchKernelGGL((mfma_gemm_tiled_kernel<FMT, 3>), grid, block, 0, stream, a, tiles_n);
-    else
-        hipLaunchKernelGGL((mfma_gemm_tiled_kernel<FMT, 2>), grid, block, 0, stream, a, tiles_n);
-    return hipGetLastError();
+    const int64_t big = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+    if (a.tiled != 3 && a.tiled != 4 && big >= 256) return launch_tiles<FMT, Tile256>(a, stream);
+    return launch_tiles<FMT, Tile128>(a, stream);
 }
 
 template <int FMT>

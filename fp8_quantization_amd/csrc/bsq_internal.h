@@ -102,7 +102,8 @@ struct GemmArgs {
     int64_t M, N;
     int32_t K;
     int32_t scale_layout;   // as in KernelArgs
-    int32_t tiled;          // MFMA GEMM: 1 128 x 128 workgroup tiles, two LDS stage buffers (3: three); 0 one wave per 16 x 16
+    int32_t tiled;          // MFMA GEMM: 1 workgroup tiles sized to the problem, 3 128 x 128 with
+                            // three LDS stage buffers, 4 128 x 128; 0 one wave per 16 x 16
 };
 
 hipError_t launch_dequantize(int fmt, const DequantArgs& a, int64_t blocks, hipStream_t stream);

@@ -114,6 +114,41 @@ def test_nan_scale_and_nan_code(bsq, fmt):
     assert np.all(np.abs(got[ok] - want[ok]) <= REL_BOUND * S[ok])
 
 
+def random_operand(fmt, rows, K, rng):
+    """Random codes (E4M3 NaN codes replaced by 1.0) and row-major scale
+    bytes in [120, 134]: any bytes are valid operands for the GEMM."""
+    width = K if fmt == MXFP8 else K // 2
+    q = rng.integers(0, 256, (rows, width), dtype=np.uint8)
+    if fmt == MXFP8:
+        q[(q & 0x7F) == 0x7F] = 0x38
+    s = rng.integers(120, 135, (rows, K // 32), dtype=np.uint8)
+    return q, s
+
+
+@pytest.mark.parametrize("fmt", [MXFP4, MXFP8])
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 7168), (4000, 4100, 1536)])
+def test_full_size_sampled_outputs(bsq, fmt, M, N, K):
+    """At the measured GEMM's size (and a ragged one), where the library takes
+    its 256 x 256 tiles: sampled rows and columns, edges included, against the
+    oracle's exact GEMM of those rows and columns."""
+    rng = np.random.default_rng(M + N + K + fmt)
+    qa, sa = random_operand(fmt, M, K, rng)
+    qb, sb = random_operand(fmt, N, K, rng)
+    got = bsq.block_scaled_matmul_mfma(dev(qa), dev(oracle.scales_to_mfma16(sa)), dev(qb),
+                                       dev(oracle.scales_to_mfma16(sb)), fmt, K)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, M - 2, M - 1],
+                                     rng.integers(0, M, 24)]))
+    cols = np.unique(np.concatenate([[0, 15, 16, 255, 256, N - 17, N - 1],
+                                     rng.integers(0, N, 24)]))
+    got = got.cpu().numpy()[np.ix_(rows, cols)].astype(np.float64)
+    want = oracle.block_scaled_matmul(qa[rows], sa[rows], qb[cols], sb[cols], fmt, K)
+    S = magnitude_sum(qa[rows], sa[rows], qb[cols], sb[cols], fmt, K)
+    ratio = np.max(np.abs(got - want) / np.maximum(S, 1e-300))
+    print(f"format {fmt} {M}x{N}x{K} sampled: max |err| / sum|ab| = {ratio:.3e}")
+    assert ratio <= REL_BOUND
+
+
 def grouped_case(fmt, G, E, N, K, rows, seed, misaligned=None):
     """Routed activations quantized by the oracle's grouped quantizer (scales
     then mapped into the MFMA layout) and E experts' [N, K] weights (one
