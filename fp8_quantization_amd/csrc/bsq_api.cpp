@@ -560,8 +560,10 @@ int block_scaled_matmul_mfma(int format, int block_size, int scale_layout,
         if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || lda_q % 16 != 0 || ldb_q % 16 != 0)
             return fail(BSQ_ERR_INVALID_ARG,
                         "code rows must be 16-byte aligned (codes and ldq multiples of 16)");
-        if (!aligned(a_scales, 4) || !aligned(b_scales, 4))
-            return fail(BSQ_ERR_INVALID_ARG, "scales must be 4-byte aligned");
+        if (!aligned(a_scales, 16) || !aligned(b_scales, 16) || lda_s % 16 != 0 ||
+            ldb_s % 16 != 0)
+            return fail(BSQ_ERR_INVALID_ARG,
+                        "scale row groups must be 16-byte aligned (scales and lds multiples of 16)");
     }
     if (!c || !aligned(c, 4)) return fail(BSQ_ERR_INVALID_ARG, "c must be a 4-byte aligned device array");
     if (ldc < N) return fail(BSQ_ERR_INVALID_ARG, "ldc=%lld must be >= N=%lld", (long long)ldc,
@@ -626,8 +628,10 @@ int grouped_block_scaled_matmul_mfma(int format, int block_size, int scale_layou
         if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || lda_q % 16 != 0 || ldb_q % 16 != 0)
             return fail(BSQ_ERR_INVALID_ARG,
                         "code rows must be 16-byte aligned (codes and ldq multiples of 16)");
-        if (!aligned(a_scales, 4) || !aligned(b_scales, 4))
-            return fail(BSQ_ERR_INVALID_ARG, "scales must be 4-byte aligned");
+        if (!aligned(a_scales, 16) || !aligned(b_scales, 16) || lda_s % 16 != 0 ||
+            ldb_s % 16 != 0)
+            return fail(BSQ_ERR_INVALID_ARG,
+                        "scale row groups must be 16-byte aligned (scales and lds multiples of 16)");
     }
     if (!c || !aligned(c, 4)) return fail(BSQ_ERR_INVALID_ARG, "c must be a 4-byte aligned device array");
     if (ldc < N) return fail(BSQ_ERR_INVALID_ARG, "ldc=%lld must be >= N=%lld", (long long)ldc,

@@ -259,12 +259,14 @@ int block_scaled_matmul_naive(int format, int block_size, int scale_layout,
  * v_mfma_scale_f32_16x16x128_f8f6f4, reading two MX quantizer outputs as
  * they are -- codes row-major, scales in BSQ_SCALES_MFMA16 -- the CDNA4
  * counterpart of the block-scaled matmuls the "block_scaled_quantization"
- * module page lists.  One wave per 16 x 16 tile of c, no LDS staging: a
- * consumer of the layout, not a tuned GEMM.  The instruction's own
- * arithmetic sets the accuracy: FP4 products and their sums come out as
- * exact fp32 sums would; FP8 products are summed inside each 128-element
- * K step at reduced precision (measured error up to about 2^-12 of the
- * largest product of the step); steps are accumulated in fp32.
+ * module page lists.  Workgroups compute 256 x 256 tiles of c (128 x 128
+ * when the larger ones would not fill the chip), staging 128-byte K slices
+ * of both operands and their scale records in LDS through the direct
+ * global-to-LDS loads.  The instruction's own arithmetic sets the accuracy:
+ * FP4 products and their sums come out as exact fp32 sums would; FP8
+ * products are summed inside each 128-element K step at reduced precision
+ * (measured error up to about 2^-12 of the largest product of the step);
+ * steps are accumulated in fp32 in ascending K.
  *
  *   format, block_size   (BSQ_MXFP4, 32) or (BSQ_MXFP8, 32); NVFP4 ->
  *                        BSQ_ERR_UNSUPPORTED.
@@ -272,7 +274,9 @@ int block_scaled_matmul_naive(int format, int block_size, int scale_layout,
  *                        BSQ_ERR_UNSUPPORTED).
  *   a_codes, lda_q       operand A [M, K]: code rows 16-byte aligned (base
  *                        and lda_q multiples of 16); a_scales, lda_s its
- *                        scales in the MFMA layout, 4-byte aligned.
+ *                        scales in the MFMA layout, ceil(M / 16) row groups
+ *                        of lda_s bytes, 16-byte aligned (base and lda_s
+ *                        multiples of 16).
  *   b_codes, ...         operand B [N, K], likewise.
  *   M, N, K              K % 128 == 0; M * N <= 2^38.
  *   c, ldc               fp32 [M, ldc], 4-byte aligned, ldc >= N.
@@ -299,7 +303,8 @@ int block_scaled_matmul_mfma(int format, int block_size, int scale_layout,
  *
  *   format, block_size, scale_layout   as for block_scaled_matmul_mfma.
  *   a_codes, lda_q       [max_rows, K] codes (routed order), 16-byte aligned rows.
- *   a_scales, lda_s      MFMA-layout scales over num_scale_rows rows.
+ *   a_scales, lda_s      MFMA-layout scales over num_scale_rows rows, 16-byte
+ *                        aligned row groups.
  *   row_offsets, scales_offsets, expert_ids, num_groups   as for the grouped
  *                        quantizer; each scales_offsets[g] must be a multiple
  *                        of 16 (the layout's row groups) -- a group that is

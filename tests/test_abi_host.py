@@ -238,7 +238,8 @@ def test_mfma_matmul_validation(lib):
     assert mm(K=96) == INVALID                                  # K % 128
     assert mm(a=FAKE + 8) == INVALID                            # code rows 16-byte aligned
     assert mm(ldq=264) == INVALID                               # ldq % 16 (FP4: >= 256)
-    assert mm(sa=FAKE + 2) == INVALID                           # scales 4-byte aligned
+    assert mm(sa=FAKE + 4) == INVALID                           # scales 16-byte aligned
+    assert mm(lds=260) == INVALID                               # lds % 16
     assert mm(lds=128) == INVALID                               # one record per 512 of K
     assert mm(c=None) == INVALID
     assert mm(ldc=8) == INVALID
@@ -252,16 +253,18 @@ def test_grouped_mfma_matmul_validation(lib):
                   i64, p, i64, p]
 
     def gm(fmt=MXFP4, bs=32, layout=1, G=2, max_rows=64, nsr=64, E=2, N=32, K=512, ro=FAKE,
-           a=FAKE, c=FAKE, ldc=32):
+           a=FAKE, c=FAKE, ldc=32, sb=FAKE, ldb_s=256):
         ldq = K if fmt == MXFP8 else K // 2
         return f(fmt, bs, layout, a, ldq, FAKE, 256, ro, FAKE, FAKE, G, max_rows, nsr, FAKE, ldq,
-                 FAKE, 256, E, N, K, c, ldc, None)
+                 sb, ldb_s, E, N, K, c, ldc, None)
     assert gm(fmt=NVFP4, bs=16) == UNSUPPORTED
     assert gm(layout=0) == UNSUPPORTED
     assert gm(E=0) == INVALID
     assert gm(K=96) == INVALID
     assert gm(ro=None) == INVALID
     assert gm(a=FAKE + 8) == INVALID
+    assert gm(sb=FAKE + 4) == INVALID                           # scales 16-byte aligned
+    assert gm(ldb_s=260) == INVALID                             # lds % 16
     assert gm(c=None) == INVALID
     assert gm(ldc=16) == INVALID
     assert gm(max_rows=(1 << 32) + 1) == INVALID
