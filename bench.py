@@ -271,6 +271,23 @@ def time_steps(runner, steps, warmup):
     return wall, start.elapsed_time(end) / steps
 
 
+def launch_percentiles(runner, n, offset):
+    """Per-launch durations (µs) of n further launches, each bracketed by its
+    own HIP event pair on the launch stream, still rotating over the buffer
+    sets: median, p10 and p90."""
+    torch = runner.torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        runner.step(offset + i)
+        b.record()
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    return {"median": round(float(np.median(us)), 3), "p10": round(float(np.percentile(us, 10)), 3),
+            "p90": round(float(np.percentile(us, 90)), 3), "n": n}
+
+
 def measure(name, steps, warmup, rotate=True):
     import workloads as W
     producer = name in PRODUCERS
@@ -281,10 +298,11 @@ def measure(name, steps, warmup, rotate=True):
     nb = min(nb, 64)
     runner = Runner(case, nb, producer)
     wall, kern = time_steps(runner, steps, warmup)
+    runner.percentiles = launch_percentiles(runner, steps, warmup + steps)
     return case, runner, nbytes, elems, nb, wall, kern
 
 
-def summary(name, nbytes, elems, wall, launch_ms, steps, nb):
+def summary(name, nbytes, elems, wall, launch_ms, steps, nb, percentiles=None):
     k = launch_ms * 1e-3
     return {
         "workload": name,
@@ -292,6 +310,7 @@ def summary(name, nbytes, elems, wall, launch_ms, steps, nb):
         "elements": elems,
         "buffer_sets": nb,
         "launch_us_mean": round(k * 1e6, 3),
+        "launch_us_each": percentiles,
         "GBps": round(nbytes / k / 1e9, 1),
         "frac_of_8TBps": round(nbytes / k / 1e9 / PEAK_HBM_GBS, 4),
         "Gelem_per_s": round(elems / k / 1e9, 1),
@@ -329,11 +348,18 @@ def cpu_baseline(case, runner, target_cpu_seconds=12.0, max_wall_seconds=20.0):
     s0 = runner.sets[0]
     ok = bool(np.array_equal(s0["q"][:rows].cpu().numpy(), qh) and
               np.array_equal(s0["s"][:rows].cpu().numpy(), sh))
+    # the same oracle on one thread, over a smaller leading sample (about 3 s)
+    rows1 = int(min(M, max(1, 3.0 / max(per_row * threads, 1e-9))))
+    t = time.perf_counter()
+    oracle.quantize(case.x[:rows1], case.fmt, case.tensor_sf, nthreads=1)
+    dt1 = time.perf_counter() - t
     return {
         "value": round(nbytes / dt / 1e9, 3),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
+        "one_thread": {"value": round(rows1 * K * bytes_per_element(case.fmt) / dt1 / 1e9, 3),
+                       "sample": f"first {rows1} rows, {dt1:.2f} s wall on 1 thread"},
         "sample": f"first {rows} of {M} rows of the {case.name} input, {reps} pass(es) "
                   f"({reps * rows * K} elements, {nbytes / 1e6:.1f} MB algorithmic), "
                   f"{dt:.2f} s wall on {threads} thread(s)",
@@ -396,7 +422,7 @@ def main():
     import fp8_quantization_amd as bsq
 
     case, runner, nbytes, elems, nb, wall, kern = measure(args.workload, args.steps, args.warmup)
-    head = summary(args.workload, nbytes, elems, wall, kern, args.steps, nb)
+    head = summary(args.workload, nbytes, elems, wall, kern, args.steps, nb, runner.percentiles)
     log("[bench] headline", json.dumps(head))
     achieved = nbytes / (kern * 1e-3) / 1e9
     quantizer = args.workload not in PRODUCERS and not args.workload.startswith(
@@ -415,7 +441,7 @@ def main():
             if name == args.workload:
                 continue
             c2, r2, nb2, el2, nbs2, w2, k2 = measure(name, args.steps, args.warmup)
-            s = summary(name, nb2, el2, w2, k2, args.steps, nbs2)
+            s = summary(name, nb2, el2, w2, k2, args.steps, nbs2, r2.percentiles)
             if name.startswith(("mfma_gemm", "mfma_grouped_gemm")):
                 tf = gemm_flops(c2) / (k2 * 1e-3) / 1e12
                 peak = PEAK_MFMA_TFLOPS[c2.fmt]
@@ -460,7 +486,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "traffic_note": traffic_note,
-                     "launch_us_mean": head["launch_us_mean"]},
+                     "launch_us_mean": head["launch_us_mean"],
+                     "launch_us_each": head["launch_us_each"]},
         "cpu_baseline": cpu,
         "secondary": secondary,
     }
