@@ -334,8 +334,8 @@ __device__ __forceinline__ void dense_desc(const GemmArgs& a, int64_t tiles_n, G
 
 // Grouped per-expert form: blockIdx.y is the 128-column tile of c, blockIdx.x
 // a 128-row tile counted across the groups in order (group g has
-// ceil(m_g / 128) of them); each workgroup finds its group by scanning the
-// offsets.  Group g multiplies its routed rows (codes row r, scale row
+// ceil(m_g / 128) of them); each wave finds its group from the offsets.
+// Group g multiplies its routed rows (codes row r, scale row
 // scales_offsets[g] + r - row_offsets[g]) by the B of expert expert_ids[g]
 // ([N, K] codes from row e N, scales from row group e ceil(N / 16)).  A group
 // whose metadata falls outside the buffers, or whose scale offset is not a
@@ -346,16 +346,36 @@ __device__ __forceinline__ bool grouped_desc(const GemmArgs& a, const GroupedGem
     int64_t t = blockIdx.x;
     int grp = -1;
     int64_t lo = 0, hi = 0;
-    for (int h = 0; h < g.num_groups; ++h) {
-        const int64_t l = g.row_offsets[h], u = g.row_offsets[h + 1];
-        const int64_t tiles = u > l ? (u - l + kTileM - 1) / kTileM : 0;
-        if (t < tiles) {
-            grp = h;
-            lo = l;
-            hi = u;
+    // The wave reads 64 groups' offsets at a time and finds the group holding
+    // tile t from the prefix sum of their tile counts across the lanes (t and
+    // every sum are wave-uniform).  A group-by-group walk measured 29 us on its
+    // own for the 128-expert prefill routing.
+    const int lane = (int)(threadIdx.x & 63);
+    for (int h0 = 0; h0 < g.num_groups; h0 += 64) {
+        const int h = h0 + lane;
+        uint32_t l = 0, u = 0, tiles = 0;
+        if (h < g.num_groups) {
+            l = g.row_offsets[h];
+            u = g.row_offsets[h + 1];
+            tiles = u > l ? (uint32_t)(((uint64_t)u - l + kTileM - 1) / kTileM) : 0u;
+        }
+        uint32_t incl = tiles;                               // at most 2^25 + 64 in total
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t v = (uint32_t)__shfl_up((int)incl, off);
+            if (lane >= off) incl += v;
+        }
+        const uint32_t total = (uint32_t)__shfl((int)incl, 63);
+        if (t < (int64_t)total) {
+            // the first lane past t has tiles > 0, so it is a real group
+            const int L = __ffsll(__ballot((int64_t)incl > t)) - 1;
+            grp = h0 + L;
+            lo = (uint32_t)__shfl((int)l, L);
+            hi = (uint32_t)__shfl((int)u, L);
+            t -= (uint32_t)__shfl((int)(incl - tiles), L);
             break;
         }
-        t -= tiles;
+        t -= total;
     }
     if (grp < 0) return false;                               // past the last group's tiles
     const int e = g.expert_ids[grp];

@@ -179,7 +179,8 @@ def grouped_case(fmt, G, E, N, K, rows, seed, misaligned=None):
 
 @pytest.mark.parametrize("fmt", [MXFP4, MXFP8])
 @pytest.mark.parametrize("G,E,N,K,rows", [(1, 1, 128, 256, 128), (5, 3, 100, 512, 300),
-                                          (40, 16, 160, 1024, 900), (9, 4, 256, 7168, 700)])
+                                          (40, 16, 160, 1024, 900), (9, 4, 256, 7168, 700),
+                                          (130, 20, 96, 512, 3000), (200, 7, 48, 256, 9000)])
 def test_grouped_mfma_matches_oracle(bsq, fmt, G, E, N, K, rows):
     d = grouped_case(fmt, G, E, N, K, rows, seed=G + N + K + fmt)
     out = torch.full((d["max_rows"], N), 7.0, dtype=torch.float32, device="cuda")
