@@ -282,11 +282,13 @@ struct TileCfg {
     static constexpr int IM = TM / WAVES_M / 16, JN = TN / WAVES_N / 16;
     static constexpr int kChunksA = TM / 8 / NW;               // 1 KiB row chunks per wave
     static constexpr int kChunksB = TN / 8 / NW;
-    static constexpr int kPerWave = kChunksA + kChunksB + 1;   // direct loads per wave per stage
     static constexpr int kRecords = (TM + TN) / 16;            // scale records per stage
+    static constexpr int kRecordLoads = kRecords / (4 * NW);   // 1 KiB runs of records per wave
+    static constexpr int kPerWave = kChunksA + kChunksB + kRecordLoads;  // direct loads per stage
     static constexpr int kStageBytes = (TM + TN) * 128 + kRecords * 256;
-    // every wave moves the same rows and one 1 KiB run of records per stage
-    static_assert(TM % (8 * NW) == 0 && TN % (8 * NW) == 0 && kRecords == 4 * NW, "tile shape");
+    // every wave moves the same number of rows and of 1 KiB runs of records
+    static_assert(TM % (8 * NW) == 0 && TN % (8 * NW) == 0 && kRecords % (4 * NW) == 0,
+                  "tile shape");
 };
 using Tile128 = TileCfg<128, 128, 2, 2>;   // 4 waves of 64 x 64
 using Tile256 = TileCfg<256, 256, 2, 4>;   // 8 waves of 128 x 64
@@ -471,17 +473,21 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const 
             dma16(d.b + rb * d.ldb_q + kb, buf + TM * 128 + chunk * 1024);
         }
         // scale records of the stage's 512 elements (A row groups, then B row
-        // groups): wave w moves records 4 w .. 4 w + 3, lane L bytes 16 (L % 16) of
-        // record 4 w + L / 16
-        const int rec = 4 * wave + (lane >> 4);
+        // groups): run j = wave + NW i holds records 4 j .. 4 j + 3, lane L moving
+        // bytes 16 (L % 16) of record 4 j + L / 16
         const int k512 = (s * kStageElems) / 512;
-        const bool is_a = rec < TM / 16;
-        const int g = is_a ? rec : rec - TM / 16;
-        const int64_t groups = is_a ? d.a_groups : d.b_groups;
-        const int64_t gg = g < groups ? g : groups - 1;
-        const uint8_t* src = (is_a ? d.as + gg * d.lda_s : d.bs + gg * d.ldb_s) +
-                             (int64_t)k512 * 256 + 16 * (lane & 15);
-        dma16(src, buf + (TM + Cfg::TN) * 128 + wave * 1024);
+#pragma unroll
+        for (int i = 0; i < Cfg::kRecordLoads; ++i) {
+            const int run = wave + Cfg::NW * i;
+            const int rec = 4 * run + (lane >> 4);
+            const bool is_a = rec < TM / 16;
+            const int g = is_a ? rec : rec - TM / 16;
+            const int64_t groups = is_a ? d.a_groups : d.b_groups;
+            const int64_t gg = g < groups ? g : groups - 1;
+            const uint8_t* src = (is_a ? d.as + gg * d.lda_s : d.bs + gg * d.ldb_s) +
+                                 (int64_t)k512 * 256 + 16 * (lane & 15);
+            dma16(src, buf + (TM + Cfg::TN) * 128 + run * 1024);
+        }
     };
 
     mfma_v4f acc[IM][JN];
