@@ -193,10 +193,11 @@ __global__ void __launch_bounds__(kThreadsPerBlock) naive_matmul_kernel(const Ge
 //
 // c = A B^T with gfx950's scaled matrix instruction
 // v_mfma_scale_f32_16x16x128_f8f6f4, reading the quantizers' MX output as
-// is: codes row-major, scales in the MFMA layout.  One wave per 16 x 16 tile
-// of c; per 128-element K step each lane loads its operand fragments
-// straight from the code rows, and per 512 elements one scale dword per lane
-// per operand, whose byte t feeds step t (opsel = t).
+// is: codes row-major, scales in the MFMA layout.  Per 512 elements of K each
+// lane takes one scale dword per operand, whose byte t feeds K step t
+// (opsel = t).  Two forms: the simple one below (one wave per 16 x 16 tile
+// of c, fragments loaded straight from the code rows; kept behind a knob)
+// and the LDS-tiled one after it, which the library uses.
 //
 // Operand fragments (measured with one-wave probes of known operands):
 // lane l serves row l % 16 of its operand and group g = l / 16;
@@ -292,9 +293,9 @@ struct TileCfg {
 };
 using Tile128 = TileCfg<128, 128, 2, 2>;   // 4 waves of 64 x 64
 using Tile256 = TileCfg<256, 256, 2, 4>;   // 8 waves of 128 x 64
-constexpr int kTileM = 128, kTileN = 128;  // grouped form
+constexpr int kTileM = Tile128::TM, kTileN = Tile128::TN;  // grouped form
 
-// One 128 x 128 tile of c: operand rows and scale groups relative to the
+// One workgroup tile of c: operand rows and scale groups relative to the
 // tile's first row, valid-row counts, and the output window.
 struct GemmTile {
     const uint8_t* a;          // A codes, first row of the tile
@@ -707,7 +708,7 @@ namespace {
 template <int FMT>
 hipError_t launch_mfma_grouped(const GemmArgs& a, const GroupedGemmArgs& g, hipStream_t stream) {
     const dim3 grid((uint32_t)g.m_tiles, (uint32_t)((a.N + kTileN - 1) / kTileN));
-    const dim3 block(kThreadsPerBlock);
+    const dim3 block(64 * Tile128::NW);
     if (a.tiled == 3)
         hipLaunchKernelGGL((mfma_gemm_grouped_kernel<FMT, 3>), grid, block, 0, stream, a, g);
     else

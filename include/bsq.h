@@ -328,8 +328,10 @@ int grouped_block_scaled_matmul_mfma(int format, int block_size, int scale_layou
                                      int64_t ldb_s, int64_t num_experts,
                                      int64_t N, int64_t K, float* c, int64_t ldc, void* stream);
 
-/* Message for the last non-OK status returned on the calling thread ("" if
-   none).  The pointer stays valid until the next call on that thread. */
+/* Message of the calling thread's most recent call into this library when
+   that call returned a non-OK status ("" after a call that returned
+   BSQ_OK, or before any call).  The pointer stays valid until the next
+   call on that thread. */
 const char* bsq_last_error(void);
 
 /* Library version, e.g. "1.0.0". */

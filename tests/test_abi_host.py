@@ -87,6 +87,13 @@ def test_unsupported_pairs(lib, fmt, bs):
     assert lib.bsq_last_error()
 
 
+def test_last_error_is_cleared_by_a_successful_call(lib):
+    assert dense(lib, K=48) == INVALID                          # K % 32
+    assert b"K=48" in lib.bsq_last_error()
+    assert dense(lib, M=0, x=None, codes=None, scales=None) == OK   # no-op, returns BSQ_OK
+    assert lib.bsq_last_error() == b""
+
+
 def test_unsupported_layout(lib):
     assert dense(lib, layout=2) == UNSUPPORTED
     assert b"layout" in lib.bsq_last_error()
