@@ -6,12 +6,18 @@ kernels of ``libbsq.so``; torch provides device memory (``torch.empty``),
 pointers (``data_ptr``) and the current stream.  There is no CPU fallback:
 if the library is not built, importing this package raises ``ImportError``.
 
-The two entry points carry the names of the C ABI (``include/bsq.h``), the
-MI355X counterparts of the launchers on the Modular
-"block_scaled_quantization" module page; the grouped arguments follow the
+The functions carry the names of the C ABI's entry points (``include/bsq.h``);
+the quantizers are the MI355X counterparts of the launchers on the Modular
+"block_scaled_quantization" module page, and the grouped arguments follow the
 "grouped_quantize_dynamic_scaled_fp4_async_kernel" page (uint32 row_offsets
 and scales_offsets, int32 expert_ids, fp32 per-expert scale, optional int32
 row_indices).
+
+The C ABI receives pointers and strides only, so the sizes of the tensors
+behind them are checked here: every tensor a call reads or writes must hold
+the window the kernels touch, or the call raises before anything runs
+(``BsqError`` with BSQ_ERR_INVALID_ARG for a size, ``TypeError`` for a dtype,
+device or layout).
 """
 import ctypes
 import os
@@ -117,13 +123,37 @@ def _ld(t: torch.Tensor) -> int:
     return t.stride(0) if t.dim() == 2 and t.shape[0] > 1 else t.shape[-1]
 
 
+def _need(name, t, dtype, rows, cols):
+    """A 2-D GPU tensor of ``dtype`` with unit column stride holding at least
+    rows x cols (the window the kernels read or write)."""
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or t.dim() != 2 or not t.is_cuda \
+            or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise TypeError(f"{name} must be a 2-D row-major {dtype} GPU tensor")
+    if t.shape[0] < rows or t.shape[1] < cols:
+        raise BsqError(1, f"{name} is {tuple(t.shape)}; it must be at least [{rows}, {cols}]")
+    return t
+
+
+def _need_vec(name, t, dtypes, n):
+    """A contiguous 1-D GPU tensor of one of ``dtypes`` with at least n entries."""
+    if not isinstance(t, torch.Tensor) or t.dtype not in dtypes or not t.is_cuda or \
+            not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous GPU tensor of dtype {dtypes}")
+    if t.numel() < n:
+        raise BsqError(1, f"{name} has {t.numel()} entries; it needs at least {n}")
+    return t
+
+
+_OFFSETS = (torch.uint32, torch.int32)
+
+
 def _as_bf16_matrix(x: torch.Tensor) -> torch.Tensor:
     if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
         raise TypeError(f"x must hold BF16 values (bfloat16/int16/uint16), got {x.dtype}")
     if x.dim() != 2 or x.stride(1) != 1:
-        raise ValueError("x must be a 2-D row-major tensor with unit column stride")
+        raise TypeError("x must be a 2-D row-major tensor with unit column stride")
     if not x.is_cuda:
-        raise ValueError("x must be a GPU tensor")
+        raise TypeError("x must be a GPU tensor")
     return x
 
 
@@ -143,6 +173,9 @@ def quantize_block_scaled(x: torch.Tensor, fmt, tensor_sf: float = 1.0, codes=No
     if scales is None:
         scales = torch.empty(scale_shape(f, M, K, scale_layout) if bs else (M, 0),
                              dtype=torch.uint8, device=x.device)
+    if bs:
+        _need("codes", codes, torch.uint8, M, code_width(f, K))
+        _need("scales", scales, torch.uint8, *scale_shape(f, M, K, scale_layout))
     _check(_lib.quantize_block_scaled(f, bs, scale_layout, _ptr(x), M, K, _ld(x), _ptr(codes),
                                       _ld(codes), _ptr(scales), _ld(scales),
                                       float(tensor_sf), _stream_ptr(stream, x.device)))
@@ -165,29 +198,26 @@ def grouped_quantize_block_scaled(x: torch.Tensor, fmt, row_offsets: torch.Tenso
     x = _as_bf16_matrix(x)
     S, K = x.shape
     bs = BLOCK_SIZE.get(f, 0)
-    for name, t, dt in (("row_offsets", row_offsets, (torch.uint32, torch.int32)),
-                        ("scales_offsets", scales_offsets, (torch.uint32, torch.int32)),
-                        ("expert_ids", expert_ids, (torch.int32,))):
-        if t.dtype not in dt or not t.is_cuda or not t.is_contiguous():
-            raise TypeError(f"{name} must be a contiguous GPU tensor of dtype {dt}")
+    _need_vec("expert_ids", expert_ids, (torch.int32,), 0)
     G = expert_ids.shape[0]
-    if row_offsets.shape[0] != G + 1 or scales_offsets.shape[0] != G + 1:
-        raise ValueError("row_offsets and scales_offsets must have num_groups + 1 entries")
+    for name, t in (("row_offsets", row_offsets), ("scales_offsets", scales_offsets)):
+        _need_vec(name, t, _OFFSETS, G + 1)
+        if t.shape[0] != G + 1:
+            raise ValueError("row_offsets and scales_offsets must have num_groups + 1 entries")
     E = 0
     if tensor_sf is not None:
-        if tensor_sf.dtype != torch.float32 or not tensor_sf.is_cuda or not tensor_sf.is_contiguous():
-            raise TypeError("tensor_sf must be a contiguous float32 GPU tensor")
-        E = tensor_sf.shape[0]
+        E = _need_vec("tensor_sf", tensor_sf, (torch.float32,), 0).shape[0]
     if row_indices is not None:
-        if row_indices.dtype != torch.int32 or not row_indices.is_cuda or \
-                not row_indices.is_contiguous() or row_indices.shape[0] < max_rows:
-            raise TypeError("row_indices must be a contiguous int32 GPU tensor of >= max_rows")
+        _need_vec("row_indices", row_indices, (torch.int32,), max_rows)
     if codes is None:
         codes = torch.empty((max_rows, code_width(f, K) if bs else 0), dtype=torch.uint8,
                             device=x.device)
     if scales is None:
         scales = torch.empty(scale_shape(f, num_scale_rows, K, scale_layout) if bs else
                              (num_scale_rows, 0), dtype=torch.uint8, device=x.device)
+    if bs:
+        _need("codes", codes, torch.uint8, max_rows, code_width(f, K))
+        _need("scales", scales, torch.uint8, *scale_shape(f, num_scale_rows, K, scale_layout))
     _check(_lib.grouped_quantize_block_scaled(
         f, bs, scale_layout, _ptr(x), S, K, _ld(x), _ptr(row_indices), _ptr(row_offsets),
         _ptr(scales_offsets), _ptr(expert_ids), _ptr(tensor_sf), G, E, max_rows, num_scale_rows,
@@ -203,6 +233,7 @@ def tensor_scale_nvfp4(x: torch.Tensor, out: torch.Tensor | None = None, stream=
     M, K = x.shape
     if out is None:
         out = torch.empty(1, dtype=torch.float32, device=x.device)
+    _need_vec("out", out, (torch.float32,), 1)
     _check(_lib.tensor_scale_nvfp4(_ptr(x), M, K, _ld(x), _ptr(out),
                                    _stream_ptr(stream, x.device)))
     return out
@@ -217,14 +248,14 @@ def grouped_tensor_scale_nvfp4(x: torch.Tensor, row_offsets: torch.Tensor,
     passed as ``tensor_sf`` to ``grouped_quantize_block_scaled``."""
     x = _as_bf16_matrix(x)
     S, K = x.shape
-    G = expert_ids.shape[0]
-    if row_offsets.shape[0] != G + 1:
+    G = _need_vec("expert_ids", expert_ids, (torch.int32,), 0).shape[0]
+    if _need_vec("row_offsets", row_offsets, _OFFSETS, G + 1).shape[0] != G + 1:
         raise ValueError("row_offsets must have num_groups + 1 entries")
-    if row_indices is not None and (row_indices.dtype != torch.int32 or
-                                    row_indices.shape[0] < max_rows):
-        raise TypeError("row_indices must be an int32 GPU tensor of >= max_rows")
+    if row_indices is not None:
+        _need_vec("row_indices", row_indices, (torch.int32,), max_rows)
     if out is None:
         out = torch.empty(num_experts, dtype=torch.float32, device=x.device)
+    _need_vec("out", out, (torch.float32,), num_experts)
     _check(_lib.grouped_tensor_scale_nvfp4(
         _ptr(x), S, K, _ld(x), _ptr(row_indices), _ptr(row_offsets), _ptr(expert_ids), G,
         num_experts, max_rows, _ptr(out), _stream_ptr(stream, x.device)))
@@ -245,14 +276,26 @@ def dequantize_block_scaled(codes: torch.Tensor, scales: torch.Tensor, fmt, K: i
     f = _fmt(fmt)
     codes, scales = _as_code_matrix("codes", codes), _as_code_matrix("scales", scales)
     M = codes.shape[0]
-    if scales.shape[0] != scale_shape(f, M, K, scale_layout)[0]:
-        raise ValueError("scales has the wrong number of rows (row groups) for codes")
+    if f in BLOCK_SIZE:
+        _need("codes", codes, torch.uint8, M, code_width(f, K))
+        _need("scales", scales, torch.uint8, *scale_shape(f, M, K, scale_layout))
     if out is None:
         out = torch.empty((M, K), dtype=torch.float32, device=codes.device)
+    _need("out", out, torch.float32, M, K)
     _check(_lib.dequantize_block_scaled(f, BLOCK_SIZE.get(f, 0), scale_layout, _ptr(codes), M,
                                         K, _ld(codes), _ptr(scales), _ld(scales), float(tensor_sf),
                                         _ptr(out), _ld(out), _stream_ptr(stream, codes.device)))
     return out
+
+
+def _check_operands(f, K, scale_layout, *operands):
+    """Each GEMM operand (codes, scales, rows, name prefix) holds rows x K codes
+    and the scales of those rows in ``scale_layout``."""
+    if f not in BLOCK_SIZE:
+        return
+    for codes, scales, rows, pre in operands:
+        _need(pre + "codes", codes, torch.uint8, rows, code_width(f, K))
+        _need(pre + "scales", scales, torch.uint8, *scale_shape(f, rows, K, scale_layout))
 
 
 def block_scaled_matmul_naive(a_codes, a_scales, b_codes, b_scales, fmt, K: int,
@@ -265,8 +308,10 @@ def block_scaled_matmul_naive(a_codes, a_scales, b_codes, b_scales, fmt, K: int,
     a_codes, a_scales = _as_code_matrix("a_codes", a_codes), _as_code_matrix("a_scales", a_scales)
     b_codes, b_scales = _as_code_matrix("b_codes", b_codes), _as_code_matrix("b_scales", b_scales)
     M, N = a_codes.shape[0], b_codes.shape[0]
+    _check_operands(f, K, scale_layout, (a_codes, a_scales, M, "a_"), (b_codes, b_scales, N, "b_"))
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
+    _need("out", out, torch.float32, M, N)
     _check(_lib.block_scaled_matmul_naive(
         f, BLOCK_SIZE.get(f, 0), scale_layout, _ptr(a_codes), _ld(a_codes), _ptr(a_scales),
         _ld(a_scales), float(a_tsf), _ptr(b_codes), _ld(b_codes), _ptr(b_scales), _ld(b_scales),
@@ -283,8 +328,11 @@ def block_scaled_matmul_mfma(a_codes, a_scales, b_codes, b_scales, fmt, K: int, 
     a_codes, a_scales = _as_code_matrix("a_codes", a_codes), _as_code_matrix("a_scales", a_scales)
     b_codes, b_scales = _as_code_matrix("b_codes", b_codes), _as_code_matrix("b_scales", b_scales)
     M, N = a_codes.shape[0], b_codes.shape[0]
+    _check_operands(f, K, SCALES_MFMA16, (a_codes, a_scales, M, "a_"),
+                    (b_codes, b_scales, N, "b_"))
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
+    _need("out", out, torch.float32, M, N)
     _check(_lib.block_scaled_matmul_mfma(
         f, BLOCK_SIZE.get(f, 0), SCALES_MFMA16, _ptr(a_codes), _ld(a_codes), _ptr(a_scales),
         _ld(a_scales), _ptr(b_codes), _ld(b_codes), _ptr(b_scales), _ld(b_scales), M, N, K,
@@ -304,12 +352,22 @@ def grouped_block_scaled_matmul_mfma(a_codes, a_scales, row_offsets, scales_offs
     f = _fmt(fmt)
     a_codes, a_scales = _as_code_matrix("a_codes", a_codes), _as_code_matrix("a_scales", a_scales)
     b_codes, b_scales = _as_code_matrix("b_codes", b_codes), _as_code_matrix("b_scales", b_scales)
-    if b_codes.shape[0] % num_experts:
-        raise ValueError("b_codes must hold num_experts * N rows")
+    if num_experts < 1 or b_codes.shape[0] % num_experts:
+        raise BsqError(1, "b_codes must hold num_experts * N rows, num_experts >= 1")
     N = b_codes.shape[0] // num_experts
-    G = expert_ids.shape[0]
+    G = _need_vec("expert_ids", expert_ids, (torch.int32,), 0).shape[0]
+    for name, t in (("row_offsets", row_offsets), ("scales_offsets", scales_offsets)):
+        if _need_vec(name, t, _OFFSETS, G + 1).shape[0] != G + 1:
+            raise ValueError("row_offsets and scales_offsets must have num_groups + 1 entries")
+    if f in BLOCK_SIZE:
+        _need("a_codes", a_codes, torch.uint8, max_rows, code_width(f, K))
+        _need("a_scales", a_scales, torch.uint8, *scale_shape(f, num_scale_rows, K, SCALES_MFMA16))
+        groups_b, width_b = scale_shape(f, N, K, SCALES_MFMA16)
+        _need("b_scales", b_scales, torch.uint8, num_experts * groups_b, width_b)
+        _need("b_codes", b_codes, torch.uint8, num_experts * N, code_width(f, K))
     if out is None:
         out = torch.empty((max_rows, N), dtype=torch.float32, device=a_codes.device)
+    _need("out", out, torch.float32, max_rows, N)
     _check(_lib.grouped_block_scaled_matmul_mfma(
         f, BLOCK_SIZE.get(f, 0), SCALES_MFMA16, _ptr(a_codes), _ld(a_codes), _ptr(a_scales),
         _ld(a_scales), _ptr(row_offsets), _ptr(scales_offsets), _ptr(expert_ids), G, max_rows,
