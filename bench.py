@@ -383,6 +383,33 @@ def traffic_from_counters(nbytes_per_launch):
 
 # ------------------------------------------------------------------ main
 
+def vendor_cast_context(runner, steps, warmup):
+    """Context for the headline: torch's own elementwise cast of the same BF16
+    buffers to float8_e4m3fn (2 bytes read and 1 written per element, the
+    MXFP8 byte mix without the scales), rotated and timed like the quantizer.
+    A vendor streaming kernel of this mix shows what such a stream reaches on
+    this chip; it computes no block scales."""
+    torch = runner.torch
+    if not hasattr(torch, "float8_e4m3fn"):
+        return None
+    xs = [st["x"].view(torch.bfloat16) for st in runner.sets]
+    outs = [torch.empty(x.shape, dtype=torch.float8_e4m3fn, device="cuda") for x in xs]
+    for i in range(warmup):
+        outs[i % len(xs)].copy_(xs[i % len(xs)])
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        outs[i % len(xs)].copy_(xs[i % len(xs)])
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / steps * 1e3
+    nbytes = xs[0].numel() * 3
+    return {"kernel": "torch bf16 -> float8_e4m3fn cast (same inputs, same rotation)",
+            "bytes_per_launch": nbytes, "launch_us_mean": round(us, 3),
+            "GBps": round(nbytes / us / 1e3, 1)}
+
+
 def copy_calibration(nbytes, steps):
     import torch
     n = nbytes // 4
@@ -431,6 +458,11 @@ def main():
         traffic, traffic_note = None, "counters are taken on the quantizer only"
     else:
         traffic, traffic_note = traffic_from_counters(nbytes)
+
+    context = None
+    if args.workload == "dense_mxfp8":
+        context = vendor_cast_context(runner, args.steps, args.warmup)
+        log("[bench] context", json.dumps(context))
 
     secondary = []
     if not args.no_secondary:
@@ -489,6 +521,7 @@ def main():
                      "launch_us_mean": head["launch_us_mean"],
                      "launch_us_each": head["launch_us_each"]},
         "cpu_baseline": cpu,
+        "stream_context": context,
         "secondary": secondary,
     }
     print(json.dumps(line), flush=True)
