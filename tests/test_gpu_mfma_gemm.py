@@ -222,6 +222,38 @@ def test_grouped_mfma_skips_a_misaligned_group(bsq):
     assert hi1 == lo1 or np.all(got[lo1:hi1] != 7.0)
 
 
+def test_grouped_mfma_skips_bad_expert_ids_and_rows_past_max_rows(bsq):
+    """Groups whose expert id is out of range, or whose rows run past
+    max_rows, are skipped (their rows keep the caller's bytes); every other
+    group matches the oracle."""
+    fmt, G, E, N, K = MXFP4, 7, 3, 64, 256
+    d = grouped_case(fmt, G, E, N, K, 500, seed=78)
+    ro, ids = d["ro"], d["ids"].copy()
+    ids[1], ids[3] = E, -1                                  # out of range both ways
+    counts = np.diff(ro)
+    assert counts[1] > 0 and counts[3] > 0 and counts[6] > 1
+    max_rows = int(ro[6]) + int(counts[6]) // 2             # group 6 runs past it
+    out = torch.full((max_rows, N), 7.0, dtype=torch.float32, device="cuda")
+    bsq.grouped_block_scaled_matmul_mfma(
+        dev(d["qa"]), dev(d["la"]), dev(ro.view(np.int32)), dev(d["so"].view(np.int32)),
+        dev(ids), max_rows, d["nsr"], dev(d["qb"]), dev(d["lb"]), E, fmt, K, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    for g in range(G):
+        lo, hi, so = int(ro[g]), int(ro[g + 1]), int(d["so"][g])
+        if g in (1, 3, 6):
+            assert np.all(got[lo:min(hi, max_rows)] == 7.0), g
+            continue
+        if hi == lo:
+            continue
+        e = int(ids[g])
+        qa, sa = d["qa"][lo:hi], d["sa"][so:so + hi - lo]
+        qb, sb = d["qb"][e * N:(e + 1) * N], d["sb"][e * N:(e + 1) * N]
+        want = oracle.block_scaled_matmul(qa, sa, qb, sb, fmt, K)
+        S = magnitude_sum(qa, sa, qb, sb, fmt, K)
+        assert np.all(np.abs(got[lo:hi] - want) <= REL_BOUND * S), g
+
+
 def test_zero_k_and_empty(bsq):
     z = bsq.block_scaled_matmul_mfma(torch.zeros((5, 0), dtype=torch.uint8, device="cuda"),
                                      torch.zeros((1, 0), dtype=torch.uint8, device="cuda"),
