@@ -23,7 +23,6 @@ Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5]
        python bench.py --copy-bytes N   (plain copy kernel, for counter calibration)
 """
 import argparse
-import dataclasses
 import hashlib
 import json
 import os
@@ -56,12 +55,8 @@ def load_workload(name):
         "dense_nvfp4": W.dense_nvfp4_scaled_rows,
         "grouped_nvfp4": W.grouped_nvfp4_prefill,
         # the same routing quantized to the MX formats (large grouped MX path)
-        "grouped_mxfp8": lambda: dataclasses.replace(
-            W.grouped_nvfp4_prefill(), fmt=W.MXFP8, tensor_sf=None,
-            name="grouped_mxfp8_prefill_16384x7168_e128"),
-        "grouped_mxfp4": lambda: dataclasses.replace(
-            W.grouped_nvfp4_prefill(), fmt=W.MXFP4, tensor_sf=None,
-            name="grouped_mxfp4_prefill_16384x7168_e128"),
+        "grouped_mxfp8": lambda: W.grouped_mx_prefill(W.MXFP8),
+        "grouped_mxfp4": lambda: W.grouped_mx_prefill(W.MXFP4),
         "grouped_mxfp4_decode": lambda: W.grouped_mx_decode(W.MXFP4),
         "grouped_mxfp8_decode": lambda: W.grouped_mx_decode(W.MXFP8),
         # dequantization of codes and scales of the dense MXFP8 / NVFP4 sizes

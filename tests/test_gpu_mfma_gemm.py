@@ -149,6 +149,47 @@ def test_full_size_sampled_outputs(bsq, fmt, M, N, K):
     assert ratio <= REL_BOUND
 
 
+def mfma16_rows_to_row_major(lay, rows, nblk):
+    """Row-major scales [len(rows), nblk] of the given rows of an MFMA-layout
+    buffer, through the oracle's index map (offsets within a row group depend
+    only on r % 16 and the block)."""
+    lds = lay.shape[1]
+    inner = np.array([[oracle.mfma16_scale_offset(r16, kb, lds) for kb in range(nblk)]
+                      for r16 in range(16)], np.int64)
+    rows = np.asarray(rows, np.int64)
+    return lay.reshape(-1)[(rows // 16)[:, None] * lds + inner[rows % 16]]
+
+
+def test_grouped_gemm_prefill_full_size_sampled(bsq):
+    """The measured grouped GEMM (prefill routing, 128 experts, N = 512,
+    K = 7168): rows sampled from the largest, a mid-sized and the smallest
+    nonempty groups, first and last rows included, against the oracle."""
+    c = W.grouped_gemm_prefill(W.MXFP4)
+    fmt, K, E = c.fmt, c.K, c.num_experts
+    N = c.b_codes.shape[0] // E
+    nblk = K // 32
+    ro, so, ids = c.row_offsets, c.scales_offsets, c.expert_ids
+    out = bsq.grouped_block_scaled_matmul_mfma(
+        dev(c.a_codes), dev(c.a_scales), dev(ro.view(np.int32)), dev(so.view(np.int32)),
+        dev(ids), c.max_rows, c.num_scale_rows, dev(c.b_codes), dev(c.b_scales), E, fmt, K)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    counts = np.diff(ro.astype(np.int64))
+    nonempty = np.nonzero(counts)[0]
+    by_size = nonempty[np.argsort(counts[nonempty])]
+    rng = np.random.default_rng(5)
+    for g in (by_size[-1], by_size[len(by_size) // 2], by_size[0]):
+        lo, hi, e = int(ro[g]), int(ro[g + 1]), int(ids[g])
+        rows = np.unique(np.concatenate([[lo, hi - 1], rng.integers(lo, hi, 6)]))
+        sa = mfma16_rows_to_row_major(c.a_scales, int(so[g]) + rows - lo, nblk)
+        brows = e * N + np.arange(N)
+        sb = mfma16_rows_to_row_major(c.b_scales, brows, nblk)
+        qa, qb = c.a_codes[rows], c.b_codes[brows]
+        want = oracle.block_scaled_matmul(qa, sa, qb, sb, fmt, K)
+        S = magnitude_sum(qa, sa, qb, sb, fmt, K)
+        assert np.all(np.abs(got[rows] - want) <= REL_BOUND * S), (g, counts[g])
+
+
 def grouped_case(fmt, G, E, N, K, rows, seed, misaligned=None):
     """Routed activations quantized by the oracle's grouped quantizer (scales
     then mapped into the MFMA layout) and E experts' [N, K] weights (one

@@ -154,6 +154,13 @@ def test_grouped_nvfp4_prefill_16384x7168(bsq):
 
 
 @pytest.mark.parametrize("fmt", [oracle.MXFP4, oracle.MXFP8], ids=["mxfp4", "mxfp8"])
+def test_grouped_mx_prefill_16384x7168(bsq, fmt):
+    """The prefill routing quantized to the MX formats, as measured."""
+    c = W.grouped_mx_prefill(fmt)
+    assert_same(*grouped_pair(bsq, c), c.name)
+
+
+@pytest.mark.parametrize("fmt", [oracle.MXFP4, oracle.MXFP8], ids=["mxfp4", "mxfp8"])
 def test_grouped_decode_gather_512x2048(bsq, fmt):
     c = W.grouped_mx_decode(fmt)
     assert_same(*grouped_pair(bsq, c, pad_rows=3, pad_scale_rows=5), c.name)

@@ -47,7 +47,10 @@ def amax_of(h: np.ndarray) -> np.float32:
 
 
 def tensor_scale(h: np.ndarray) -> np.float32:
-    """fl32(amax / 2688); 1.0 for an empty or all-zero tensor."""
+    """fl32(amax / 2688); 1.0 for an empty or all-zero tensor.  The NVFP4
+    workloads' recipe for their input tensor scales: it sets an input and is
+    never an expected value (the device tensor-scale producer is checked
+    against the oracle's own definition, clamps included)."""
     a = amax_of(h)
     if a == 0:
         return np.float32(1.0)
@@ -149,6 +152,16 @@ def grouped_nvfp4_prefill(seed: int = 1004, rows: int = 16384, K: int = 7168,
     return GroupedCase("grouped_nvfp4_prefill_16384x7168_e128", NVFP4, x, ro, so,
                        np.arange(experts, dtype=np.int32), sf, None, max_rows=rows,
                        num_scale_rows=int(so[-1]), extra={"counts": counts})
+
+
+def grouped_mx_prefill(fmt: int) -> GroupedCase:
+    """The grouped NVFP4 prefill routing and activations, quantized to an MX
+    format instead (no tensor scales)."""
+    c = grouped_nvfp4_prefill()
+    name = {MXFP4: "mxfp4", MXFP8: "mxfp8"}[fmt]
+    return GroupedCase(f"grouped_{name}_prefill_16384x7168_e128", fmt, c.x, c.row_offsets,
+                       c.scales_offsets, c.expert_ids, None, None, max_rows=c.max_rows,
+                       num_scale_rows=c.num_scale_rows, extra=c.extra)
 
 
 def grouped_mx_decode(fmt: int = MXFP4, seed: int = 1005, tokens: int = 64, K: int = 2048,
