@@ -343,7 +343,7 @@ def cpu_baseline(case, runner, target_cpu_seconds=12.0, max_wall_seconds=20.0):
     s0 = runner.sets[0]
     ok = bool(np.array_equal(s0["q"][:rows].cpu().numpy(), qh) and
               np.array_equal(s0["s"][:rows].cpu().numpy(), sh))
-    # the same oracle on one thread, over a smaller leading sample (about 3 s)
+    # the same oracle on one thread, over a smaller leading sample (a few seconds at most)
     rows1 = int(min(M, max(1, 3.0 / max(per_row * threads, 1e-9))))
     t = time.perf_counter()
     oracle.quantize(case.x[:rows1], case.fmt, case.tensor_sf, nthreads=1)
