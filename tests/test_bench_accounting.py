@@ -1,0 +1,53 @@
+"""The byte and flop counts behind bench.py's achieved GB/s and TFLOP/s,
+pinned to the per-element figures stated for each workload: BF16 read (2
+bytes) plus codes (1 byte FP8, 1/2 FP4) plus one scale byte per block, times
+the elements a launch processes, plus the grouping metadata; each distinct
+gathered source row is read once.  CPU only: no kernel runs."""
+import numpy as np
+import pytest
+
+import bench
+import workloads as W
+
+
+def test_dense_workloads():
+    assert bench.algorithmic_bytes(W.dense_mxfp8_scaled_rows()) == (177_995_776, 8192 * 7168)
+    assert bench.algorithmic_bytes(W.dense_nvfp4_scaled_rows()) == (300_941_312, 16384 * 7168)
+    assert bench.algorithmic_bytes(W.dense_mxfp4_small()) == (1_327_104, 128 * 4096)
+    for fmt, per in ((W.MXFP4, 2.53125), (W.MXFP8, 3.03125), (W.NVFP4, 2.5625)):
+        assert bench.bytes_per_element(fmt) == per
+
+
+def test_grouped_workloads():
+    c = W.grouped_nvfp4_prefill()
+    # 16384 x 7168 x 2.5625 + (129 + 129 + 128 + 128) x 4 bytes of offsets, ids and scales
+    assert bench.algorithmic_bytes(c) == (300_943_368, 16384 * 7168)
+    assert 16384 * 7168 * 2.5625 + (129 + 129 + 128 + 128) * 4 == 300_943_368
+    for fmt, want in ((W.MXFP4, 824_328), (W.MXFP8, 1_348_616)):
+        d = W.grouped_mx_decode(fmt)
+        distinct = np.unique(d.row_indices).size
+        assert distinct == 64                    # every token is routed
+        assert bench.algorithmic_bytes(d)[0] == want
+
+
+def test_tensor_scale_producer_bytes():
+    assert bench.producer_bytes(W.dense_nvfp4_scaled_rows()) == (16384 * 7168 * 2 + 4,
+                                                                16384 * 7168)
+    nb, elems = bench.producer_bytes(W.grouped_nvfp4_prefill())
+    assert nb == 16384 * 7168 * 2 + (129 + 128 + 128) * 4 and elems == 16384 * 7168
+
+
+def test_dequantize_and_gemm_accounting():
+    d = W.dequant_random_bytes(W.MXFP8, 256, 7168, seed=1)
+    assert bench.algorithmic_bytes(d) == (256 * 7168 * (1 + 4) + 256 * 224, 256 * 7168)
+    g = W.gemm_random_operands(W.MXFP4, 256, 512, 1024, seed=2)
+    nb, _ = bench.algorithmic_bytes(g)
+    rec = 256 * (1024 // 512)                    # MFMA-layout bytes per 16 rows
+    assert nb == 256 * 512 + 512 * 512 + (256 // 16 + 512 // 16) * rec + 4 * 256 * 512
+    assert bench.gemm_flops(g) == 2 * 256 * 512 * 1024
+
+
+@pytest.mark.parametrize("name", ["mfma_gemm_mxfp8", "mfma_gemm_mxfp4"])
+def test_measured_gemm_flops(name):
+    c = bench.load_workload(name)
+    assert bench.gemm_flops(c) == 2 * 4096 * 4096 * 7168
