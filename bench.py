@@ -18,7 +18,7 @@ uses the host wall clock of the same loop.  The CPU oracle is timed on a bounded
 sample of the same workload on the host's cores (``cpu_baseline``), and its
 output doubles as a parity check of that sample.
 
-Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+Usage: python bench.py [--gpus 1] [--steps 500] [--warmup 20]
        [--workload dense_mxfp8] [--no-secondary] [--no-cpu-baseline]
        python bench.py --copy-bytes N   (plain copy kernel, for counter calibration)
 """
@@ -283,6 +283,32 @@ def launch_percentiles(runner, n, offset):
             "p90": round(float(np.percentile(us, 90)), 3), "n": n}
 
 
+def graph_launch_us(runner, n_launch=64, replays=20):
+    """Mean duration per launch (µs) when n_launch launches, rotating over the
+    buffer sets, are replayed from one captured HIP graph: no host launch cost
+    sits between the kernels, so for a small problem this is the kernel's own
+    time plus the dispatch gap, where the eager loop measures the host."""
+    torch = runner.torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n_launch):
+            runner.step(i)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return round(a.elapsed_time(b) / (n_launch * replays) * 1e3, 3)
+
+
+# below this many bytes per launch the host's launch cost exceeds the kernel's
+# time, and the graph replay figure is the one that describes the kernel
+LATENCY_BOUND_BYTES = 16 << 20
+
+
 def measure(name, steps, warmup, rotate=True):
     import workloads as W
     producer = name in PRODUCERS
@@ -294,12 +320,13 @@ def measure(name, steps, warmup, rotate=True):
     runner = Runner(case, nb, producer)
     wall, kern = time_steps(runner, steps, warmup)
     runner.percentiles = launch_percentiles(runner, steps, warmup + steps)
+    runner.graph_us = graph_launch_us(runner) if nbytes < LATENCY_BOUND_BYTES else None
     return case, runner, nbytes, elems, nb, wall, kern
 
 
-def summary(name, nbytes, elems, wall, launch_ms, steps, nb, percentiles=None):
+def summary(name, nbytes, elems, wall, launch_ms, steps, nb, percentiles=None, graph_us=None):
     k = launch_ms * 1e-3
-    return {
+    out = {
         "workload": name,
         "bytes_per_launch": nbytes,
         "elements": elems,
@@ -311,6 +338,10 @@ def summary(name, nbytes, elems, wall, launch_ms, steps, nb, percentiles=None):
         "Gelem_per_s": round(elems / k / 1e9, 1),
         "wall_GBps": round(nbytes * steps / wall / 1e9, 1),
     }
+    if graph_us is not None:  # latency-bound: the kernel's time without the host's launch cost
+        out.update({"graph_us_mean": graph_us, "graph_GBps": round(nbytes / graph_us / 1e3, 1),
+                    "graph_Gelem_per_s": round(elems / graph_us / 1e3, 1)})
+    return out
 
 
 # ------------------------------------------------------------------ CPU baseline
@@ -420,8 +451,8 @@ def copy_calibration(nbytes, steps):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="dense_mxfp8")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -444,7 +475,8 @@ def main():
     import fp8_quantization_amd as bsq
 
     case, runner, nbytes, elems, nb, wall, kern = measure(args.workload, args.steps, args.warmup)
-    head = summary(args.workload, nbytes, elems, wall, kern, args.steps, nb, runner.percentiles)
+    head = summary(args.workload, nbytes, elems, wall, kern, args.steps, nb, runner.percentiles,
+                   runner.graph_us)
     log("[bench] headline", json.dumps(head))
     achieved = nbytes / (kern * 1e-3) / 1e9
     quantizer = args.workload not in PRODUCERS and not args.workload.startswith(
@@ -468,7 +500,7 @@ def main():
             if name == args.workload:
                 continue
             c2, r2, nb2, el2, nbs2, w2, k2 = measure(name, args.steps, args.warmup)
-            s = summary(name, nb2, el2, w2, k2, args.steps, nbs2, r2.percentiles)
+            s = summary(name, nb2, el2, w2, k2, args.steps, nbs2, r2.percentiles, r2.graph_us)
             if name.startswith(("mfma_gemm", "mfma_grouped_gemm")):
                 tf = gemm_flops(c2) / (k2 * 1e-3) / 1e12
                 peak = PEAK_MFMA_TFLOPS[c2.fmt]

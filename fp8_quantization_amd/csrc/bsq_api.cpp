@@ -245,7 +245,7 @@ int tsf_geometry(bsq::KernelArgs& a, int64_t* blocks, int* waves_per_block,
 }
 
 // Launch geometry: one wave per tile, four waves per workgroup.
-//  * Dense: tiles of 2 chunks (1024 elements: two 16-byte loads per lane).
+//  * Dense, large: tiles of 2 chunks (1024 elements: two 16-byte loads per lane).
 //    Many short waves keep the most loads in flight across the chip and
 //    leave the smallest tail; 1 or 4 chunks per wave, and a persistent grid
 //    walking the tiles, measured slower.
@@ -254,11 +254,14 @@ int tsf_geometry(bsq::KernelArgs& a, int64_t* blocks, int* waves_per_block,
 //    expert's reciprocal table.  On the 16384 x 7168 prefill: NVFP4 49.7 us
 //    against 51.8 with 2 chunks and 51.6 with 8; MXFP8 and MXFP4 equal
 //    within noise at 2, 4 and 8.
-//  * Grouped, small (decode-sized, latency-bound): tiles of 1 chunk, for the
-//    most parallel waves.
+//  * Small (at most 2^22 elements, latency-bound), dense or grouped: tiles of
+//    1 chunk, for the most parallel waves.  Timed from a replayed HIP graph:
+//    the 512 routed rows x 2048 decode gather 3.07 us against 3.10 with 2
+//    chunks and 3.40 with 4; dense 128 x 4096 MXFP4 2.32 us against 2.40 and
+//    2.61.
 int launch(int format, bool grouped, bsq::KernelArgs& a, hipStream_t stream) {
     const bool small = (double)a.rows * (double)a.K <= (double)(1 << 22);
-    int u = grouped ? (small ? 1 : 4) : 2;
+    int u = small ? 1 : grouped ? 4 : 2;
     if (tile_knob()) u = tile_knob();
     int64_t blocks = 0;
     if (st_geometry(a, u, &blocks) != BSQ_OK) return BSQ_ERR_INVALID_ARG;
