@@ -262,8 +262,10 @@ __device__ __forceinline__ LaneOut quantize_lane(const uint4& w, const Nvfp4Wave
 // ---------------------------------------------------------------- kernel
 //
 // One wave converts one tile: U consecutive chunks (U * 512 elements) of one
-// row.  Loads and stores carry the non-temporal hint: the data streams through
-// once, so it should not displace anything from the caches.
+// row.  Loads carry the non-temporal hint: the data streams through once, so
+// it should not displace anything from the caches.  Stores take the cache
+// policy measured best for the code width and problem size (kStoreStream,
+// kStoreWriteThrough below).
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
@@ -272,6 +274,20 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 // format; no swizzle, stride 0), and the load's nontemporal cache policy.
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kBufferNontemporal = 2;
+// Cache policy of the quantizers' code and scale stores (the aux operand of
+// the buffer store: bit 1 nt, bit 4 sc1).  Measured in alternation on one box:
+//  * FP4 codes (4 bytes per lane per store) of large problems go out with
+//    device scope (sc1), which writes through the XCD's L2: grouped MXFP4 on
+//    the 16384 x 7168 prefill routing took 45.4 us against 48.5 with nt,
+//    dense NVFP4 16384 x 7168 48.1 against 49.0, grouped NVFP4 49.3 against
+//    49.8;
+//  * FP8 codes (8 bytes per lane) go out non-temporal: grouped MXFP8 on the
+//    same routing took 62.0 us with sc1 against 56.6 with nt;
+//  * small problems (one chunk per wave) go out non-temporal: the MXFP4
+//    decode gather (512 routed rows x 2048) took 3.96 us with sc1 against
+//    3.09 with nt, where the write-through's latency is on the critical path.
+constexpr int kStoreStream = 2;         // nt
+constexpr int kStoreWriteThrough = 16;  // sc1
 
 __device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
     const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
@@ -388,6 +404,17 @@ __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const Kernel
     Nvfp4Wave nw{};
     if constexpr (FMT == 2) nw = nvfp4_wave_setup(tsf, lane);
 
+    // store descriptors over this row's codes and its scale bytes (the
+    // offsets below stay inside them; a store outside would be dropped)
+    constexpr int kPolicy = (T::kFp4 && U > 1) ? kStoreWriteThrough : kStoreStream;
+    const int code_bytes = T::kFp4 ? a.K / 2 : a.K;
+    const int scale_bytes = mfma_layout ? a.chunks_per_row * 256 - 4 * (int)(scale_row & 15)
+                                        : a.K / T::kBlock;
+    const __amdgpu_buffer_rsrc_t qrsrc =
+        __builtin_amdgcn_make_buffer_rsrc(qrow, (short)0, code_bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t srsrc =
+        __builtin_amdgcn_make_buffer_rsrc(srow, (short)0, scale_bytes, kBufferWord3);
+
     uint32_t sb[U], q0[U], q1[U];  // per chunk: scale byte, packed codes (FP4: q0 only)
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -404,10 +431,10 @@ __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const Kernel
         const uint32_t col = (uint32_t)((c0 + u) * kChunkElems + lane * kElemsPerLane);
         if (col < (uint32_t)a.K) {
             if constexpr (T::kFp4) {
-                __builtin_nontemporal_store(q0[u], reinterpret_cast<uint32_t*>(qrow + col / 2));
+                __builtin_amdgcn_raw_buffer_store_b32(q0[u], qrsrc, (int)(col / 2), 0, kPolicy);
             } else {
                 const u32x2_t v = {q0[u], q1[u]};
-                __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(qrow + col));
+                __builtin_amdgcn_raw_buffer_store_b64(v, qrsrc, (int)col, 0, kPolicy);
             }
         }
     }
@@ -426,9 +453,10 @@ __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const Kernel
         // block b = lane / L of chunk c0 + u; in the MFMA layout a chunk is one
         // record and block b goes to lane-dword 16 (b % 4), byte b / 4
         const int b = lane / L;
-        uint8_t* dst = mfma_layout ? srow + (c0 + u) * 256 + 64 * (b & 3) + (b >> 2)
-                                   : srow + col / T::kBlock;
-        if (u < nch && u < U && col < (uint32_t)a.K) __builtin_nontemporal_store((uint8_t)v, dst);
+        const int off = mfma_layout ? (c0 + u) * 256 + 64 * (b & 3) + (b >> 2)
+                                    : (int)(col / T::kBlock);
+        if (u < nch && u < U && col < (uint32_t)a.K)
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, srsrc, off, 0, kPolicy);
     }
 }
 
