@@ -38,7 +38,9 @@ def layout_buffer(bsq, fmt, rows, K, extra=0):
 
 @pytest.mark.parametrize("fmt", [MXFP4, MXFP8])
 @pytest.mark.parametrize("M,K,extra", [(1, 32, 0), (16, 512, 0), (37, 1056, 0), (300, 2048, 64),
-                                       (129, 7168, 0), (5, 544, 256)])
+                                       (129, 7168, 0), (5, 544, 256),
+                                       # over 2^22 elements: tiles of 2 chunks, ragged last tile
+                                       (1000, 4544, 0), (1003, 4608, 32)])
 def test_dense_quantize_writes_the_layout(bsq, fmt, M, K, extra):
     x = W.random_bf16((M, K), seed=M + K + fmt, scale_log2_range=(-30, 30), special_frac=0.002)
     buf = layout_buffer(bsq, fmt, M, K, extra)
@@ -52,10 +54,14 @@ def test_dense_quantize_writes_the_layout(bsq, fmt, M, K, extra):
 
 
 @pytest.mark.parametrize("fmt", [MXFP4, MXFP8])
-@pytest.mark.parametrize("gather,pad16", [(False, True), (True, True), (True, False)])
-def test_grouped_quantize_writes_the_layout(bsq, fmt, gather, pad16):
+@pytest.mark.parametrize("gather,pad16,K", [(False, True, 1024), (True, True, 1024),
+                                            (True, False, 1024),
+                                            # 350+ routed rows x 12544: over 2^22 elements
+                                            # (tiles of 4 chunks), last tile 1 partial chunk
+                                            (True, True, 12544), (False, False, 12544)])
+def test_grouped_quantize_writes_the_layout(bsq, fmt, gather, pad16, K):
     rng = np.random.default_rng(fmt * 3 + gather + 2 * pad16)
-    S, K, G = 400, 1024, 23
+    S, G = 400, 23
     x = W.random_bf16((S, K), seed=S + fmt, scale_log2_range=(-10, 10), special_frac=0.001)
     w = rng.random(G) * (rng.random(G) > 0.3)
     w[0] += 1e-3

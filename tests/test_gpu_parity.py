@@ -182,6 +182,22 @@ def test_ragged_shapes_padded_strides(bsq, fmt, M, K):
 
 @pytest.mark.parametrize("fmt", [oracle.MXFP4, oracle.MXFP8, oracle.NVFP4],
                          ids=["mxfp4", "mxfp8", "nvfp4"])
+@pytest.mark.parametrize("M,K", [(1000, 4544), (1001, 4608), (600, 7200)])
+def test_dense_large_problem_path(bsq, fmt, M, K):
+    """Over 2^22 elements dense rows go in tiles of 2 chunks (512 elements
+    each), and FP4 codes take the write-through stores.  K = 4544 is 9 chunks,
+    the last holding 448 elements, so every row ends in a half-empty tile with
+    a partial chunk; K = 4608 is 9 whole chunks; K = 7200 is 14 whole chunks and
+    a 32-element one.  Strides are padded."""
+    assert M * K > (1 << 22)
+    x = W.random_bf16((M, K), seed=M + K + 100 * fmt, scale_log2_range=(-20, 20),
+                      special_frac=0.001)
+    tsf = 0.01 if fmt == oracle.NVFP4 else 1.0
+    assert_same(*dense_pair(bsq, x, fmt, tsf, pad_x=40, pad_q=16, pad_s=5), f"{M}x{K}")
+
+
+@pytest.mark.parametrize("fmt", [oracle.MXFP4, oracle.MXFP8, oracle.NVFP4],
+                         ids=["mxfp4", "mxfp8", "nvfp4"])
 def test_nvfp4_nk_16_not_32(bsq, fmt):
     # K = 16 * odd: NVFP4 accepts it (packed row is 8 * odd bytes); MX rejects it
     x = W.random_bf16((9, 48), seed=5)
@@ -257,11 +273,13 @@ def test_grouped_random_offsets(bsq, fmt, G, gather, first, extra):
 
 @pytest.mark.parametrize("fmt", [oracle.MXFP4, oracle.MXFP8, oracle.NVFP4],
                          ids=["mxfp4", "mxfp8", "nvfp4"])
-@pytest.mark.parametrize("G,gather", [(5, False), (129, True), (600, False)])
-def test_grouped_large_problem_path(bsq, fmt, G, gather):
-    """Over 2^22 routed elements the library switches to 4-chunk tiles and the
-    offsets-only group search; K = 4608 leaves a ragged 1-chunk last tile."""
-    rows, K = 1200, 4608
+@pytest.mark.parametrize("G,gather,K", [(5, False, 4608), (129, True, 4608), (600, False, 4608),
+                                         (129, True, 4544), (7, False, 4544)])
+def test_grouped_large_problem_path(bsq, fmt, G, gather, K):
+    """Over 2^22 routed elements the library switches to 4-chunk tiles (and,
+    for FP4 codes, write-through stores); K = 4608 leaves a ragged 1-chunk last
+    tile, K = 4544 a last tile of one partial chunk (448 elements)."""
+    rows = 1200
     assert rows * K > (1 << 22)
     c = make_grouped(fmt, S=1300, K=K, G=G, E=G + 3, rows=rows, gather=gather, seed=G + 7,
                      first_row=2, extra_rows=5)
