@@ -67,6 +67,7 @@ def load_workload(name):
         "mfma_gemm_mxfp8": lambda: W.gemm_random_operands(W.MXFP8, 4096, 4096, 7168, seed=1202),
         "mfma_gemm_mxfp4": lambda: W.gemm_random_operands(W.MXFP4, 4096, 4096, 7168, seed=1201),
         "mfma_grouped_gemm_mxfp4": lambda: W.grouped_gemm_prefill(W.MXFP4),
+        "mfma_grouped_gemm_mxfp4_decode": lambda: W.grouped_gemm_decode(W.MXFP4),
     }
     return table[name]()
 
@@ -120,11 +121,18 @@ def algorithmic_bytes(case):
     import workloads as W
     if isinstance(case, W.DequantCase):
         return dequant_bytes(case)
-    if isinstance(case, W.GroupedGemmCase):   # operands and metadata read once + c written
+    if isinstance(case, W.GroupedGemmCase):
+        # routed A, its scale records and the metadata read once; the weights
+        # and scale records of each expert that owns rows read once (an
+        # expert with no rows is never read); c written
         N = case.b_codes.shape[0] // case.num_experts
+        E = case.num_experts
         meta = 4 * (case.row_offsets.size + case.scales_offsets.size + case.expert_ids.size)
-        return int(case.a_codes.nbytes + case.a_scales.nbytes + case.b_codes.nbytes +
-                   case.b_scales.nbytes + meta + 4 * case.max_rows * N), case.max_rows * N
+        counts = np.diff(case.row_offsets.astype(np.int64))
+        used = np.unique(case.expert_ids[counts > 0]).size
+        return int(case.a_codes.nbytes + case.a_scales.nbytes +
+                   used * (case.b_codes.nbytes + case.b_scales.nbytes) // E +
+                   meta + 4 * case.max_rows * N), case.max_rows * N
     if isinstance(case, W.GemmCase):    # operands read once + c written
         M, N = case.a_codes.shape[0], case.b_codes.shape[0]
         return int(case.a_codes.nbytes + case.a_scales.nbytes + case.b_codes.nbytes +
@@ -496,7 +504,8 @@ def main():
         for name in ("dense_nvfp4", "grouped_nvfp4", "dense_mxfp4", "grouped_mxfp4_decode",
                      "grouped_mxfp8_decode", "grouped_mxfp8", "grouped_mxfp4",
                      "tsf_dense_nvfp4", "tsf_grouped_nvfp4", "dequant_mxfp8", "dequant_nvfp4",
-                     "mfma_gemm_mxfp8", "mfma_gemm_mxfp4", "mfma_grouped_gemm_mxfp4"):
+                     "mfma_gemm_mxfp8", "mfma_gemm_mxfp4", "mfma_grouped_gemm_mxfp4",
+                     "mfma_grouped_gemm_mxfp4_decode"):
             if name == args.workload:
                 continue
             c2, r2, nb2, el2, nbs2, w2, k2 = measure(name, args.steps, args.warmup)

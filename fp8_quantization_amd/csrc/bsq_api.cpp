@@ -66,7 +66,9 @@ int tile_knob() {
 //   BSQ_MFMA_TILED           matrix-core GEMM: two LDS stage buffers, 256 x 256 tiles where
 //                            they fill the chip and 128 x 128 otherwise (default); 2 one wave
 //                            per 16 x 16 tile (dense); 3 128 x 128 tiles, three stage
-//                            buffers; 4 128 x 128 tiles (dense)
+//                            buffers; 4 128 x 128 tiles (dense); 5 / 6 the grouped
+//                            form's decode (16-row) / prefill (128-row) kernel whatever
+//                            the rows per group
 int mfma_tiled_knob() {
     static const int v = env_knob("BSQ_MFMA_TILED");
     return v;
@@ -647,8 +649,16 @@ int grouped_block_scaled_matmul_mfma(int format, int block_size, int scale_layou
     g.num_experts = (int32_t)num_experts;
     g.max_rows = max_rows;
     g.num_scale_rows = num_scale_rows;
-    g.m_tiles = (max_rows + 127) / 128 + num_groups;   // each group adds at most one partial tile
-    if (g.m_tiles > 0x7FFFFFFFLL || (N + 127) / 128 > 65535)
+    // Few rows per group (at most 16 on average over max_rows, as in a decode
+    // step): 16-row tiles with the weights streamed straight to registers.
+    // Otherwise 128-row tiles staged through LDS.
+    const int knob = mfma_tiled_knob();
+    g.decode = knob == 5 || (knob != 6 && max_rows <= 16 * num_groups);
+    const int64_t tile_m = g.decode ? bsq::kDecodeTileRows : 128;
+    const int64_t tile_n = g.decode ? bsq::kDecodeTileCols : 128;
+    g.m_tiles = (max_rows + tile_m - 1) / tile_m + num_groups;  // each group adds at most one
+                                                                // partial tile
+    if (g.m_tiles > 0x7FFFFFFFLL || (N + tile_n - 1) / tile_n > 65535)
         return fail(BSQ_ERR_INVALID_ARG, "problem too large for one launch");
     bsq::GemmArgs a{};
     a.a_codes = static_cast<const uint8_t*>(a_codes);

@@ -335,17 +335,18 @@ __device__ __forceinline__ void dense_desc(const GemmArgs& a, int64_t tiles_n, G
     d.K = a.K;
 }
 
-// Grouped per-expert form: blockIdx.y is the 128-column tile of c, blockIdx.x
-// a 128-row tile counted across the groups in order (group g has
-// ceil(m_g / 128) of them); each wave finds its group from the offsets.
+// Grouped per-expert form: blockIdx.y is the TN-column tile of c, blockIdx.x
+// a TM-row tile counted across the groups in order (group g has ceil(m_g /
+// TM) of them); each wave finds its group from the offsets.
 // Group g multiplies its routed rows (codes row r, scale row
 // scales_offsets[g] + r - row_offsets[g]) by the B of expert expert_ids[g]
 // ([N, K] codes from row e N, scales from row group e ceil(N / 16)).  A group
 // whose metadata falls outside the buffers, or whose scale offset is not a
 // multiple of 16 (the layout's row groups), is skipped: returns false.
+template <int TM, int TN>
 __device__ __forceinline__ bool grouped_desc(const GemmArgs& a, const GroupedGemmArgs& g,
                                              GemmTile& d) {
-    const int64_t n0 = (int64_t)blockIdx.y * kTileN;
+    const int64_t n0 = (int64_t)blockIdx.y * TN;
     int64_t t = blockIdx.x;
     int grp = -1;
     int64_t lo = 0, hi = 0;
@@ -360,7 +361,7 @@ __device__ __forceinline__ bool grouped_desc(const GemmArgs& a, const GroupedGem
         if (h < g.num_groups) {
             l = g.row_offsets[h];
             u = g.row_offsets[h + 1];
-            tiles = u > l ? (uint32_t)(((uint64_t)u - l + kTileM - 1) / kTileM) : 0u;
+            tiles = u > l ? (uint32_t)(((uint64_t)u - l + TM - 1) / TM) : 0u;
         }
         uint32_t incl = tiles;                               // at most 2^25 + 64 in total
 #pragma unroll
@@ -383,7 +384,7 @@ __device__ __forceinline__ bool grouped_desc(const GemmArgs& a, const GroupedGem
     if (grp < 0) return false;                               // past the last group's tiles
     const int e = g.expert_ids[grp];
     const int64_t so = g.scales_offsets[grp];
-    const int64_t r0 = lo + t * kTileM;
+    const int64_t r0 = lo + t * TM;
     if (hi > g.max_rows || e < 0 || e >= g.num_experts || so % 16 != 0 ||
         so + (hi - lo) > g.num_scale_rows)
         return false;
@@ -391,7 +392,7 @@ __device__ __forceinline__ bool grouped_desc(const GemmArgs& a, const GroupedGem
     d.a = a.a_codes + r0 * a.lda_q;
     d.lda_q = a.lda_q;
     d.a_rows = hi - r0;
-    d.as = a.a_scales + ((so + t * kTileM) >> 4) * a.lda_s;
+    d.as = a.a_scales + ((so + t * TM) >> 4) * a.lda_s;
     d.lda_s = a.lda_s;
     d.a_groups = (hi - r0 + 15) / 16;
     d.b = a.b_codes + ((int64_t)e * a.N + n0) * a.ldb_q;
@@ -624,8 +625,116 @@ __global__ void __launch_bounds__(64 * Tile128::NW)
 mfma_gemm_grouped_kernel(const GemmArgs a, const GroupedGemmArgs g) {
     BSQ_STAGE_BUFFERS(NBUF, Tile128::kStageBytes)
     GemmTile d;
-    if (!grouped_desc(a, g, d)) return;
+    if (!grouped_desc<kTileM, kTileN>(a, g, d)) return;
     run_tile<FMT, NBUF, Tile128>(d, stage0, stage1, stage2);
+}
+
+// ------------------------------------------------------------ decode regime
+//
+// Grouped GEMM for groups of a few rows each (a decode step: a handful of
+// tokens per expert).  A 128-row tile would spend nearly all of its matrix
+// work and LDS traffic on padding rows, and the expert's weights dominate the
+// bytes, so this form is built around streaming B once per 16 routed rows:
+//  * a workgroup takes 16 rows of one group (the instruction's smallest M)
+//    and kSkinnyWaves x 16 J columns of c; each wave owns J 16 x 16 tiles of
+//    c over the whole of K;
+//  * no LDS: every lane loads its own A and B fragments from global memory
+//    straight into registers, 512 elements of K (four K steps, one scale
+//    dword per operand) per round, so a wave keeps 4 (J + 1) 16-byte loads
+//    (MXFP4) or twice that (MXFP8) in flight, and the waves sharing a SIMD
+//    cover each other's latency;
+//  * rows past the group load its last row and columns past N the last B
+//    row (their outputs are never stored), so every load is in bounds.
+// It follows the decode entry in the "NVFP4 routing" section of the grouped
+// block-scaled SM100 matmul's "dispatch" page (few rows per expert: a narrow
+// tile on the token side), with the smallest tile the CDNA4 instruction has.
+constexpr int kSkinnyRows = kDecodeTileRows, kSkinnyWaves = 4, kSkinnyJ = 4;
+constexpr int kSkinnyCols = kSkinnyWaves * 16 * kSkinnyJ;
+static_assert(kSkinnyRows == 16 && kSkinnyCols == kDecodeTileCols, "decode tile shape");
+
+template <int FMT, int S>
+__device__ __forceinline__ mfma_v4f mfma_opsel(const mfma_v8i& fa, const mfma_v8i& fb,
+                                              const mfma_v4f& acc, uint32_t sa, uint32_t sb) {
+    constexpr int kFmt = FMT == 1 ? 0 : 4;  // instruction format codes: 0 E4M3, 4 E2M1
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb, acc, kFmt, kFmt, S, (int)sa, S,
+                                                            (int)sb);
+}
+
+// One K step S (of the round's four) of the wave's J tiles, if it exists.
+template <int FMT, int J, int S>
+__device__ __forceinline__ void skinny_step(const mfma_v8i (&fa)[4], const mfma_v8i (&fb)[4][J],
+                                            mfma_v4f (&acc)[J], uint32_t sa,
+                                            const uint32_t (&sb)[J], bool live) {
+    if (!live) return;
+#pragma unroll
+    for (int j = 0; j < J; ++j) acc[j] = mfma_opsel<FMT, S>(fa[S], fb[S][j], acc[j], sa, sb[j]);
+}
+
+template <int FMT, int J>
+__device__ __forceinline__ void gemm_tile_skinny(const GemmTile& d) {
+    const int lane = (int)(threadIdx.x & 63);
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int cb = 16 * J * wave;                            // the wave's first column
+    if (cb >= d.c_cols) return;                              // wave-uniform: nothing here
+    const int fr = lane & 15, fg = lane >> 4;
+    const int64_t ra = fr < d.a_rows ? fr : d.a_rows - 1;
+    const uint8_t* arow = d.a + ra * d.lda_q;
+    const uint8_t* asr = d.as + 4 * lane;                    // the tile's one A row group
+    const uint8_t* brow[J];
+    const uint8_t* bsr[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int64_t rb = cb + 16 * j + fr, gb = (cb + 16 * j) >> 4;
+        brow[j] = d.b + (rb < d.b_rows ? rb : d.b_rows - 1) * d.ldb_q;
+        bsr[j] = d.bs + (gb < d.b_groups ? gb : d.b_groups - 1) * d.ldb_s + 4 * lane;
+    }
+    mfma_v4f acc[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) acc[j] = (mfma_v4f){0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int nk = d.K / 128;                                // K steps (K is a multiple of 128)
+    for (int k4 = 0; k4 < nk; k4 += 4) {
+        const int rec = (k4 >> 2) * 256;                     // the round's 512-element record
+        const uint32_t sa = *reinterpret_cast<const uint32_t*>(asr + rec);
+        uint32_t sb[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) sb[j] = *reinterpret_cast<const uint32_t*>(bsr[j] + rec);
+        mfma_v8i fa[4], fb[4][J];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const bool live = k4 + st < nk;
+            fa[st] = load_fragment<FMT>(arow, (k4 + st) * 128, fg, live);
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+                fb[st][j] = load_fragment<FMT>(brow[j], (k4 + st) * 128, fg, live);
+        }
+        skinny_step<FMT, J, 0>(fa, fb, acc, sa, sb, true);
+        skinny_step<FMT, J, 1>(fa, fb, acc, sa, sb, k4 + 1 < nk);
+        skinny_step<FMT, J, 2>(fa, fb, acc, sa, sb, k4 + 2 < nk);
+        skinny_step<FMT, J, 3>(fa, fb, acc, sa, sb, k4 + 3 < nk);
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int64_t col = cb + 16 * j + fr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t row = 4 * fg + e;
+            if (row < d.c_rows && col < d.c_cols) d.c[row * d.ldc + col] = acc[j][e];
+        }
+    }
+}
+
+// One workgroup per 16-row tile and 256-column tile.  Measured on the decode
+// routing (512 routed rows over 256 experts, N = 7168, K = 2048): 345 us,
+// against 349-410 us with each workgroup looping over 2 to 28 column tiles
+// (one group lookup for several tiles), 376 us with non-temporal B loads,
+// and 385 us for the 128-row kernel.
+template <int FMT>
+__global__ void __launch_bounds__(64 * kSkinnyWaves)
+mfma_gemm_grouped_skinny_kernel(const GemmArgs a, const GroupedGemmArgs g) {
+    GemmTile d;
+    if (!grouped_desc<kSkinnyRows, kSkinnyCols>(a, g, d)) return;
+    gemm_tile_skinny<FMT, kSkinnyJ>(d);
 }
 
 template <int FMT, class Cfg>
@@ -707,6 +816,12 @@ hipError_t launch_dequantize(int fmt, const DequantArgs& a, int64_t blocks, hipS
 namespace {
 template <int FMT>
 hipError_t launch_mfma_grouped(const GemmArgs& a, const GroupedGemmArgs& g, hipStream_t stream) {
+    if (g.decode) {
+        const dim3 grid((uint32_t)g.m_tiles, (uint32_t)((a.N + kSkinnyCols - 1) / kSkinnyCols));
+        hipLaunchKernelGGL((mfma_gemm_grouped_skinny_kernel<FMT>), grid, dim3(64 * kSkinnyWaves), 0,
+                           stream, a, g);
+        return hipGetLastError();
+    }
     const dim3 grid((uint32_t)g.m_tiles, (uint32_t)((a.N + kTileN - 1) / kTileN));
     const dim3 block(64 * Tile128::NW);
     if (a.tiled == 3)

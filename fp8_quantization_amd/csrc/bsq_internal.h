@@ -113,6 +113,8 @@ hipError_t launch_mfma_matmul(int fmt, const GemmArgs& a, hipStream_t stream);
 
 // Grouped per-expert GEMM: A rows grouped by row_offsets (scale rows by
 // scales_offsets), B = num_experts stacked [N, K] operands; GemmArgs.M unused.
+// Tile of the grouped GEMM's decode form: rows of one group x columns of c.
+constexpr int kDecodeTileRows = 16, kDecodeTileCols = 256;
 struct GroupedGemmArgs {
     const uint32_t* row_offsets;     // [num_groups + 1]
     const uint32_t* scales_offsets;  // [num_groups + 1]
@@ -121,7 +123,9 @@ struct GroupedGemmArgs {
     int32_t num_experts;
     int64_t max_rows;                // rows of A codes and of c
     int64_t num_scale_rows;          // scale rows of A
-    int64_t m_tiles;                 // grid bound on 128-row tiles over all groups
+    int64_t m_tiles;                 // grid bound on row tiles over all groups
+    int32_t decode;                  // 1: 16-row tiles, B streamed to registers (few rows
+                                     // per group); 0: 128-row tiles staged through LDS
 };
 hipError_t launch_mfma_grouped_matmul(int fmt, const GemmArgs& a, const GroupedGemmArgs& g,
                                       hipStream_t stream);

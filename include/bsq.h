@@ -301,6 +301,14 @@ int block_scaled_matmul_mfma(int format, int block_size, int scale_layout,
  * expert e's weights.  Rows of c no group owns are not written.  Accuracy
  * as for block_scaled_matmul_mfma.
  *
+ * Two kernels, chosen on the host from max_rows / num_groups (the offsets
+ * stay on the device), after the decode / prefill split in the "NVFP4
+ * routing" section of the grouped block-scaled SM100 matmul's "dispatch"
+ * page: at most 16 rows per group on average
+ * (decode) takes 16-row tiles that stream each expert's weights into
+ * registers; more takes 128-row tiles staged through LDS.  Both give the
+ * same results within the stated bound.
+ *
  *   format, block_size, scale_layout   as for block_scaled_matmul_mfma.
  *   a_codes, lda_q       [max_rows, K] codes (routed order), 16-byte aligned rows.
  *   a_scales, lda_s      MFMA-layout scales over num_scale_rows rows, 16-byte

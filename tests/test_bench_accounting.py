@@ -51,3 +51,19 @@ def test_dequantize_and_gemm_accounting():
 def test_measured_gemm_flops(name):
     c = bench.load_workload(name)
     assert bench.gemm_flops(c) == 2 * 4096 * 4096 * 7168
+
+
+def test_grouped_gemm_bytes_count_only_experts_with_rows():
+    """Routed A and its scale records, the weights of each expert that owns
+    rows (an expert with no rows is never read), the metadata, and c."""
+    for c in (W.grouped_gemm_prefill(W.MXFP4, rows=512, K=256, N=64, experts=16),
+              W.grouped_gemm_decode(W.MXFP4, tokens=8, K=256, N=32, experts=64, topk=2)):
+        E, K = c.num_experts, c.K
+        N = c.b_codes.shape[0] // E
+        counts = np.diff(c.row_offsets.astype(np.int64))
+        used = int(np.count_nonzero(counts))             # expert_ids = arange: one group each
+        assert 0 < used < E                              # some experts are empty
+        per_expert = N * K // 2 + ((N + 15) // 16) * ((K // 32 + 15) // 16) * 256
+        want = (c.a_codes.nbytes + c.a_scales.nbytes + used * per_expert +
+                4 * (2 * (E + 1) + E) + 4 * c.max_rows * N)
+        assert bench.algorithmic_bytes(c) == (want, c.max_rows * N)

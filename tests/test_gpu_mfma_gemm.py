@@ -190,6 +190,36 @@ def test_grouped_gemm_prefill_full_size_sampled(bsq):
         assert np.all(np.abs(got[rows] - want) <= REL_BOUND * S), (g, counts[g])
 
 
+def test_grouped_gemm_decode_full_size_sampled(bsq):
+    """The measured decode GEMM (64 tokens routed top-8 over 256 experts, N =
+    7168, K = 2048): every row of the largest group, the smallest nonempty one
+    and two others, against the oracle."""
+    c = W.grouped_gemm_decode(W.MXFP4)
+    fmt, K, E = c.fmt, c.K, c.num_experts
+    N = c.b_codes.shape[0] // E
+    assert c.max_rows <= 16 * E                   # the decode kernel
+    nblk = K // 32
+    ro, so, ids = c.row_offsets, c.scales_offsets, c.expert_ids
+    out = bsq.grouped_block_scaled_matmul_mfma(
+        dev(c.a_codes), dev(c.a_scales), dev(ro.view(np.int32)), dev(so.view(np.int32)),
+        dev(ids), c.max_rows, c.num_scale_rows, dev(c.b_codes), dev(c.b_scales), E, fmt, K)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    counts = np.diff(ro.astype(np.int64))
+    nonempty = np.nonzero(counts)[0]
+    by_size = nonempty[np.argsort(counts[nonempty], kind="stable")]
+    for g in (by_size[-1], by_size[0], by_size[len(by_size) // 3], by_size[2 * len(by_size) // 3]):
+        lo, hi, e = int(ro[g]), int(ro[g + 1]), int(ids[g])
+        rows = np.arange(lo, hi)
+        sa = mfma16_rows_to_row_major(c.a_scales, int(so[g]) + rows - lo, nblk)
+        brows = e * N + np.arange(N)
+        sb = mfma16_rows_to_row_major(c.b_scales, brows, nblk)
+        qa, qb = c.a_codes[rows], c.b_codes[brows]
+        want = oracle.block_scaled_matmul(qa, sa, qb, sb, fmt, K)
+        S = magnitude_sum(qa, sa, qb, sb, fmt, K)
+        assert np.all(np.abs(got[rows] - want) <= REL_BOUND * S), (g, counts[g])
+
+
 def grouped_case(fmt, G, E, N, K, rows, seed, misaligned=None):
     """Routed activations quantized by the oracle's grouped quantizer (scales
     then mapped into the MFMA layout) and E experts' [N, K] weights (one
@@ -223,18 +253,44 @@ def grouped_case(fmt, G, E, N, K, rows, seed, misaligned=None):
                                           (40, 16, 160, 1024, 900), (9, 4, 256, 7168, 700),
                                           (130, 20, 96, 512, 3000), (200, 7, 48, 256, 9000)])
 def test_grouped_mfma_matches_oracle(bsq, fmt, G, E, N, K, rows):
+    """Groups of more than 16 rows on average: 128-row tiles staged in LDS."""
     d = grouped_case(fmt, G, E, N, K, rows, seed=G + N + K + fmt)
-    out = torch.full((d["max_rows"], N), 7.0, dtype=torch.float32, device="cuda")
+    assert d["max_rows"] > 16 * G
+    check_grouped_run(bsq, fmt, d, G, E, N, K)
+
+
+@pytest.mark.parametrize("fmt", [MXFP4, MXFP8])
+@pytest.mark.parametrize("G,E,N,K,rows", [(64, 16, 300, 2048, 400), (40, 8, 96, 512, 300),
+                                          (100, 12, 512, 1152, 700), (16, 4, 128, 7168, 240),
+                                          (256, 32, 272, 256, 512)])
+def test_grouped_mfma_decode_matches_oracle(bsq, fmt, G, E, N, K, rows):
+    """At most 16 rows per group on average (a decode step): 16-row tiles with
+    the weights streamed to registers.  N = 300, 96 and 272 leave partial
+    column tiles and idle waves; K = 1152 and 256 end in a partial round of K
+    steps; groups of 16 to 40 rows (G = 16) take several row tiles."""
+    d = grouped_case(fmt, G, E, N, K, rows, seed=G + N + K + fmt + 11)
+    assert d["max_rows"] <= 16 * G
+    check_grouped_run(bsq, fmt, d, G, E, N, K)
+
+
+def check_grouped_run(bsq, fmt, d, G, E, N, K, ids=None, max_rows=None, skipped=()):
+    """Run the grouped GEMM on grouped_case data (optionally with other expert
+    ids or a smaller max_rows) into a buffer of 7.0s; every group not in
+    `skipped` must match the oracle within the bound, and every other row keep
+    7.0."""
+    ids = d["ids"] if ids is None else ids
+    max_rows = d["max_rows"] if max_rows is None else max_rows
+    out = torch.full((max_rows, N), 7.0, dtype=torch.float32, device="cuda")
     bsq.grouped_block_scaled_matmul_mfma(
         dev(d["qa"]), dev(d["la"]), dev(d["ro"].view(np.int32)), dev(d["so"].view(np.int32)),
-        dev(d["ids"]), d["max_rows"], d["nsr"], dev(d["qb"]), dev(d["lb"]), E, fmt, K, out=out)
+        dev(ids), max_rows, d["nsr"], dev(d["qb"]), dev(d["lb"]), E, fmt, K, out=out)
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
-    owned = np.zeros(d["max_rows"], bool)
+    owned = np.zeros(max_rows, bool)
     worst = 0.0
     for g in range(G):
-        lo, hi, so, e = int(d["ro"][g]), int(d["ro"][g + 1]), int(d["so"][g]), int(d["ids"][g])
-        if hi == lo:
+        lo, hi, so, e = int(d["ro"][g]), int(d["ro"][g + 1]), int(d["so"][g]), int(ids[g])
+        if hi == lo or g in skipped:
             continue
         owned[lo:hi] = True
         qa, sa = d["qa"][lo:hi], d["sa"][so:so + hi - lo]
@@ -246,6 +302,25 @@ def test_grouped_mfma_matches_oracle(bsq, fmt, G, E, N, K, rows):
         worst = max(worst, float(np.max(err / np.maximum(S, 1e-300))))
     assert np.all(got[~owned] == 7.0)              # rows no group owns are not written
     print(f"format {fmt} G={G} N={N} K={K}: max |err| / sum|ab| = {worst:.3e}")
+
+
+@pytest.mark.parametrize("fmt", [MXFP4, MXFP8])
+def test_grouped_mfma_decode_skips_bad_groups(bsq, fmt):
+    """The decode kernel skips what the 128-row one skips: a group whose scale
+    offset is not a multiple of 16, groups whose expert id is out of range
+    either way, and a group running past max_rows."""
+    G, E, N, K, rows = 30, 5, 80, 512, 150
+    counts = grouped_case(fmt, G, E, N, K, rows, seed=79)["counts"]
+    nonempty = [int(g) for g in np.nonzero(counts)[0] if g >= 1]
+    mis, bad_hi, bad_lo = nonempty[0], nonempty[1], nonempty[2]
+    last = [g for g in nonempty if counts[g] > 1][-1]
+    d = grouped_case(fmt, G, E, N, K, rows, seed=79, misaligned=mis)
+    ids = d["ids"].copy()
+    ids[bad_hi], ids[bad_lo] = E, -1
+    max_rows = int(d["ro"][last]) + int(counts[last]) // 2
+    assert max_rows <= 16 * G
+    check_grouped_run(bsq, fmt, d, G, E, N, K, ids=ids, max_rows=max_rows,
+                      skipped=(mis, bad_hi, bad_lo, last) + tuple(range(last + 1, G)))
 
 
 def test_grouped_mfma_skips_a_misaligned_group(bsq):

@@ -289,6 +289,36 @@ def grouped_gemm_prefill(fmt: int = MXFP4, seed: int = 1203, rows: int = 16384, 
                            rows, nsr, codes(experts * N), b_scales, experts, K)
 
 
+def grouped_gemm_decode(fmt: int = MXFP4, seed: int = 1204, tokens: int = 64, K: int = 2048,
+                        N: int = 7168, experts: int = 256, topk: int = 8) -> GroupedGemmCase:
+    """The decode routing of grouped_mx_decode (each of 64 tokens picks 8 of
+    256 experts uniformly without repeats; 512 routed rows ordered stably by
+    expert; scale rows padded to 128 per expert) with random codes and scale
+    bytes in [120, 134] for the routed activations [512, K] and for the
+    experts' [N, K] weights."""
+    rng = np.random.default_rng(seed)
+    choice = np.stack([rng.choice(experts, topk, replace=False) for _ in range(tokens)])
+    counts = np.bincount(choice.reshape(-1), minlength=experts)
+    ro, so = offsets_from_counts(counts, 128)
+    width = K if fmt == MXFP8 else K // 2
+    rec = ((K // 32 + 15) // 16) * 256
+    rows = tokens * topk
+
+    def codes(n):
+        c = rng.integers(0, 256, (n, width), dtype=np.uint8)
+        if fmt == MXFP8:
+            c[(c & 0x7F) == 0x7F] = 0x38
+        return c
+
+    nsr = int(so[-1])
+    a_scales = rng.integers(120, 135, ((nsr + 15) // 16, rec), dtype=np.uint8)
+    b_scales = rng.integers(120, 135, (experts * ((N + 15) // 16), rec), dtype=np.uint8)
+    name = {MXFP4: "mxfp4", MXFP8: "mxfp8"}[fmt]
+    return GroupedGemmCase(f"mfma_grouped_gemm_{name}_decode_{rows}x{N}x{K}_e{experts}", fmt,
+                           codes(rows), a_scales, ro, so, np.arange(experts, dtype=np.int32),
+                           rows, nsr, codes(experts * N), b_scales, experts, K)
+
+
 def sweep_matrix(bs: int, background: str = "zeros", anchor_bits: int = 0,
                  seed: int = 0) -> np.ndarray:
     """[bs * 65536, bs] BF16 patterns.  Row p * 65536 + h holds pattern h at
