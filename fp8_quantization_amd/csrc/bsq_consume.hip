@@ -648,7 +648,7 @@ mfma_gemm_grouped_kernel(const GemmArgs a, const GroupedGemmArgs g) {
 // It follows the decode entry in the "NVFP4 routing" section of the grouped
 // block-scaled SM100 matmul's "dispatch" page (few rows per expert: a narrow
 // tile on the token side), with the smallest tile the CDNA4 instruction has.
-constexpr int kSkinnyRows = kDecodeTileRows, kSkinnyWaves = 4, kSkinnyJ = 4;
+constexpr int kSkinnyRows = kDecodeTileRows, kSkinnyWaves = 4, kSkinnyJ = 2;
 constexpr int kSkinnyCols = kSkinnyWaves * 16 * kSkinnyJ;
 static_assert(kSkinnyRows == 16 && kSkinnyCols == kDecodeTileCols, "decode tile shape");
 
@@ -724,11 +724,14 @@ __device__ __forceinline__ void gemm_tile_skinny(const GemmTile& d) {
     }
 }
 
-// One workgroup per 16-row tile and 256-column tile.  Measured on the decode
-// routing (512 routed rows over 256 experts, N = 7168, K = 2048): 345 us,
-// against 349-410 us with each workgroup looping over 2 to 28 column tiles
-// (one group lookup for several tiles), 376 us with non-temporal B loads,
-// and 385 us for the 128-row kernel.
+// One workgroup per 16-row tile and 128-column tile (4 waves of J = 2 tiles
+// of c).  Measured on the decode routing (512 routed rows over 256 experts,
+// N = 7168, K = 2048): 341 us, against 345 / 361 / 379 us with J = 4 / 1 / 8
+// and 343 / 349 us with 8 waves of J = 2 / 4; 345-410 us with each workgroup
+// looping over several column tiles (one group lookup for several tiles);
+// 376 us with non-temporal B loads; 390 us with the next round's loads issued
+// before this round's products (two register sets: one wave per SIMD); and
+// 385 us for the 128-row kernel.
 template <int FMT>
 __global__ void __launch_bounds__(64 * kSkinnyWaves)
 mfma_gemm_grouped_skinny_kernel(const GemmArgs a, const GroupedGemmArgs g) {

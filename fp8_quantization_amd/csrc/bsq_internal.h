@@ -114,7 +114,7 @@ hipError_t launch_mfma_matmul(int fmt, const GemmArgs& a, hipStream_t stream);
 // Grouped per-expert GEMM: A rows grouped by row_offsets (scale rows by
 // scales_offsets), B = num_experts stacked [N, K] operands; GemmArgs.M unused.
 // Tile of the grouped GEMM's decode form: rows of one group x columns of c.
-constexpr int kDecodeTileRows = 16, kDecodeTileCols = 256;
+constexpr int kDecodeTileRows = 16, kDecodeTileCols = 128;
 struct GroupedGemmArgs {
     const uint32_t* row_offsets;     // [num_groups + 1]
     const uint32_t* scales_offsets;  // [num_groups + 1]
