@@ -648,7 +648,7 @@ mfma_gemm_grouped_kernel(const GemmArgs a, const GroupedGemmArgs g) {
 // It follows the decode entry in the "NVFP4 routing" section of the grouped
 // block-scaled SM100 matmul's "dispatch" page (few rows per expert: a narrow
 // tile on the token side), with the smallest tile the CDNA4 instruction has.
-constexpr int kSkinnyRows = kDecodeTileRows, kSkinnyWaves = 4, kSkinnyJ = 2;
+constexpr int kSkinnyRows = kDecodeTileRows, kSkinnyWaves = 4, kSkinnyJ = 2, kSkinnyRecs = 1;
 constexpr int kSkinnyCols = kSkinnyWaves * 16 * kSkinnyJ;
 static_assert(kSkinnyRows == 16 && kSkinnyCols == kDecodeTileCols, "decode tile shape");
 
@@ -661,17 +661,21 @@ __device__ __forceinline__ mfma_v4f mfma_opsel(const mfma_v8i& fa, const mfma_v8
 }
 
 // One K step S (of the round's four) of the wave's J tiles, if it exists.
+// The products of one K step of the wave's J tiles; S is the step's place in
+// its 512-element scale record (the instruction's scale byte select).
 template <int FMT, int J, int S>
-__device__ __forceinline__ void skinny_step(const mfma_v8i (&fa)[4], const mfma_v8i (&fb)[4][J],
+__device__ __forceinline__ void skinny_step(const mfma_v8i& fa, const mfma_v8i (&fb)[J],
                                             mfma_v4f (&acc)[J], uint32_t sa,
-                                            const uint32_t (&sb)[J], bool live) {
-    if (!live) return;
+                                            const uint32_t (&sb)[J]) {
 #pragma unroll
-    for (int j = 0; j < J; ++j) acc[j] = mfma_opsel<FMT, S>(fa[S], fb[S][j], acc[j], sa, sb[j]);
+    for (int j = 0; j < J; ++j) acc[j] = mfma_opsel<FMT, S>(fa, fb[j], acc[j], sa, sb[j]);
 }
 
-template <int FMT, int J>
+// A wave's J 16 x 16 tiles of c over all of K, in rounds of R scale records
+// (4 R K steps): all of a round's loads are issued, then its products.
+template <int FMT, int J, int R>
 __device__ __forceinline__ void gemm_tile_skinny(const GemmTile& d) {
+    constexpr int KU = 4 * R;                                // K steps per round
     const int lane = (int)(threadIdx.x & 63);
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int cb = 16 * J * wave;                            // the wave's first column
@@ -693,25 +697,36 @@ __device__ __forceinline__ void gemm_tile_skinny(const GemmTile& d) {
     for (int j = 0; j < J; ++j) acc[j] = (mfma_v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
     const int nk = d.K / 128;                                // K steps (K is a multiple of 128)
-    for (int k4 = 0; k4 < nk; k4 += 4) {
-        const int rec = (k4 >> 2) * 256;                     // the round's 512-element record
-        const uint32_t sa = *reinterpret_cast<const uint32_t*>(asr + rec);
-        uint32_t sb[J];
+    for (int k0 = 0; k0 < nk; k0 += KU) {
+        uint32_t sa[R], sb[R][J];
 #pragma unroll
-        for (int j = 0; j < J; ++j) sb[j] = *reinterpret_cast<const uint32_t*>(bsr[j] + rec);
-        mfma_v8i fa[4], fb[4][J];
+        for (int r = 0; r < R; ++r) {                        // the round's scale records
+            sa[r] = 0u;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const bool live = k4 + st < nk;
-            fa[st] = load_fragment<FMT>(arow, (k4 + st) * 128, fg, live);
+            for (int j = 0; j < J; ++j) sb[r][j] = 0u;
+            if (k0 + 4 * r >= nk) continue;
+            const int rec = ((k0 >> 2) + r) * 256;
+            sa[r] = *reinterpret_cast<const uint32_t*>(asr + rec);
+#pragma unroll
+            for (int j = 0; j < J; ++j) sb[r][j] = *reinterpret_cast<const uint32_t*>(bsr[j] + rec);
+        }
+        mfma_v8i fa[KU], fb[KU][J];
+#pragma unroll
+        for (int st = 0; st < KU; ++st) {
+            const bool live = k0 + st < nk;
+            fa[st] = load_fragment<FMT>(arow, (k0 + st) * 128, fg, live);
 #pragma unroll
             for (int j = 0; j < J; ++j)
-                fb[st][j] = load_fragment<FMT>(brow[j], (k4 + st) * 128, fg, live);
+                fb[st][j] = load_fragment<FMT>(brow[j], (k0 + st) * 128, fg, live);
         }
-        skinny_step<FMT, J, 0>(fa, fb, acc, sa, sb, true);
-        skinny_step<FMT, J, 1>(fa, fb, acc, sa, sb, k4 + 1 < nk);
-        skinny_step<FMT, J, 2>(fa, fb, acc, sa, sb, k4 + 2 < nk);
-        skinny_step<FMT, J, 3>(fa, fb, acc, sa, sb, k4 + 3 < nk);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int k = k0 + 4 * r;
+            if (k < nk) skinny_step<FMT, J, 0>(fa[4 * r], fb[4 * r], acc, sa[r], sb[r]);
+            if (k + 1 < nk) skinny_step<FMT, J, 1>(fa[4 * r + 1], fb[4 * r + 1], acc, sa[r], sb[r]);
+            if (k + 2 < nk) skinny_step<FMT, J, 2>(fa[4 * r + 2], fb[4 * r + 2], acc, sa[r], sb[r]);
+            if (k + 3 < nk) skinny_step<FMT, J, 3>(fa[4 * r + 3], fb[4 * r + 3], acc, sa[r], sb[r]);
+        }
     }
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -730,14 +745,15 @@ __device__ __forceinline__ void gemm_tile_skinny(const GemmTile& d) {
 // and 343 / 349 us with 8 waves of J = 2 / 4; 345-410 us with each workgroup
 // looping over several column tiles (one group lookup for several tiles);
 // 376 us with non-temporal B loads; 390 us with the next round's loads issued
-// before this round's products (two register sets: one wave per SIMD); and
-// 385 us for the 128-row kernel.
+// before this round's products (two register sets: one wave per SIMD);
+// rounds of 2 scale records 339 us (J = 2) and 351 / 371 us (J = 1, 2 / 4
+// records), so longer rounds do not pay; and 385 us for the 128-row kernel.
 template <int FMT>
 __global__ void __launch_bounds__(64 * kSkinnyWaves)
 mfma_gemm_grouped_skinny_kernel(const GemmArgs a, const GroupedGemmArgs g) {
     GemmTile d;
     if (!grouped_desc<kSkinnyRows, kSkinnyCols>(a, g, d)) return;
-    gemm_tile_skinny<FMT, kSkinnyJ>(d);
+    gemm_tile_skinny<FMT, kSkinnyJ, kSkinnyRecs>(d);
 }
 
 template <int FMT, class Cfg>
