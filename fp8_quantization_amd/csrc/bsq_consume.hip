@@ -638,17 +638,16 @@ mfma_gemm_grouped_kernel(const GemmArgs a, const GroupedGemmArgs g) {
 //  * a workgroup takes 16 rows of one group (the instruction's smallest M)
 //    and kSkinnyWaves x 16 J columns of c; each wave owns J 16 x 16 tiles of
 //    c over the whole of K;
-//  * no LDS: every lane loads its own A and B fragments from global memory
-//    straight into registers, 512 elements of K (four K steps, one scale
-//    dword per operand) per round, so a wave keeps 4 (J + 1) 16-byte loads
-//    (MXFP4) or twice that (MXFP8) in flight, and the waves sharing a SIMD
-//    cover each other's latency;
+//  * each wave streams its own B rows through its own LDS slice, 512
+//    elements of K (four K steps, one scale dword per operand) per round,
+//    with no barrier; A fragments go straight to registers; the waves
+//    sharing a CU cover each other's latency;
 //  * rows past the group load its last row and columns past N the last B
 //    row (their outputs are never stored), so every load is in bounds.
 // It follows the decode entry in the "NVFP4 routing" section of the grouped
 // block-scaled SM100 matmul's "dispatch" page (few rows per expert: a narrow
 // tile on the token side), with the smallest tile the CDNA4 instruction has.
-constexpr int kSkinnyRows = kDecodeTileRows, kSkinnyWaves = 4, kSkinnyJ = 2, kSkinnyRecs = 1;
+constexpr int kSkinnyRows = kDecodeTileRows, kSkinnyWaves = 4, kSkinnyJ = 2;
 constexpr int kSkinnyCols = kSkinnyWaves * 16 * kSkinnyJ;
 static_assert(kSkinnyRows == 16 && kSkinnyCols == kDecodeTileCols, "decode tile shape");
 
@@ -671,62 +670,101 @@ __device__ __forceinline__ void skinny_step(const mfma_v8i& fa, const mfma_v8i (
     for (int j = 0; j < J; ++j) acc[j] = mfma_opsel<FMT, S>(fa, fb[j], acc[j], sa, sb[j]);
 }
 
-// A wave's J 16 x 16 tiles of c over all of K, in rounds of R scale records
-// (4 R K steps): all of a round's loads are issued, then its products.
-template <int FMT, int J, int R>
-__device__ __forceinline__ void gemm_tile_skinny(const GemmTile& d) {
-    constexpr int KU = 4 * R;                                // K steps per round
+// A wave's J 16 x 16 tiles of c over all of K, in rounds of 4 K steps (one
+// 512-element scale record).  Each round's B rows (16 J rows) go to the
+// wave's own LDS slice with direct loads, 1 KiB per instruction as whole
+// 16-byte pieces of kRowBytes-byte row segments (4 rows per instruction for
+// E2M1, 2 for E4M3), so every request covers whole cache lines; piece p of
+// row r is stored at slot p ^ (r % kPieces), so the fragment reads of 16 rows
+// fall in distinct banks.  A fragments (16 rows, shared by every wave and
+// read from L2) go straight to registers.  Only the wave itself reads its
+// slice, so there is no barrier: the compiler's wait for the direct loads
+// precedes the reads, and the reads are complete before the next round's
+// loads overwrite the slice.
+template <int FMT, int J>
+__device__ __forceinline__ void gemm_tile_skinny(const GemmTile& d, uint8_t* stage) {
+    constexpr int kRowBytes = FMT == 1 ? 512 : 256;          // a row's bytes per round
+    constexpr int kPieces = kRowBytes / 16;
+    constexpr int kRows = 16 * J;
+    constexpr int kRowsPerInst = 64 / kPieces;
+    constexpr int kInsts = kRows / kRowsPerInst;
+    constexpr int kWaveBytes = kRows * kRowBytes;
     const int lane = (int)(threadIdx.x & 63);
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int cb = 16 * J * wave;                            // the wave's first column
-    if (cb >= d.c_cols) return;                              // wave-uniform: nothing here
+    const int cb = 16 * J * wave;
+    if (cb >= d.c_cols) return;
     const int fr = lane & 15, fg = lane >> 4;
     const int64_t ra = fr < d.a_rows ? fr : d.a_rows - 1;
     const uint8_t* arow = d.a + ra * d.lda_q;
-    const uint8_t* asr = d.as + 4 * lane;                    // the tile's one A row group
-    const uint8_t* brow[J];
+    const uint8_t* asr = d.as + 4 * lane;
     const uint8_t* bsr[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-        const int64_t rb = cb + 16 * j + fr, gb = (cb + 16 * j) >> 4;
-        brow[j] = d.b + (rb < d.b_rows ? rb : d.b_rows - 1) * d.ldb_q;
+        const int64_t gb = (cb + 16 * j) >> 4;
         bsr[j] = d.bs + (gb < d.b_groups ? gb : d.b_groups - 1) * d.ldb_s + 4 * lane;
     }
+    // this lane's row and piece in each direct load of a round
+    const int lrow = lane / kPieces, lslot = lane % kPieces;
+    const uint8_t* src[kInsts];
+    int piece_off[kInsts];
+#pragma unroll
+    for (int i = 0; i < kInsts; ++i) {
+        const int r = i * kRowsPerInst + lrow;                // row within the wave's rows
+        const int64_t rb = cb + r < d.b_rows ? cb + r : d.b_rows - 1;
+        src[i] = d.b + rb * d.ldb_q;
+        piece_off[i] = 16 * (lslot ^ (r % kPieces));
+    }
+    uint8_t* slice = stage + wave * kWaveBytes;
+    const int row_bytes = FMT == 1 ? d.K : d.K / 2;
     mfma_v4f acc[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) acc[j] = (mfma_v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int nk = d.K / 128;                                // K steps (K is a multiple of 128)
-    for (int k0 = 0; k0 < nk; k0 += KU) {
-        uint32_t sa[R], sb[R][J];
+    const int nk = d.K / 128;
+    for (int k0 = 0; k0 < nk; k0 += 4) {
+        // reads of the previous round are done before their slots are refilled
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int rb0 = k0 * (kRowBytes / 4);                 // the round's first byte in a row
 #pragma unroll
-        for (int r = 0; r < R; ++r) {                        // the round's scale records
-            sa[r] = 0u;
-#pragma unroll
-            for (int j = 0; j < J; ++j) sb[r][j] = 0u;
-            if (k0 + 4 * r >= nk) continue;
-            const int rec = ((k0 >> 2) + r) * 256;
-            sa[r] = *reinterpret_cast<const uint32_t*>(asr + rec);
-#pragma unroll
-            for (int j = 0; j < J; ++j) sb[r][j] = *reinterpret_cast<const uint32_t*>(bsr[j] + rec);
+        for (int i = 0; i < kInsts; ++i) {
+            int off = rb0 + piece_off[i];
+            off = off < row_bytes ? off : 0;                  // past K (a partial round): any in-row bytes
+            __builtin_amdgcn_global_load_lds(const_cast<uint8_t*>(src[i] + off), slice + i * 1024, 16,
+                                             0, 0);
         }
-        mfma_v8i fa[KU], fb[KU][J];
+        const int rec = (k0 >> 2) * 256;
+        const uint32_t sa = *reinterpret_cast<const uint32_t*>(asr + rec);
+        uint32_t sb[J];
 #pragma unroll
-        for (int st = 0; st < KU; ++st) {
-            const bool live = k0 + st < nk;
-            fa[st] = load_fragment<FMT>(arow, (k0 + st) * 128, fg, live);
+        for (int j = 0; j < J; ++j) sb[j] = *reinterpret_cast<const uint32_t*>(bsr[j] + rec);
+        mfma_v8i fa[4];
 #pragma unroll
-            for (int j = 0; j < J; ++j)
-                fb[st][j] = load_fragment<FMT>(brow[j], (k0 + st) * 128, fg, live);
-        }
+        for (int st = 0; st < 4; ++st) fa[st] = load_fragment<FMT>(arow, (k0 + st) * 128, fg, k0 + st < nk);
+        auto frag = [&](int st, int j) {
+            const int r = 16 * j + fr;
+            const uint8_t* row = slice + r * kRowBytes;
+            mfma_v8i v;
+            if constexpr (FMT == 1) {
+                const int p0 = 8 * st + fg, p1 = 8 * st + 4 + fg;
+                const int4 lo = *reinterpret_cast<const int4*>(row + 16 * (p0 ^ (r % kPieces)));
+                const int4 hi = *reinterpret_cast<const int4*>(row + 16 * (p1 ^ (r % kPieces)));
+                v = (mfma_v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            } else {
+                const int p = 4 * st + fg;
+                const int4 q = *reinterpret_cast<const int4*>(row + 16 * (p ^ (r % kPieces)));
+                v = (mfma_v8i){q.x, q.y, q.z, q.w, 0, 0, 0, 0};
+            }
+            return v;
+        };
+        mfma_v8i fb[4][J];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int k = k0 + 4 * r;
-            if (k < nk) skinny_step<FMT, J, 0>(fa[4 * r], fb[4 * r], acc, sa[r], sb[r]);
-            if (k + 1 < nk) skinny_step<FMT, J, 1>(fa[4 * r + 1], fb[4 * r + 1], acc, sa[r], sb[r]);
-            if (k + 2 < nk) skinny_step<FMT, J, 2>(fa[4 * r + 2], fb[4 * r + 2], acc, sa[r], sb[r]);
-            if (k + 3 < nk) skinny_step<FMT, J, 3>(fa[4 * r + 3], fb[4 * r + 3], acc, sa[r], sb[r]);
-        }
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int j = 0; j < J; ++j) fb[st][j] = frag(st, j);
+        skinny_step<FMT, J, 0>(fa[0], fb[0], acc, sa, sb);
+        if (k0 + 1 < nk) skinny_step<FMT, J, 1>(fa[1], fb[1], acc, sa, sb);
+        if (k0 + 2 < nk) skinny_step<FMT, J, 2>(fa[2], fb[2], acc, sa, sb);
+        if (k0 + 3 < nk) skinny_step<FMT, J, 3>(fa[3], fb[3], acc, sa, sb);
     }
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -741,19 +779,23 @@ __device__ __forceinline__ void gemm_tile_skinny(const GemmTile& d) {
 
 // One workgroup per 16-row tile and 128-column tile (4 waves of J = 2 tiles
 // of c).  Measured on the decode routing (512 routed rows over 256 experts,
-// N = 7168, K = 2048): 341 us, against 345 / 361 / 379 us with J = 4 / 1 / 8
-// and 343 / 349 us with 8 waves of J = 2 / 4; 345-410 us with each workgroup
-// looping over several column tiles (one group lookup for several tiles);
-// 376 us with non-temporal B loads; 390 us with the next round's loads issued
-// before this round's products (two register sets: one wave per SIMD);
-// rounds of 2 scale records 339 us (J = 2) and 351 / 371 us (J = 1, 2 / 4
-// records), so longer rounds do not pay; and 385 us for the 128-row kernel.
+// N = 7168, K = 2048), MXFP4: 309 us, against 341 us for the same tiles with
+// every fragment loaded straight from global memory into registers (each
+// load then covers 64 bytes of each of 16 rows, so every cache line is
+// requested twice), and 385 us for the 128-row kernel.  With the register
+// form, other shapes and schedules measured no better: J = 1 / 4 / 8, 8
+// waves, rounds of 8 or 16 K steps, a workgroup looping over several column
+// tiles, non-temporal loads, and the next round's loads issued before this
+// round's products (two register sets: one wave per SIMD).  With the LDS
+// form, J = 1 (4 or 8 waves) took 315 us and 2 waves of J = 2 309 us.
 template <int FMT>
 __global__ void __launch_bounds__(64 * kSkinnyWaves)
 mfma_gemm_grouped_skinny_kernel(const GemmArgs a, const GroupedGemmArgs g) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kSkinnyWaves * 16 * kSkinnyJ *
+                                                          (FMT == 1 ? 512 : 256)];
     GemmTile d;
     if (!grouped_desc<kSkinnyRows, kSkinnyCols>(a, g, d)) return;
-    gemm_tile_skinny<FMT, kSkinnyJ, kSkinnyRecs>(d);
+    gemm_tile_skinny<FMT, kSkinnyJ>(d, stage);
 }
 
 template <int FMT, class Cfg>

@@ -124,7 +124,7 @@ struct GroupedGemmArgs {
     int64_t max_rows;                // rows of A codes and of c
     int64_t num_scale_rows;          // scale rows of A
     int64_t m_tiles;                 // grid bound on row tiles over all groups
-    int32_t decode;                  // 1: 16-row tiles, B streamed to registers (few rows
+    int32_t decode;                  // 1: 16-row tiles, B streamed through LDS (few rows
                                      // per group); 0: 128-row tiles staged through LDS
 };
 hipError_t launch_mfma_grouped_matmul(int fmt, const GemmArgs& a, const GroupedGemmArgs& g,

@@ -305,8 +305,8 @@ int block_scaled_matmul_mfma(int format, int block_size, int scale_layout,
  * stay on the device), after the decode / prefill split in the "NVFP4
  * routing" section of the grouped block-scaled SM100 matmul's "dispatch"
  * page: at most 16 rows per group on average
- * (decode) takes 16-row tiles that stream each expert's weights into
- * registers; more takes 128-row tiles staged through LDS.  Both give the
+ * (decode) takes 16-row tiles that stream each expert's weights through
+ * each wave's own LDS slice; more takes 128-row tiles staged through LDS.  Both give the
  * same results within the stated bound.
  *
  *   format, block_size, scale_layout   as for block_scaled_matmul_mfma.

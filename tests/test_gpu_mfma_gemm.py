@@ -265,7 +265,7 @@ def test_grouped_mfma_matches_oracle(bsq, fmt, G, E, N, K, rows):
                                           (256, 32, 272, 256, 512)])
 def test_grouped_mfma_decode_matches_oracle(bsq, fmt, G, E, N, K, rows):
     """At most 16 rows per group on average (a decode step): 16-row tiles with
-    the weights streamed to registers.  N = 300, 96 and 272 leave partial
+    the weights streamed through LDS.  N = 300, 96 and 272 leave partial
     column tiles and idle waves; K = 1152 and 256 end in a partial round of K
     steps; groups of 16 to 40 rows (G = 16) take several row tiles."""
     d = grouped_case(fmt, G, E, N, K, rows, seed=G + N + K + fmt + 11)
