@@ -246,16 +246,20 @@ int tsf_geometry(bsq::KernelArgs& a, int64_t* blocks, int* waves_per_block,
     return BSQ_OK;
 }
 
-// Launch geometry: one wave per tile, four waves per workgroup.
-//  * Dense, large: tiles of 2 chunks (1024 elements: two 16-byte loads per lane).
-//    Many short waves keep the most loads in flight across the chip and
-//    leave the smallest tail; 1 or 4 chunks per wave, and a persistent grid
-//    walking the tiles, measured slower.
-//  * Grouped, large (more than 2^22 routed elements, bandwidth-bound): tiles
-//    of 4 chunks, amortising each wave's group search and (NVFP4) the
-//    expert's reciprocal table.  On the 16384 x 7168 prefill: NVFP4 49.7 us
-//    against 51.8 with 2 chunks and 51.6 with 8; MXFP8 and MXFP4 equal
-//    within noise at 2, 4 and 8.
+// Launch geometry: one wave per tile, four waves per workgroup.  Chunks per
+// tile, as measured on one box (the store policies of bsq_kernels.hip in
+// place; a persistent grid walking the tiles measured slower everywhere):
+//  * Dense MXFP8, large: 2 chunks (1024 elements, two 16-byte loads per
+//    lane).  [8192, 7168]: 29.2 us against 29.9 with 4; earlier, with the
+//    same stores, 31.0 against 35.5 with 1.
+//  * Dense MXFP4 / NVFP4, large (FP4 codes stored write-through): 4 chunks.
+//    [16384, 7168]: MXFP4 45.3 us against 46.0-46.3 with 2 and 46.0 with 8;
+//    NVFP4 46.2-46.6 against 47.7-48.2 with 2 and 47.7 with 8.
+//  * Grouped, large (more than 2^22 routed elements): 4 chunks, which also
+//    amortise each wave's group search and (NVFP4) the expert's reciprocal
+//    table.  16384 x 7168 prefill: NVFP4 49.5-49.8 us against 53.3-53.6 with
+//    2 and 49.7-50.0 with 8; MXFP4 45.4-45.6 against 48.5 with 2 and 46.6
+//    with 8; MXFP8 equal within noise at 2, 4 and 8.
 //  * Small (at most 2^22 elements, latency-bound), dense or grouped: tiles of
 //    1 chunk, for the most parallel waves.  Timed from a replayed HIP graph:
 //    the 512 routed rows x 2048 decode gather 3.07 us against 3.10 with 2
@@ -263,7 +267,7 @@ int tsf_geometry(bsq::KernelArgs& a, int64_t* blocks, int* waves_per_block,
 //    2.61.
 int launch(int format, bool grouped, bsq::KernelArgs& a, hipStream_t stream) {
     const bool small = (double)a.rows * (double)a.K <= (double)(1 << 22);
-    int u = small ? 1 : grouped ? 4 : 2;
+    int u = small ? 1 : (grouped || format != BSQ_MXFP8) ? 4 : 2;
     if (tile_knob()) u = tile_knob();
     int64_t blocks = 0;
     if (st_geometry(a, u, &blocks) != BSQ_OK) return BSQ_ERR_INVALID_ARG;

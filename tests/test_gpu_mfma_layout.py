@@ -39,7 +39,8 @@ def layout_buffer(bsq, fmt, rows, K, extra=0):
 @pytest.mark.parametrize("fmt", [MXFP4, MXFP8])
 @pytest.mark.parametrize("M,K,extra", [(1, 32, 0), (16, 512, 0), (37, 1056, 0), (300, 2048, 64),
                                        (129, 7168, 0), (5, 544, 256),
-                                       # over 2^22 elements: tiles of 2 chunks, ragged last tile
+                                       # over 2^22 elements: tiles of 2 (MXFP8) or 4 (MXFP4)
+                                       # chunks, ragged last tile
                                        (1000, 4544, 0), (1003, 4608, 32)])
 def test_dense_quantize_writes_the_layout(bsq, fmt, M, K, extra):
     x = W.random_bf16((M, K), seed=M + K + fmt, scale_log2_range=(-30, 30), special_frac=0.002)

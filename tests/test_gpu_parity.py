@@ -184,11 +184,11 @@ def test_ragged_shapes_padded_strides(bsq, fmt, M, K):
                          ids=["mxfp4", "mxfp8", "nvfp4"])
 @pytest.mark.parametrize("M,K", [(1000, 4544), (1001, 4608), (600, 7200)])
 def test_dense_large_problem_path(bsq, fmt, M, K):
-    """Over 2^22 elements dense rows go in tiles of 2 chunks (512 elements
-    each), and FP4 codes take the write-through stores.  K = 4544 is 9 chunks,
-    the last holding 448 elements, so every row ends in a half-empty tile with
-    a partial chunk; K = 4608 is 9 whole chunks; K = 7200 is 14 whole chunks and
-    a 32-element one.  Strides are padded."""
+    """Over 2^22 elements dense rows go in tiles of 2 (MXFP8) or 4 (FP4)
+    chunks of 512 elements, and FP4 codes take the write-through stores.
+    K = 4544 is 9 chunks, the last holding 448 elements, so every row ends in
+    a partly empty tile with a partial chunk; K = 4608 is 9 whole chunks;
+    K = 7200 is 14 whole chunks and a 32-element one.  Strides are padded."""
     assert M * K > (1 << 22)
     x = W.random_bf16((M, K), seed=M + K + 100 * fmt, scale_log2_range=(-20, 20),
                       special_frac=0.001)
