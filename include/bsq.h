@@ -304,7 +304,7 @@ int block_scaled_matmul_mfma(int format, int block_size, int scale_layout,
  * Two kernels, chosen on the host from max_rows / num_groups (the offsets
  * stay on the device), after the decode / prefill split in the "NVFP4
  * routing" section of the grouped block-scaled SM100 matmul's "dispatch"
- * page: at most 16 rows per group on average
+ * page: at most 8 rows per group on average
  * (decode) takes 16-row tiles that stream each expert's weights through
  * each wave's own LDS slice; more takes 128-row tiles staged through LDS.  Both give the
  * same results within the stated bound.

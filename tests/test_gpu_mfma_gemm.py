@@ -197,7 +197,7 @@ def test_grouped_gemm_decode_full_size_sampled(bsq):
     c = W.grouped_gemm_decode(W.MXFP4)
     fmt, K, E = c.fmt, c.K, c.num_experts
     N = c.b_codes.shape[0] // E
-    assert c.max_rows <= 16 * E                   # the decode kernel
+    assert c.max_rows <= 8 * E                    # the decode kernel
     nblk = K // 32
     ro, so, ids = c.row_offsets, c.scales_offsets, c.expert_ids
     out = bsq.grouped_block_scaled_matmul_mfma(
@@ -253,23 +253,23 @@ def grouped_case(fmt, G, E, N, K, rows, seed, misaligned=None):
                                           (40, 16, 160, 1024, 900), (9, 4, 256, 7168, 700),
                                           (130, 20, 96, 512, 3000), (200, 7, 48, 256, 9000)])
 def test_grouped_mfma_matches_oracle(bsq, fmt, G, E, N, K, rows):
-    """Groups of more than 16 rows on average: 128-row tiles staged in LDS."""
+    """Groups of more than 8 rows on average: 128-row tiles staged in LDS."""
     d = grouped_case(fmt, G, E, N, K, rows, seed=G + N + K + fmt)
-    assert d["max_rows"] > 16 * G
+    assert d["max_rows"] > 8 * G
     check_grouped_run(bsq, fmt, d, G, E, N, K)
 
 
 @pytest.mark.parametrize("fmt", [MXFP4, MXFP8])
 @pytest.mark.parametrize("G,E,N,K,rows", [(64, 16, 300, 2048, 400), (40, 8, 96, 512, 300),
-                                          (100, 12, 512, 1152, 700), (16, 4, 128, 7168, 240),
+                                          (100, 12, 512, 1152, 700), (32, 4, 128, 7168, 240),
                                           (256, 32, 272, 256, 512)])
 def test_grouped_mfma_decode_matches_oracle(bsq, fmt, G, E, N, K, rows):
-    """At most 16 rows per group on average (a decode step): 16-row tiles with
+    """At most 8 rows per group on average (a decode step): 16-row tiles with
     the weights streamed through LDS.  N = 300, 96 and 272 leave partial
     column tiles and idle waves; K = 1152 and 256 end in a partial round of K
-    steps; groups of 16 to 40 rows (G = 16) take several row tiles."""
+    steps; groups of 17 to 23 rows (G = 32) take several row tiles."""
     d = grouped_case(fmt, G, E, N, K, rows, seed=G + N + K + fmt + 11)
-    assert d["max_rows"] <= 16 * G
+    assert d["max_rows"] <= 8 * G
     check_grouped_run(bsq, fmt, d, G, E, N, K)
 
 
@@ -318,7 +318,7 @@ def test_grouped_mfma_decode_skips_bad_groups(bsq, fmt):
     ids = d["ids"].copy()
     ids[bad_hi], ids[bad_lo] = E, -1
     max_rows = int(d["ro"][last]) + int(counts[last]) // 2
-    assert max_rows <= 16 * G
+    assert max_rows <= 8 * G
     check_grouped_run(bsq, fmt, d, G, E, N, K, ids=ids, max_rows=max_rows,
                       skipped=(mis, bad_hi, bad_lo, last) + tuple(range(last + 1, G)))
 
