@@ -66,11 +66,19 @@ int tile_knob() {
 //   BSQ_MFMA_TILED           matrix-core GEMM: two LDS stage buffers, 256 x 256 tiles where
 //                            they fill the chip and 128 x 128 otherwise (default); 2 one wave
 //                            per 16 x 16 tile (dense); 3 128 x 128 tiles, three stage
-//                            buffers; 4 128 x 128 tiles (dense); 5 / 6 the grouped
-//                            form's decode (16-row) / prefill (128-row) kernel whatever
-//                            the rows per group
+//                            buffers; 4 128 x 128 tiles (dense)
 int mfma_tiled_knob() {
     static const int v = env_knob("BSQ_MFMA_TILED");
+    return v;
+}
+//   BSQ_GROUPED_TILE_ROWS    grouped matrix-core GEMM: rows per tile, whatever the rows per
+//                            group: 16 or 32 (B streamed through each wave's LDS) or 128
+//                            (tiles staged through LDS)
+int grouped_tile_rows_knob() {
+    static const int v = [] {
+        const int r = env_knob("BSQ_GROUPED_TILE_ROWS");
+        return (r == 16 || r == 32 || r == 128) ? r : 0;
+    }();
     return v;
 }
 //   BSQ_TSF_WAVES_PER_CU     tensor-scale reduction: resident waves per CU
@@ -653,15 +661,18 @@ int grouped_block_scaled_matmul_mfma(int format, int block_size, int scale_layou
     g.num_experts = (int32_t)num_experts;
     g.max_rows = max_rows;
     g.num_scale_rows = num_scale_rows;
-    // Few rows per group (at most 8 on average over max_rows, as in a decode
-    // step): 16-row tiles with the weights streamed through each wave's LDS.
-    // Otherwise 128-row tiles staged through LDS.  Measured on 256 experts,
-    // N = 512, K = 7168 (MXFP4), decode against 128-row form: 90 / 108 us at
-    // 4 rows per expert, 104 / 110 at 8, 124 / 113 at 16, 188 / 117 at 32.
-    const int knob = mfma_tiled_knob();
-    g.decode = knob == 5 || (knob != 6 && max_rows <= 8 * num_groups);
-    const int64_t tile_m = g.decode ? bsq::kDecodeTileRows : 128;
-    const int64_t tile_n = g.decode ? bsq::kDecodeTileCols : 128;
+    // Rows per tile from the rows per group on average (max_rows / num_groups;
+    // the offsets stay on the device).  Few rows per group, as in a decode
+    // step, take 16- or 32-row tiles with the weights streamed through each
+    // wave's LDS; more take 128-row tiles staged through LDS.  Measured on 256
+    // experts, N = 512, K = 7168 (MXFP4), 16 / 32 / 64 / 128-row tiles: at 4
+    // rows per expert 90 / 92 / 106 / 117 us; at 8, 103 / 97 / 114 / 108; at
+    // 16, 125 / 108 / 117 / 119; at 32, 190 / 155 / 148 / 124; at 64, 339 /
+    // 229 / 224 / 130.
+    int tile_m = max_rows <= 4 * num_groups ? 16 : max_rows <= 16 * num_groups ? 32 : 128;
+    if (grouped_tile_rows_knob()) tile_m = grouped_tile_rows_knob();
+    g.row_blocks = tile_m < 128 ? tile_m / 16 : 0;
+    const int64_t tile_n = g.row_blocks ? bsq::kDecodeTileCols : 128;
     g.m_tiles = (max_rows + tile_m - 1) / tile_m + num_groups;  // each group adds at most one
                                                                 // partial tile
     if (g.m_tiles > 0x7FFFFFFFLL || (N + tile_n - 1) / tile_n > 65535)

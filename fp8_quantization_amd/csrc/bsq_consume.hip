@@ -647,9 +647,9 @@ mfma_gemm_grouped_kernel(const GemmArgs a, const GroupedGemmArgs g) {
 // It follows the decode entry in the "NVFP4 routing" section of the grouped
 // block-scaled SM100 matmul's "dispatch" page (few rows per expert: a narrow
 // tile on the token side), with the smallest tile the CDNA4 instruction has.
-constexpr int kSkinnyRows = kDecodeTileRows, kSkinnyWaves = 4, kSkinnyJ = 2;
+constexpr int kSkinnyWaves = 4, kSkinnyJ = 2;
 constexpr int kSkinnyCols = kSkinnyWaves * 16 * kSkinnyJ;
-static_assert(kSkinnyRows == 16 && kSkinnyCols == kDecodeTileCols, "decode tile shape");
+static_assert(kSkinnyCols == kDecodeTileCols, "decode tile shape");
 
 template <int FMT, int S>
 __device__ __forceinline__ mfma_v4f mfma_opsel(const mfma_v8i& fa, const mfma_v8i& fb,
@@ -660,28 +660,33 @@ __device__ __forceinline__ mfma_v4f mfma_opsel(const mfma_v8i& fa, const mfma_v8
 }
 
 // One K step S (of the round's four) of the wave's J tiles, if it exists.
-// The products of one K step of the wave's J tiles; S is the step's place in
-// its 512-element scale record (the instruction's scale byte select).
-template <int FMT, int J, int S>
-__device__ __forceinline__ void skinny_step(const mfma_v8i& fa, const mfma_v8i (&fb)[J],
-                                            mfma_v4f (&acc)[J], uint32_t sa,
+// The products of one K step of the wave's MB x J tiles; S is the step's
+// place in its 512-element scale record (the instruction's scale byte select).
+template <int FMT, int J, int MB, int S>
+__device__ __forceinline__ void skinny_step(const mfma_v8i (&fa)[MB], const mfma_v8i (&fb)[J],
+                                            mfma_v4f (&acc)[MB][J], const uint32_t (&sa)[MB],
                                             const uint32_t (&sb)[J]) {
 #pragma unroll
-    for (int j = 0; j < J; ++j) acc[j] = mfma_opsel<FMT, S>(fa, fb[j], acc[j], sa, sb[j]);
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+            acc[m][j] = mfma_opsel<FMT, S>(fa[m], fb[j], acc[m][j], sa[m], sb[j]);
 }
 
-// A wave's J 16 x 16 tiles of c over all of K, in rounds of 4 K steps (one
-// 512-element scale record).  Each round's B rows (16 J rows) go to the
+// A wave's MB x J 16 x 16 tiles of c (16 MB rows of one group, 16 J
+// columns) over all of K, in rounds of 4 K steps (one 512-element scale
+// record).  Each round's B rows (16 J rows) go to the
 // wave's own LDS slice with direct loads, 1 KiB per instruction as whole
 // 16-byte pieces of kRowBytes-byte row segments (4 rows per instruction for
 // E2M1, 2 for E4M3), so every request covers whole cache lines; piece p of
 // row r is stored at slot p ^ (r % kPieces), so the fragment reads of 16 rows
 // fall in distinct banks.  A fragments (16 rows, shared by every wave and
-// read from L2) go straight to registers.  Only the wave itself reads its
+// read from L2) go straight to registers, MB row blocks of them, so each
+// B byte staged feeds MB products.  Only the wave itself reads its
 // slice, so there is no barrier: the compiler's wait for the direct loads
 // precedes the reads, and the reads are complete before the next round's
 // loads overwrite the slice.
-template <int FMT, int J>
+template <int FMT, int J, int MB>
 __device__ __forceinline__ void gemm_tile_skinny(const GemmTile& d, uint8_t* stage) {
     constexpr int kRowBytes = FMT == 1 ? 512 : 256;          // a row's bytes per round
     constexpr int kPieces = kRowBytes / 16;
@@ -694,9 +699,16 @@ __device__ __forceinline__ void gemm_tile_skinny(const GemmTile& d, uint8_t* sta
     const int cb = 16 * J * wave;
     if (cb >= d.c_cols) return;
     const int fr = lane & 15, fg = lane >> 4;
-    const int64_t ra = fr < d.a_rows ? fr : d.a_rows - 1;
-    const uint8_t* arow = d.a + ra * d.lda_q;
-    const uint8_t* asr = d.as + 4 * lane;
+    // row block m: rows 16 m .. 16 m + 15 of the tile; rows past the group
+    // load its last row, row groups past it its last scale record
+    const uint8_t* arow[MB];
+    const uint8_t* asr[MB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+        const int64_t r = 16 * m + fr, gm = m;
+        arow[m] = d.a + (r < d.a_rows ? r : d.a_rows - 1) * d.lda_q;
+        asr[m] = d.as + (gm < d.a_groups ? gm : d.a_groups - 1) * d.lda_s + 4 * lane;
+    }
     const uint8_t* bsr[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -716,9 +728,11 @@ __device__ __forceinline__ void gemm_tile_skinny(const GemmTile& d, uint8_t* sta
     }
     uint8_t* slice = stage + wave * kWaveBytes;
     const int row_bytes = FMT == 1 ? d.K : d.K / 2;
-    mfma_v4f acc[J];
+    mfma_v4f acc[MB][J];
 #pragma unroll
-    for (int j = 0; j < J; ++j) acc[j] = (mfma_v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int j = 0; j < J; ++j) acc[m][j] = (mfma_v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
     const int nk = d.K / 128;
     for (int k0 = 0; k0 < nk; k0 += 4) {
@@ -733,13 +747,17 @@ __device__ __forceinline__ void gemm_tile_skinny(const GemmTile& d, uint8_t* sta
                                              0, 0);
         }
         const int rec = (k0 >> 2) * 256;
-        const uint32_t sa = *reinterpret_cast<const uint32_t*>(asr + rec);
-        uint32_t sb[J];
+        uint32_t sa[MB], sb[J];
+#pragma unroll
+        for (int m = 0; m < MB; ++m) sa[m] = *reinterpret_cast<const uint32_t*>(asr[m] + rec);
 #pragma unroll
         for (int j = 0; j < J; ++j) sb[j] = *reinterpret_cast<const uint32_t*>(bsr[j] + rec);
-        mfma_v8i fa[4];
+        mfma_v8i fa[4][MB];
 #pragma unroll
-        for (int st = 0; st < 4; ++st) fa[st] = load_fragment<FMT>(arow, (k0 + st) * 128, fg, k0 + st < nk);
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int m = 0; m < MB; ++m)
+                fa[st][m] = load_fragment<FMT>(arow[m], (k0 + st) * 128, fg, k0 + st < nk);
         auto frag = [&](int st, int j) {
             const int r = 16 * j + fr;
             const uint8_t* row = slice + r * kRowBytes;
@@ -761,20 +779,22 @@ __device__ __forceinline__ void gemm_tile_skinny(const GemmTile& d, uint8_t* sta
         for (int st = 0; st < 4; ++st)
 #pragma unroll
             for (int j = 0; j < J; ++j) fb[st][j] = frag(st, j);
-        skinny_step<FMT, J, 0>(fa[0], fb[0], acc, sa, sb);
-        if (k0 + 1 < nk) skinny_step<FMT, J, 1>(fa[1], fb[1], acc, sa, sb);
-        if (k0 + 2 < nk) skinny_step<FMT, J, 2>(fa[2], fb[2], acc, sa, sb);
-        if (k0 + 3 < nk) skinny_step<FMT, J, 3>(fa[3], fb[3], acc, sa, sb);
+        skinny_step<FMT, J, MB, 0>(fa[0], fb[0], acc, sa, sb);
+        if (k0 + 1 < nk) skinny_step<FMT, J, MB, 1>(fa[1], fb[1], acc, sa, sb);
+        if (k0 + 2 < nk) skinny_step<FMT, J, MB, 2>(fa[2], fb[2], acc, sa, sb);
+        if (k0 + 3 < nk) skinny_step<FMT, J, MB, 3>(fa[3], fb[3], acc, sa, sb);
     }
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const int64_t col = cb + 16 * j + fr;
+    for (int m = 0; m < MB; ++m)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int64_t row = 4 * fg + e;
-            if (row < d.c_rows && col < d.c_cols) d.c[row * d.ldc + col] = acc[j][e];
+        for (int j = 0; j < J; ++j) {
+            const int64_t col = cb + 16 * j + fr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t row = 16 * m + 4 * fg + e;
+                if (row < d.c_rows && col < d.c_cols) d.c[row * d.ldc + col] = acc[m][j][e];
+            }
         }
-    }
 }
 
 // One workgroup per 16-row tile and 128-column tile (4 waves of J = 2 tiles
@@ -788,14 +808,14 @@ __device__ __forceinline__ void gemm_tile_skinny(const GemmTile& d, uint8_t* sta
 // tiles, non-temporal loads, and the next round's loads issued before this
 // round's products (two register sets: one wave per SIMD).  With the LDS
 // form, J = 1 (4 or 8 waves) took 315 us and 2 waves of J = 2 309 us.
-template <int FMT>
+template <int FMT, int MB>
 __global__ void __launch_bounds__(64 * kSkinnyWaves)
 mfma_gemm_grouped_skinny_kernel(const GemmArgs a, const GroupedGemmArgs g) {
     __shared__ __attribute__((aligned(16))) uint8_t stage[kSkinnyWaves * 16 * kSkinnyJ *
                                                           (FMT == 1 ? 512 : 256)];
     GemmTile d;
-    if (!grouped_desc<kSkinnyRows, kSkinnyCols>(a, g, d)) return;
-    gemm_tile_skinny<FMT, kSkinnyJ>(d, stage);
+    if (!grouped_desc<16 * MB, kSkinnyCols>(a, g, d)) return;
+    gemm_tile_skinny<FMT, kSkinnyJ, MB>(d, stage);
 }
 
 template <int FMT, class Cfg>
@@ -877,10 +897,20 @@ hipError_t launch_dequantize(int fmt, const DequantArgs& a, int64_t blocks, hipS
 namespace {
 template <int FMT>
 hipError_t launch_mfma_grouped(const GemmArgs& a, const GroupedGemmArgs& g, hipStream_t stream) {
-    if (g.decode) {
+    if (g.row_blocks > 0) {
         const dim3 grid((uint32_t)g.m_tiles, (uint32_t)((a.N + kSkinnyCols - 1) / kSkinnyCols));
-        hipLaunchKernelGGL((mfma_gemm_grouped_skinny_kernel<FMT>), grid, dim3(64 * kSkinnyWaves), 0,
-                           stream, a, g);
+        const dim3 block(64 * kSkinnyWaves);
+        switch (g.row_blocks) {
+            case 1:
+                hipLaunchKernelGGL((mfma_gemm_grouped_skinny_kernel<FMT, 1>), grid, block, 0, stream,
+                                   a, g);
+                break;
+            case 2:
+                hipLaunchKernelGGL((mfma_gemm_grouped_skinny_kernel<FMT, 2>), grid, block, 0, stream,
+                                   a, g);
+                break;
+            default: return hipErrorInvalidValue;
+        }
         return hipGetLastError();
     }
     const dim3 grid((uint32_t)g.m_tiles, (uint32_t)((a.N + kTileN - 1) / kTileN));

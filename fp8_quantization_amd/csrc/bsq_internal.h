@@ -113,8 +113,9 @@ hipError_t launch_mfma_matmul(int fmt, const GemmArgs& a, hipStream_t stream);
 
 // Grouped per-expert GEMM: A rows grouped by row_offsets (scale rows by
 // scales_offsets), B = num_experts stacked [N, K] operands; GemmArgs.M unused.
-// Tile of the grouped GEMM's decode form: rows of one group x columns of c.
-constexpr int kDecodeTileRows = 16, kDecodeTileCols = 128;
+// Columns of c in a tile of the grouped GEMM's decode form (its rows: 16 per
+// row block).
+constexpr int kDecodeTileCols = 128;
 struct GroupedGemmArgs {
     const uint32_t* row_offsets;     // [num_groups + 1]
     const uint32_t* scales_offsets;  // [num_groups + 1]
@@ -124,8 +125,9 @@ struct GroupedGemmArgs {
     int64_t max_rows;                // rows of A codes and of c
     int64_t num_scale_rows;          // scale rows of A
     int64_t m_tiles;                 // grid bound on row tiles over all groups
-    int32_t decode;                  // 1: 16-row tiles, B streamed through LDS (few rows
-                                     // per group); 0: 128-row tiles staged through LDS
+    int32_t row_blocks;              // 1 or 2: tiles of 16 row_blocks rows, B streamed
+                                     // through each wave's LDS (few rows per group); 0:
+                                     // 128-row tiles staged through LDS
 };
 hipError_t launch_mfma_grouped_matmul(int fmt, const GemmArgs& a, const GroupedGemmArgs& g,
                                       hipStream_t stream);

@@ -301,12 +301,12 @@ int block_scaled_matmul_mfma(int format, int block_size, int scale_layout,
  * expert e's weights.  Rows of c no group owns are not written.  Accuracy
  * as for block_scaled_matmul_mfma.
  *
- * Two kernels, chosen on the host from max_rows / num_groups (the offsets
- * stay on the device), after the decode / prefill split in the "NVFP4
- * routing" section of the grouped block-scaled SM100 matmul's "dispatch"
- * page: at most 8 rows per group on average
- * (decode) takes 16-row tiles that stream each expert's weights through
- * each wave's own LDS slice; more takes 128-row tiles staged through LDS.  Both give the
+ * The tile follows the rows per group on average, max_rows / num_groups,
+ * chosen on the host (the offsets stay on the device), after the decode /
+ * prefill split in the "NVFP4 routing" section of the grouped block-scaled
+ * SM100 matmul's "dispatch" page: at most 4 take 16-row tiles and at most 16
+ * take 32-row tiles, both streaming each expert's weights through each wave's
+ * own LDS slice; more take 128-row tiles staged through LDS.  All give the
  * same results within the stated bound.
  *
  *   format, block_size, scale_layout   as for block_scaled_matmul_mfma.

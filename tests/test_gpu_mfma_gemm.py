@@ -197,7 +197,7 @@ def test_grouped_gemm_decode_full_size_sampled(bsq):
     c = W.grouped_gemm_decode(W.MXFP4)
     fmt, K, E = c.fmt, c.K, c.num_experts
     N = c.b_codes.shape[0] // E
-    assert c.max_rows <= 8 * E                    # the decode kernel
+    assert tile_rows(c.max_rows, E) == 16
     nblk = K // 32
     ro, so, ids = c.row_offsets, c.scales_offsets, c.expert_ids
     out = bsq.grouped_block_scaled_matmul_mfma(
@@ -253,23 +253,32 @@ def grouped_case(fmt, G, E, N, K, rows, seed, misaligned=None):
                                           (40, 16, 160, 1024, 900), (9, 4, 256, 7168, 700),
                                           (130, 20, 96, 512, 3000), (200, 7, 48, 256, 9000)])
 def test_grouped_mfma_matches_oracle(bsq, fmt, G, E, N, K, rows):
-    """Groups of more than 8 rows on average: 128-row tiles staged in LDS."""
+    """Groups of more than 16 rows on average: 128-row tiles staged in LDS."""
     d = grouped_case(fmt, G, E, N, K, rows, seed=G + N + K + fmt)
-    assert d["max_rows"] > 8 * G
+    assert d["max_rows"] > 16 * G
     check_grouped_run(bsq, fmt, d, G, E, N, K)
 
 
+def tile_rows(max_rows, G):
+    """The library's tile for a grouped GEMM, from the rows per group."""
+    return 16 if max_rows <= 4 * G else 32 if max_rows <= 16 * G else 128
+
+
 @pytest.mark.parametrize("fmt", [MXFP4, MXFP8])
-@pytest.mark.parametrize("G,E,N,K,rows", [(64, 16, 300, 2048, 400), (40, 8, 96, 512, 300),
-                                          (100, 12, 512, 1152, 700), (32, 4, 128, 7168, 240),
-                                          (256, 32, 272, 256, 512)])
-def test_grouped_mfma_decode_matches_oracle(bsq, fmt, G, E, N, K, rows):
-    """At most 8 rows per group on average (a decode step): 16-row tiles with
-    the weights streamed through LDS.  N = 300, 96 and 272 leave partial
-    column tiles and idle waves; K = 1152 and 256 end in a partial round of K
-    steps; groups of 17 to 23 rows (G = 32) take several row tiles."""
+@pytest.mark.parametrize("G,E,N,K,rows,tile", [
+    (256, 32, 272, 256, 512, 16), (128, 16, 300, 2048, 400, 16), (100, 12, 96, 1152, 300, 16),
+    (128, 8, 128, 512, 500, 16),
+    (64, 16, 300, 2048, 400, 32), (40, 8, 96, 512, 300, 32), (100, 12, 512, 1152, 700, 32),
+    (16, 4, 128, 7168, 240, 32)])
+def test_grouped_mfma_few_rows_matches_oracle(bsq, fmt, G, E, N, K, rows, tile):
+    """At most 16 rows per group on average (decode steps): 16-row tiles (at
+    most 4 on average) or 32-row tiles, the weights streamed through LDS.
+    N = 300, 96 and 272 leave partial column tiles and idle waves; K = 1152 and
+    256 end in a partial round of K steps; groups of up to 22 rows (16-row
+    tiles, G = 128 with 500 rows) and up to 38-40 rows (32-row tiles, G = 40
+    and 16) take several row tiles."""
     d = grouped_case(fmt, G, E, N, K, rows, seed=G + N + K + fmt + 11)
-    assert d["max_rows"] <= 8 * G
+    assert tile_rows(d["max_rows"], G) == tile
     check_grouped_run(bsq, fmt, d, G, E, N, K)
 
 
@@ -305,11 +314,12 @@ def check_grouped_run(bsq, fmt, d, G, E, N, K, ids=None, max_rows=None, skipped=
 
 
 @pytest.mark.parametrize("fmt", [MXFP4, MXFP8])
-def test_grouped_mfma_decode_skips_bad_groups(bsq, fmt):
-    """The decode kernel skips what the 128-row one skips: a group whose scale
-    offset is not a multiple of 16, groups whose expert id is out of range
-    either way, and a group running past max_rows."""
-    G, E, N, K, rows = 30, 5, 80, 512, 150
+@pytest.mark.parametrize("rows,tile", [(100, 16), (150, 32)])
+def test_grouped_mfma_few_rows_skips_bad_groups(bsq, fmt, rows, tile):
+    """The 16- and 32-row kernels skip what the 128-row one skips: a group
+    whose scale offset is not a multiple of 16, groups whose expert id is out
+    of range either way, and a group running past max_rows."""
+    G, E, N, K = 30, 5, 80, 512
     counts = grouped_case(fmt, G, E, N, K, rows, seed=79)["counts"]
     nonempty = [int(g) for g in np.nonzero(counts)[0] if g >= 1]
     mis, bad_hi, bad_lo = nonempty[0], nonempty[1], nonempty[2]
@@ -318,7 +328,7 @@ def test_grouped_mfma_decode_skips_bad_groups(bsq, fmt):
     ids = d["ids"].copy()
     ids[bad_hi], ids[bad_lo] = E, -1
     max_rows = int(d["ro"][last]) + int(counts[last]) // 2
-    assert max_rows <= 8 * G
+    assert tile_rows(max_rows, G) == tile
     check_grouped_run(bsq, fmt, d, G, E, N, K, ids=ids, max_rows=max_rows,
                       skipped=(mis, bad_hi, bad_lo, last) + tuple(range(last + 1, G)))
 
