@@ -269,12 +269,13 @@ def tile_rows(max_rows, G):
     (256, 32, 272, 256, 512, 16), (128, 16, 300, 2048, 400, 16), (100, 12, 96, 1152, 300, 16),
     (128, 8, 128, 512, 500, 16),
     (64, 16, 300, 2048, 400, 32), (40, 8, 96, 512, 300, 32), (100, 12, 512, 1152, 700, 32),
-    (16, 4, 128, 7168, 240, 32)])
+    (16, 4, 128, 7168, 240, 32), (200, 10, 144, 128, 500, 16), (50, 10, 144, 128, 500, 32)])
 def test_grouped_mfma_few_rows_matches_oracle(bsq, fmt, G, E, N, K, rows, tile):
     """At most 16 rows per group on average (decode steps): 16-row tiles (at
     most 4 on average) or 32-row tiles, the weights streamed through LDS.
-    N = 300, 96 and 272 leave partial column tiles and idle waves; K = 1152 and
-    256 end in a partial round of K steps; groups of up to 22 rows (16-row
+    N = 300, 96, 272 and 144 leave partial column tiles and idle waves;
+    K = 1152, 256 and 128 end in a partial round of K steps (K = 128: a single
+    step, most of the round's weight loads clamped); groups of up to 22 rows (16-row
     tiles, G = 128 with 500 rows) and up to 38-40 rows (32-row tiles, G = 40
     and 16) take several row tiles."""
     d = grouped_case(fmt, G, E, N, K, rows, seed=G + N + K + fmt + 11)
