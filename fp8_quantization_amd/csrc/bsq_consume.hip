@@ -635,9 +635,9 @@ mfma_gemm_grouped_kernel(const GemmArgs a, const GroupedGemmArgs g) {
 // tokens per expert).  A 128-row tile would spend nearly all of its matrix
 // work and LDS traffic on padding rows, and the expert's weights dominate the
 // bytes, so this form is built around streaming B once per 16 routed rows:
-//  * a workgroup takes 16 rows of one group (the instruction's smallest M)
-//    and kSkinnyWaves x 16 J columns of c; each wave owns J 16 x 16 tiles of
-//    c over the whole of K;
+//  * a workgroup takes 16 MB rows of one group (MB = 1 or 2 blocks of the
+//    instruction's smallest M) and kSkinnyWaves x 16 J columns of c; each
+//    wave owns MB x J 16 x 16 tiles of c over the whole of K;
 //  * each wave streams its own B rows through its own LDS slice, 512
 //    elements of K (four K steps, one scale dword per operand) per round,
 //    with no barrier; A fragments go straight to registers; the waves
@@ -797,9 +797,10 @@ __device__ __forceinline__ void gemm_tile_skinny(const GemmTile& d, uint8_t* sta
         }
 }
 
-// One workgroup per 16-row tile and 128-column tile (4 waves of J = 2 tiles
-// of c).  Measured on the decode routing (512 routed rows over 256 experts,
-// N = 7168, K = 2048), MXFP4: 309 us, against 341 us for the same tiles with
+// One workgroup per 16 MB-row tile and 128-column tile (4 waves of J = 2
+// columns of tiles).  With MB = 1, measured on the decode routing (512
+// routed rows over 256 experts, N = 7168, K = 2048), MXFP4: 309 us, against
+// 341 us for the same tiles with
 // every fragment loaded straight from global memory into registers (each
 // load then covers 64 bytes of each of 16 rows, so every cache line is
 // requested twice), and 385 us for the 128-row kernel.  With the register
