@@ -636,8 +636,8 @@ mfma_gemm_grouped_kernel(const GemmArgs a, const GroupedGemmArgs g) {
 // work and LDS traffic on padding rows, and the expert's weights dominate the
 // bytes, so this form is built around streaming B once per 16 routed rows:
 //  * a workgroup takes 16 MB rows of one group (MB = 1 or 2 blocks of the
-//    instruction's smallest M) and kSkinnyWaves x 16 J columns of c; each
-//    wave owns MB x J 16 x 16 tiles of c over the whole of K;
+//    instruction's smallest M) and 128 columns of c, split over its waves;
+//    each wave owns MB x J 16 x 16 tiles of c over the whole of K;
 //  * each wave streams its own B rows through its own LDS slice, 512
 //    elements of K (four K steps, one scale dword per operand) per round,
 //    with no barrier; A fragments go straight to registers; the waves
@@ -647,9 +647,23 @@ mfma_gemm_grouped_kernel(const GemmArgs a, const GroupedGemmArgs g) {
 // It follows the decode entry in the "NVFP4 routing" section of the grouped
 // block-scaled SM100 matmul's "dispatch" page (few rows per expert: a narrow
 // tile on the token side), with the smallest tile the CDNA4 instruction has.
-constexpr int kSkinnyWaves = 4, kSkinnyJ = 2;
-constexpr int kSkinnyCols = kSkinnyWaves * 16 * kSkinnyJ;
-static_assert(kSkinnyCols == kDecodeTileCols, "decode tile shape");
+// Waves of a workgroup and 16-column tiles per wave, for MB row blocks: the
+// tile is always kDecodeTileCols = 128 columns wide.  Measured (MXFP4, 256
+// experts, N = 512, K = 7168): 16-row tiles 101.5 us at 8 rows per expert
+// with 4 waves of J = 2, 107.0 with 2 waves of J = 4; 32-row tiles 94.4 /
+// 99.4 us at 8 / 16 rows per expert with 2 waves of J = 4, 95.6 / 107.8 with
+// 4 waves of J = 2 and 93.2 / 98.9 with 1 wave of J = 8.  MXFP8 keeps J = 2:
+// with J = 4 its 32-row tiles take 332 registers, one wave per SIMD.
+template <int FMT, int MB>
+struct SkinnyShape {
+    static constexpr int J = (MB == 2 && FMT == 0) ? 4 : 2;
+    static constexpr int kWaves = kDecodeTileCols / (16 * J);
+    static constexpr int kRowBytes = FMT == 1 ? 512 : 256;   // a B row's bytes per round
+    static constexpr int kStageBytes = kWaves * 16 * J * kRowBytes;
+};
+static_assert(SkinnyShape<0, 1>::kWaves * 16 * SkinnyShape<0, 1>::J == kDecodeTileCols &&
+                  SkinnyShape<1, 2>::kWaves * 16 * SkinnyShape<1, 2>::J == kDecodeTileCols,
+              "decode tile shape");
 
 template <int FMT, int S>
 __device__ __forceinline__ mfma_v4f mfma_opsel(const mfma_v8i& fa, const mfma_v8i& fb,
@@ -810,13 +824,13 @@ __device__ __forceinline__ void gemm_tile_skinny(const GemmTile& d, uint8_t* sta
 // round's products (two register sets: one wave per SIMD).  With the LDS
 // form, J = 1 (4 or 8 waves) took 315 us and 2 waves of J = 2 309 us.
 template <int FMT, int MB>
-__global__ void __launch_bounds__(64 * kSkinnyWaves)
+__global__ void __launch_bounds__((64 * SkinnyShape<FMT, MB>::kWaves))
 mfma_gemm_grouped_skinny_kernel(const GemmArgs a, const GroupedGemmArgs g) {
-    __shared__ __attribute__((aligned(16))) uint8_t stage[kSkinnyWaves * 16 * kSkinnyJ *
-                                                          (FMT == 1 ? 512 : 256)];
+    using Sh = SkinnyShape<FMT, MB>;
+    __shared__ __attribute__((aligned(16))) uint8_t stage[Sh::kStageBytes];
     GemmTile d;
-    if (!grouped_desc<16 * MB, kSkinnyCols>(a, g, d)) return;
-    gemm_tile_skinny<FMT, kSkinnyJ, MB>(d, stage);
+    if (!grouped_desc<16 * MB, kDecodeTileCols>(a, g, d)) return;
+    gemm_tile_skinny<FMT, Sh::J, MB>(d, stage);
 }
 
 template <int FMT, class Cfg>
@@ -899,16 +913,16 @@ namespace {
 template <int FMT>
 hipError_t launch_mfma_grouped(const GemmArgs& a, const GroupedGemmArgs& g, hipStream_t stream) {
     if (g.row_blocks > 0) {
-        const dim3 grid((uint32_t)g.m_tiles, (uint32_t)((a.N + kSkinnyCols - 1) / kSkinnyCols));
-        const dim3 block(64 * kSkinnyWaves);
+        const dim3 grid((uint32_t)g.m_tiles,
+                        (uint32_t)((a.N + kDecodeTileCols - 1) / kDecodeTileCols));
         switch (g.row_blocks) {
             case 1:
-                hipLaunchKernelGGL((mfma_gemm_grouped_skinny_kernel<FMT, 1>), grid, block, 0, stream,
-                                   a, g);
+                hipLaunchKernelGGL((mfma_gemm_grouped_skinny_kernel<FMT, 1>), grid,
+                                   dim3(64 * SkinnyShape<FMT, 1>::kWaves), 0, stream, a, g);
                 break;
             case 2:
-                hipLaunchKernelGGL((mfma_gemm_grouped_skinny_kernel<FMT, 2>), grid, block, 0, stream,
-                                   a, g);
+                hipLaunchKernelGGL((mfma_gemm_grouped_skinny_kernel<FMT, 2>), grid,
+                                   dim3(64 * SkinnyShape<FMT, 2>::kWaves), 0, stream, a, g);
                 break;
             default: return hipErrorInvalidValue;
         }
