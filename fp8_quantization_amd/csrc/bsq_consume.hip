@@ -833,6 +833,19 @@ mfma_gemm_grouped_skinny_kernel(const GemmArgs a, const GroupedGemmArgs g) {
     gemm_tile_skinny<FMT, Sh::J, MB>(d, stage);
 }
 
+// The dense GEMM with few rows (a dense layer at decode) on the same
+// tiles: a 128-row tile would be mostly padding, and B, read once, is the
+// bytes that matter.  Workgroup -> (row tile, 128-column tile), row-major.
+template <int FMT, int MB>
+__global__ void __launch_bounds__((64 * SkinnyShape<FMT, MB>::kWaves))
+mfma_gemm_skinny_kernel(const GemmArgs a, int64_t tiles_n) {
+    using Sh = SkinnyShape<FMT, MB>;
+    __shared__ __attribute__((aligned(16))) uint8_t stage[Sh::kStageBytes];
+    GemmTile d;
+    dense_desc<16 * MB, kDecodeTileCols>(a, tiles_n, d);
+    gemm_tile_skinny<FMT, Sh::J, MB>(d, stage);
+}
+
 template <int FMT, class Cfg>
 hipError_t launch_tiles(const GemmArgs& a, hipStream_t stream) {
     const int64_t tiles_n = (a.N + Cfg::TN - 1) / Cfg::TN;
@@ -851,10 +864,31 @@ hipError_t launch_tiles(const GemmArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// 256 x 256 tiles (8 waves, 144 KiB of LDS in two stages, one workgroup per
-// CU) once they alone fill the chip; 128 x 128 ones otherwise, or on request
+template <int FMT>
+hipError_t launch_mfma_skinny(const GemmArgs& a, hipStream_t stream) {
+    const int64_t tiles_n = (a.N + kDecodeTileCols - 1) / kDecodeTileCols;
+    if (a.M <= 16)
+        hipLaunchKernelGGL((mfma_gemm_skinny_kernel<FMT, 1>), dim3((uint32_t)tiles_n),
+                           dim3(64 * SkinnyShape<FMT, 1>::kWaves), 0, stream, a, tiles_n);
+    else
+        hipLaunchKernelGGL((mfma_gemm_skinny_kernel<FMT, 2>),
+                           dim3((uint32_t)(((a.M + 31) / 32) * tiles_n)),
+                           dim3(64 * SkinnyShape<FMT, 2>::kWaves), 0, stream, a, tiles_n);
+    return hipGetLastError();
+}
+
+// Few rows: 16- or 32-row tiles streaming B (by default).  Measured on
+// N = 16384, K = 7168 against 128 x 128 tiles: MXFP4 M <= 16 17-18 us
+// against 23, but M = 24 / 32 with 32-row tiles (two waves per workgroup,
+// one workgroup per 128 columns) 24.3 / 24.7 against 23.6 / 23.7; MXFP8
+// M <= 16 24-26 us against 39-40, M = 24 / 32 33.0 / 37.0 against 40.1.
+// So M <= 16, and for MXFP8 M <= 32.  Otherwise 256 x 256 tiles (8 waves,
+// 144 KiB of LDS in two stages, one workgroup per CU) once they alone fill
+// the chip; 128 x 128 ones otherwise, or on request.
 template <int FMT>
 hipError_t launch_mfma_tiled(const GemmArgs& a, hipStream_t stream) {
+    if (a.tiled == 1 && (a.M <= 16 || (FMT == 1 && a.M <= 32)))
+        return launch_mfma_skinny<FMT>(a, stream);
     const int64_t big = ((a.M + 255) / 256) * ((a.N + 255) / 256);
     if (a.tiled != 3 && a.tiled != 4 && big >= 256) return launch_tiles<FMT, Tile256>(a, stream);
     return launch_tiles<FMT, Tile128>(a, stream);
