@@ -835,14 +835,28 @@ mfma_gemm_grouped_skinny_kernel(const GemmArgs a, const GroupedGemmArgs g) {
 
 // The dense GEMM with few rows (a dense layer at decode) on the same
 // tiles: a 128-row tile would be mostly padding, and B, read once, is the
-// bytes that matter.  Workgroup -> (row tile, 128-column tile), row-major.
+// bytes that matter.  Workgroup -> (row tile, column tile), row-major.  The
+// grid is only N / columns workgroups wide, so the tiles are 64 columns wide
+// (4 waves of one 16-column tile).  At N = 16384, K = 7168: 16-row tiles,
+// M = 1 / 16, MXFP4 14.8 / 15.0 us against 18.4 / 20.9 with 128 columns (4
+// waves of two), MXFP8 20.5 / 21.4 against 25.6 / 25.0; 32-row tiles,
+// M = 24 / 32, MXFP4 19.4 / 19.9 us against 20.2 / 21.3 with 128 columns,
+// MXFP8 30.0 / 34.1 against 33.1 / 37.2.
 template <int FMT, int MB>
-__global__ void __launch_bounds__((64 * SkinnyShape<FMT, MB>::kWaves))
+struct DenseSkinnyShape {
+    static constexpr int J = 1;
+    static constexpr int kWaves = 4;
+    static constexpr int kCols = kWaves * 16 * J;
+    static constexpr int kStageBytes = kWaves * 16 * J * (FMT == 1 ? 512 : 256);
+};
+
+template <int FMT, int MB>
+__global__ void __launch_bounds__((64 * DenseSkinnyShape<FMT, MB>::kWaves))
 mfma_gemm_skinny_kernel(const GemmArgs a, int64_t tiles_n) {
-    using Sh = SkinnyShape<FMT, MB>;
+    using Sh = DenseSkinnyShape<FMT, MB>;
     __shared__ __attribute__((aligned(16))) uint8_t stage[Sh::kStageBytes];
     GemmTile d;
-    dense_desc<16 * MB, kDecodeTileCols>(a, tiles_n, d);
+    dense_desc<16 * MB, Sh::kCols>(a, tiles_n, d);
     gemm_tile_skinny<FMT, Sh::J, MB>(d, stage);
 }
 
@@ -864,31 +878,31 @@ hipError_t launch_tiles(const GemmArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int FMT>
-hipError_t launch_mfma_skinny(const GemmArgs& a, hipStream_t stream) {
-    const int64_t tiles_n = (a.N + kDecodeTileCols - 1) / kDecodeTileCols;
-    if (a.M <= 16)
-        hipLaunchKernelGGL((mfma_gemm_skinny_kernel<FMT, 1>), dim3((uint32_t)tiles_n),
-                           dim3(64 * SkinnyShape<FMT, 1>::kWaves), 0, stream, a, tiles_n);
-    else
-        hipLaunchKernelGGL((mfma_gemm_skinny_kernel<FMT, 2>),
-                           dim3((uint32_t)(((a.M + 31) / 32) * tiles_n)),
-                           dim3(64 * SkinnyShape<FMT, 2>::kWaves), 0, stream, a, tiles_n);
+template <int FMT, int MB>
+hipError_t launch_mfma_skinny_mb(const GemmArgs& a, hipStream_t stream) {
+    using Sh = DenseSkinnyShape<FMT, MB>;
+    const int64_t tiles_n = (a.N + Sh::kCols - 1) / Sh::kCols;
+    const int64_t tiles = ((a.M + 16 * MB - 1) / (16 * MB)) * tiles_n;
+    hipLaunchKernelGGL((mfma_gemm_skinny_kernel<FMT, MB>), dim3((uint32_t)tiles),
+                       dim3(64 * Sh::kWaves), 0, stream, a, tiles_n);
     return hipGetLastError();
 }
 
-// Few rows: 16- or 32-row tiles streaming B (by default).  Measured on
-// N = 16384, K = 7168 against 128 x 128 tiles: MXFP4 M <= 16 17-18 us
-// against 23, but M = 24 / 32 with 32-row tiles (two waves per workgroup,
-// one workgroup per 128 columns) 24.3 / 24.7 against 23.6 / 23.7; MXFP8
-// M <= 16 24-26 us against 39-40, M = 24 / 32 33.0 / 37.0 against 40.1.
-// So M <= 16, and for MXFP8 M <= 32.  Otherwise 256 x 256 tiles (8 waves,
-// 144 KiB of LDS in two stages, one workgroup per CU) once they alone fill
-// the chip; 128 x 128 ones otherwise, or on request.
+template <int FMT>
+hipError_t launch_mfma_skinny(const GemmArgs& a, hipStream_t stream) {
+    return a.M <= 16 ? launch_mfma_skinny_mb<FMT, 1>(a, stream)
+                     : launch_mfma_skinny_mb<FMT, 2>(a, stream);
+}
+
+// Few rows (M <= 32, by default): 16- or 32-row tiles streaming B.
+// Measured on N = 16384, K = 7168 against 128 x 128 tiles: MXFP4 15.0 /
+// 19.9 us at M = 16 / 32 against 23.4 / 23.8; MXFP8 21.4 / 34.1 against
+// 39.6 / 40.3.  Otherwise 256 x 256 tiles (8 waves, 144 KiB of LDS in two
+// stages, one workgroup per CU) once they alone fill the chip; 128 x 128
+// ones otherwise, or on request.
 template <int FMT>
 hipError_t launch_mfma_tiled(const GemmArgs& a, hipStream_t stream) {
-    if (a.tiled == 1 && (a.M <= 16 || (FMT == 1 && a.M <= 32)))
-        return launch_mfma_skinny<FMT>(a, stream);
+    if (a.tiled == 1 && a.M <= 32) return launch_mfma_skinny<FMT>(a, stream);
     const int64_t big = ((a.M + 255) / 256) * ((a.N + 255) / 256);
     if (a.tiled != 3 && a.tiled != 4 && big >= 256) return launch_tiles<FMT, Tile256>(a, stream);
     return launch_tiles<FMT, Tile128>(a, stream);

@@ -262,8 +262,8 @@ int block_scaled_matmul_naive(int format, int block_size, int scale_layout,
  * module page lists.  Workgroups compute 256 x 256 tiles of c (128 x 128
  * when the larger ones would not fill the chip), staging 128-byte K slices
  * of both operands and their scale records in LDS through the direct
- * global-to-LDS loads.  With few rows (a dense layer at decode: M <= 16,
- * or M <= 32 for MXFP8) they compute 16- or 32-row tiles that stream B once
+ * global-to-LDS loads.  With few rows (a dense layer at decode: M <= 32)
+ * they compute 16- or 32-row tiles, 64 columns wide, that stream B once
  * through each wave's own LDS slice, the grouped GEMM's decode form.  The
  * instruction's own arithmetic sets the accuracy:
  * FP4 products and their sums come out as exact fp32 sums would; FP8

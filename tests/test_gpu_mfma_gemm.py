@@ -51,8 +51,7 @@ def magnitude_sum(qa, sa, qb, sb, fmt, K):
 @pytest.mark.parametrize("fmt", [MXFP4, MXFP8])
 @pytest.mark.parametrize("M,N,K", [(16, 16, 128), (37, 45, 1024), (128, 96, 2048),
                                    (33, 130, 7168), (1, 300, 640),
-                                   # few rows: 16- / 32-row tiles streaming B (by default;
-                                   # M <= 16, or M <= 32 for MXFP8)
+                                   # M <= 32: 16- / 32-row tiles streaming B (by default)
                                    (5, 1000, 1152), (24, 520, 2048), (32, 257, 256),
                                    (17, 130, 7168)])
 def test_mfma_matmul_matches_oracle(bsq, fmt, M, N, K):
