@@ -66,6 +66,9 @@ def load_workload(name):
         # the matrix-core consumer of the MFMA scale layout
         "mfma_gemm_mxfp8": lambda: W.gemm_random_operands(W.MXFP8, 4096, 4096, 7168, seed=1202),
         "mfma_gemm_mxfp4": lambda: W.gemm_random_operands(W.MXFP4, 4096, 4096, 7168, seed=1201),
+        # a dense layer at decode: 16 rows against 16384 x 7168 weights
+        "mfma_gemm_mxfp4_m16": lambda: W.gemm_random_operands(W.MXFP4, 16, 16384, 7168,
+                                                              seed=1205),
         "mfma_grouped_gemm_mxfp4": lambda: W.grouped_gemm_prefill(W.MXFP4),
         "mfma_grouped_gemm_mxfp4_decode": lambda: W.grouped_gemm_decode(W.MXFP4),
     }
@@ -504,8 +507,8 @@ def main():
         for name in ("dense_nvfp4", "grouped_nvfp4", "dense_mxfp4", "grouped_mxfp4_decode",
                      "grouped_mxfp8_decode", "grouped_mxfp8", "grouped_mxfp4",
                      "tsf_dense_nvfp4", "tsf_grouped_nvfp4", "dequant_mxfp8", "dequant_nvfp4",
-                     "mfma_gemm_mxfp8", "mfma_gemm_mxfp4", "mfma_grouped_gemm_mxfp4",
-                     "mfma_grouped_gemm_mxfp4_decode"):
+                     "mfma_gemm_mxfp8", "mfma_gemm_mxfp4", "mfma_gemm_mxfp4_m16",
+                     "mfma_grouped_gemm_mxfp4", "mfma_grouped_gemm_mxfp4_decode"):
             if name == args.workload:
                 continue
             c2, r2, nb2, el2, nbs2, w2, k2 = measure(name, args.steps, args.warmup)

@@ -67,3 +67,15 @@ def test_grouped_gemm_bytes_count_only_experts_with_rows():
         want = (c.a_codes.nbytes + c.a_scales.nbytes + used * per_expert +
                 4 * (2 * (E + 1) + E) + 4 * c.max_rows * N)
         assert bench.algorithmic_bytes(c) == (want, c.max_rows * N)
+
+
+def test_dense_decode_gemm_bytes():
+    """16 rows against 16384 x 7168 MXFP4 weights: operands and their scale
+    records read once, c written; HBM-bound (bytes at 8 TB/s outlast the
+    flops at the fp4 matrix peak)."""
+    c = bench.load_workload("mfma_gemm_mxfp4_m16")
+    nb, elems = bench.algorithmic_bytes(c)
+    rec = (7168 // 512) * 256
+    assert nb == 16 * 3584 + 16384 * 3584 + (1 + 1024) * rec + 4 * 16 * 16384
+    assert elems == 16 * 16384
+    assert nb / bench.PEAK_HBM_GBS / 1e9 > bench.gemm_flops(c) / bench.PEAK_MFMA_TFLOPS[0] / 1e12
