@@ -79,3 +79,17 @@ def test_dense_decode_gemm_bytes():
     assert nb == 16 * 3584 + 16384 * 3584 + (1 + 1024) * rec + 4 * 16 * 16384
     assert elems == 16 * 16384
     assert nb / bench.PEAK_HBM_GBS / 1e9 > bench.gemm_flops(c) / bench.PEAK_MFMA_TFLOPS[0] / 1e12
+
+
+@pytest.mark.parametrize("n", [2, 8])
+def test_bench_refuses_more_than_one_gpu(n):
+    """bench.py measures one GPU: --gpus N > 1 exits with status 2 and a
+    message, before touching torch or the library."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", str(n)],
+                         capture_output=True, text=True, timeout=120, cwd=root)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr and res.stdout == ""
