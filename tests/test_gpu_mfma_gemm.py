@@ -286,6 +286,21 @@ def test_grouped_mfma_few_rows_matches_oracle(bsq, fmt, G, E, N, K, rows, tile):
     check_grouped_run(bsq, fmt, d, G, E, N, K)
 
 
+@pytest.mark.parametrize("fmt", [MXFP4, MXFP8])
+@pytest.mark.parametrize("rows,max_rows,tile", [(125, 128, 16), (125, 129, 32), (508, 512, 32),
+                                                (508, 513, 128)])
+def test_grouped_mfma_tile_choice_at_the_cuts(bsq, fmt, rows, max_rows, tile):
+    """The tile follows max_rows / num_groups: exactly 4 rows per group on
+    average still takes 16-row tiles and one more row 32-row tiles; exactly 16
+    still takes 32-row tiles and one more row the 128-row tiles.  Every choice
+    gives the oracle's results within the bound on the same data."""
+    G, E, N, K = 32, 8, 160, 640
+    d = grouped_case(fmt, G, E, N, K, rows, seed=rows + max_rows + fmt)
+    assert int(d["ro"][-1]) == rows <= max_rows <= d["max_rows"]
+    assert tile_rows(max_rows, G) == tile
+    check_grouped_run(bsq, fmt, d, G, E, N, K, max_rows=max_rows)
+
+
 def check_grouped_run(bsq, fmt, d, G, E, N, K, ids=None, max_rows=None, skipped=()):
     """Run the grouped GEMM on grouped_case data (optionally with other expert
     ids or a smaller max_rows) into a buffer of 7.0s; every group not in
