@@ -1,28 +1,40 @@
 #!/usr/bin/env python3
 """Throughput of dynamic block-scaled quantization on one MI355X.
 
-Headline: dense BF16 -> MXFP8 quantization of an [8192, 7168] activation
-matrix (N(0, 1) rows scaled by 2^U(-8, 8), 0.1% outliers x100), block 32, E8M0
-scales.  One step = one call of the whole hot path (load, block amax, scale,
-quantize, pack, store codes and scales) over that matrix.  Metric: achieved
-HBM GB/s counting algorithmic bytes (BF16 read + codes + scales written), as a
-fraction of the 8 TB/s HBM3E peak.
+Headline: grouped per-expert BF16 -> NVFP4 quantization of the MoE prefill
+routing -- 16384 routed rows x 7168 of N(0, 1) activations over 128 experts
+(Dirichlet(0.3) counts, empty experts kept), uint32 row and scale offsets
+(scale rows padded to 128 per expert), int32 expert ids and fp32 per-expert
+tensor scales.  One step = one call of the whole hot path over that input:
+load, group search, block amax, scale, quantize, pack, store codes and
+scales.  Metric: achieved HBM GB/s counting algorithmic bytes (BF16 read +
+codes + scales written + routing metadata), as a fraction of the 8 TB/s HBM3E
+peak.  The other workloads (dense MXFP4 [128, 4096], dense MXFP8 [8192, 7168],
+dense NVFP4 [16384, 7168], the MXFP4 / MXFP8 decode gather) are measured in
+the same run, each with its own figures.
 
-Protocol: inputs are resident in HBM before timing starts.  The timed loop
-rotates over several copies of the input/output buffers whose combined size is
-well above the 256 MB last-level (MALL) cache, so each step streams from HBM
-(no warm-cache reuse).  One pair of HIP events, recorded on the stream the
-kernels run on, brackets the K back-to-back launches: their elapsed time / K
-is the mean launch duration the roofline figure uses; the headline ``value``
-uses the host wall clock of the same loop.  The CPU oracle is timed on a bounded
-sample of the same workload on the host's cores (``cpu_baseline``), and its
-output doubles as a parity check of that sample.
+Protocol.  Inputs are resident in HBM before timing starts.  Each workload's
+loop rotates over several copies of its buffers whose combined size is well
+above the 256 MB last-level (MALL) cache, so every step streams from HBM.
+The timed region is K back-to-back launches between two device
+synchronisations.  Every launch in it carries a pair of HIP events bound to
+its kernel's dispatch (``bsq_time_next_launch``, hipExtLaunchKernel on the
+launch stream): their elapsed time is the kernel's own execution, the figure
+rocprofv3's kernel trace reports, and the roofline fraction is computed from
+it (mean, and median beside it).  The headline ``value`` is the host wall
+clock of the same region.  For the large dense and grouped workloads the same
+job also times the same-byte-mix trivial stream of ``libbsq_ceiling.so`` on
+the same buffers (``ceiling``).  The CPU oracle is timed on a bounded sample
+of every quantizer workload on the host's cores, on one thread and on all of
+them, and its output is compared with the GPU's for that sample.
 
-Usage: python bench.py [--gpus 1] [--steps 500] [--warmup 20]
-       [--workload dense_mxfp8] [--no-secondary] [--no-cpu-baseline]
-       python bench.py --copy-bytes N   (plain copy kernel, for counter calibration)
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 10]
+       [--workload grouped_nvfp4] [--no-secondary] [--no-cpu-baseline] [--no-ceiling]
+       python bench.py --copy-bytes N          (plain copy, for counter calibration)
+       python bench.py --pmc-summary DIR       (counters of rocprofv3 --pmc runs -> traffic)
 """
 import argparse
+import glob
 import hashlib
 import json
 import os
@@ -37,8 +49,11 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20
 METRIC = "achieved HBM GB/s (% of 8 TB/s) for BF16→MXFP4/MXFP8/NVFP4 quant, 1 GPU"
-KERNEL_SRC = os.path.join(ROOT, "fp8_quantization_amd", "csrc", "bsq_kernels.hip")
+CSRC = os.path.join(ROOT, "fp8_quantization_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+HEADLINE = "grouped_nvfp4"
+# the host's CPU share for one GPU on the measurement box
+CPU_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 
 def log(*a):
@@ -47,32 +62,46 @@ def log(*a):
 
 # ------------------------------------------------------------------ workloads
 
-def load_workload(name):
+# quantizer workloads: name -> (builder, chunks per wave of the dense byte-mix
+# stream that prices it, or None)
+def quantizer_table():
     import workloads as W
-    table = {
-        "dense_mxfp4": W.dense_mxfp4_small,
-        "dense_mxfp8": W.dense_mxfp8_scaled_rows,
-        "dense_nvfp4": W.dense_nvfp4_scaled_rows,
-        "grouped_nvfp4": W.grouped_nvfp4_prefill,
-        # the same routing quantized to the MX formats (large grouped MX path)
-        "grouped_mxfp8": lambda: W.grouped_mx_prefill(W.MXFP8),
-        "grouped_mxfp4": lambda: W.grouped_mx_prefill(W.MXFP4),
-        "grouped_mxfp4_decode": lambda: W.grouped_mx_decode(W.MXFP4),
-        "grouped_mxfp8_decode": lambda: W.grouped_mx_decode(W.MXFP8),
-        # dequantization of codes and scales of the dense MXFP8 / NVFP4 sizes
+    return {
+        "grouped_nvfp4": (W.grouped_nvfp4_prefill, 4),
+        "dense_mxfp4": (W.dense_mxfp4_small, None),
+        "dense_mxfp8": (W.dense_mxfp8_scaled_rows, 2),
+        "dense_nvfp4": (W.dense_nvfp4_scaled_rows, 4),
+        "grouped_mxfp4_decode": (lambda: W.grouped_mx_decode(W.MXFP4), None),
+        "grouped_mxfp8_decode": (lambda: W.grouped_mx_decode(W.MXFP8), None),
+        # the prefill routing quantized to the MX formats
+        "grouped_mxfp8": (lambda: W.grouped_mx_prefill(W.MXFP8), 2),
+        "grouped_mxfp4": (lambda: W.grouped_mx_prefill(W.MXFP4), 4),
+    }
+
+
+def consumer_table():
+    import workloads as W
+    return {
+        # the NVFP4 tensor-scale producer on the dense and grouped 16384 x 7168 inputs
+        "tsf_dense_nvfp4": W.dense_nvfp4_scaled_rows,
+        "tsf_grouped_nvfp4": W.grouped_nvfp4_prefill,
+        # dequantization of random codes and scales of the dense MXFP8 / NVFP4 sizes
         "dequant_mxfp8": lambda: W.dequant_random_bytes(W.MXFP8, 8192, 7168, seed=1102),
         "dequant_nvfp4": lambda: W.dequant_random_bytes(W.NVFP4, 16384, 7168, seed=1103,
                                                         tensor_sf=0.0123),
-        # the matrix-core consumer of the MFMA scale layout
+        # the matrix-core consumers of the MFMA scale layout
         "mfma_gemm_mxfp8": lambda: W.gemm_random_operands(W.MXFP8, 4096, 4096, 7168, seed=1202),
         "mfma_gemm_mxfp4": lambda: W.gemm_random_operands(W.MXFP4, 4096, 4096, 7168, seed=1201),
-        # a dense layer at decode: 16 rows against 16384 x 7168 weights
-        "mfma_gemm_mxfp4_m16": lambda: W.gemm_random_operands(W.MXFP4, 16, 16384, 7168,
-                                                              seed=1205),
         "mfma_grouped_gemm_mxfp4": lambda: W.grouped_gemm_prefill(W.MXFP4),
         "mfma_grouped_gemm_mxfp4_decode": lambda: W.grouped_gemm_decode(W.MXFP4),
     }
-    return table[name]()
+
+
+def load_workload(name):
+    q = quantizer_table()
+    if name in q:
+        return q[name][0]()
+    return consumer_table()[name]()
 
 
 def bytes_per_element(fmt):
@@ -81,12 +110,8 @@ def bytes_per_element(fmt):
     return 2.0 + (1.0 if fmt == 1 else 0.5) + 1.0 / bs
 
 
-# NVFP4 tensor-scale producer steps, measured on the named quantizer input
-PRODUCERS = {"tsf_dense_nvfp4": "dense_nvfp4", "tsf_grouped_nvfp4": "grouped_nvfp4"}
-
-
 def producer_bytes(case):
-    """Bytes one producer step must move: the BF16 rows it reduces (each
+    """Bytes one tensor-scale step must move: the BF16 rows it reduces (each
     distinct source row once), the grouping metadata and the fp32 results."""
     import workloads as W
     K = case.x.shape[1]
@@ -163,7 +188,8 @@ def algorithmic_bytes(case):
 class Runner:
     """Holds NB resident copies of one workload's buffers and launches one
     step on copy i: the quantizer; with ``producer`` the NVFP4 tensor-scale
-    producer on the same input; for a DequantCase the dequantization."""
+    producer on the same input; for a DequantCase the dequantization; for a
+    GEMM case the matrix-core GEMM."""
 
     def __init__(self, case, nb, producer=False):
         import torch
@@ -258,40 +284,47 @@ class Runner:
                                            scales=s["s"])
 
 
-def time_steps(runner, steps, warmup):
-    """Wall time of `steps` back-to-back launches, and the mean launch
-    duration from one pair of HIP events recorded on the launch stream around
-    the whole timed loop."""
-    torch = runner.torch
-    for i in range(warmup):
-        runner.step(i)
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record()
-    for i in range(steps):
-        runner.step(warmup + i)
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return wall, start.elapsed_time(end) / steps
+# ------------------------------------------------------------------ timing
 
-
-def launch_percentiles(runner, n, offset):
-    """Per-launch durations (µs) of n further launches, each bracketed by its
-    own HIP event pair on the launch stream, still rotating over the buffer
-    sets: median, p10 and p90."""
-    torch = runner.torch
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n)]
-    for i, (a, b) in enumerate(ev):
+def recorded_events(torch, n):
+    """n pairs of timing events, each recorded once so that it exists."""
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n)]
+    for a, b in pairs:
         a.record()
-        runner.step(offset + i)
         b.record()
     torch.cuda.synchronize()
-    us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
-    return {"median": round(float(np.median(us)), 3), "p10": round(float(np.percentile(us, 10)), 3),
-            "p90": round(float(np.percentile(us, 90)), 3), "n": n}
+    return pairs
+
+
+def spread(us):
+    us = np.asarray(us, np.float64)
+    return {"mean": round(float(us.mean()), 3), "median": round(float(np.median(us)), 3),
+            "p10": round(float(np.percentile(us, 10)), 3),
+            "p90": round(float(np.percentile(us, 90)), 3), "n": int(us.size)}
+
+
+def timed_region(torch, arm, launch, steps, warmup):
+    """Warm up, then time `steps` launches between two device
+    synchronisations.  Before launch i, arm(start_i, stop_i) binds a recorded
+    event pair to that launch's kernel.  Returns the wall time of the region,
+    the per-launch span of one event pair around the whole loop (kernel times
+    plus the gaps between launches), and every kernel's own time (µs)."""
+    for i in range(warmup):
+        launch(i)
+    pairs = recorded_events(torch, steps)
+    outer = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    outer[0].record()
+    for i in range(steps):
+        arm(*pairs[i])
+        launch(warmup + i)
+    outer[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_us = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+    return wall, outer[0].elapsed_time(outer[1]) * 1e3 / steps, kernel_us
 
 
 def graph_launch_us(runner, n_launch=64, replays=20):
@@ -320,131 +353,196 @@ def graph_launch_us(runner, n_launch=64, replays=20):
 LATENCY_BOUND_BYTES = 16 << 20
 
 
-def measure(name, steps, warmup, rotate=True):
+def rotation(nbytes):
+    """Buffer sets to rotate over: together more than three times the MALL."""
+    return min(64, max(2, -(-3 * MALL_BYTES // max(nbytes, 1)) + 1))
+
+
+def measure(name, steps, warmup):
+    """One workload: its runner, algorithmic bytes and elements per launch,
+    and its timing summary."""
     import workloads as W
-    producer = name in PRODUCERS
-    case = load_workload(PRODUCERS.get(name, name))
+    producer = name.startswith("tsf_")
+    case = load_workload(name)
     nbytes, elems = producer_bytes(case) if producer else algorithmic_bytes(case)
-    rotate = rotate and not isinstance(case, (W.GemmCase, W.GroupedGemmCase))  # reuse is the point
-    nb = max(2, -(-3 * MALL_BYTES // max(nbytes, 1)) + 1) if rotate else 1
-    nb = min(nb, 64)
+    reuse = isinstance(case, (W.GemmCase, W.GroupedGemmCase))   # one set: reuse is the point
+    nb = 1 if reuse else rotation(nbytes)
     runner = Runner(case, nb, producer)
-    wall, kern = time_steps(runner, steps, warmup)
-    runner.percentiles = launch_percentiles(runner, steps, warmup + steps)
-    runner.graph_us = graph_launch_us(runner) if nbytes < LATENCY_BOUND_BYTES else None
-    return case, runner, nbytes, elems, nb, wall, kern
+    wall, region_us, kernel_us = timed_region(runner.torch, runner.bsq.time_next_launch,
+                                              runner.step, steps, warmup)
+    s = summary(name, nbytes, elems, nb, wall, region_us, kernel_us, steps)
+    if nbytes < LATENCY_BOUND_BYTES:
+        g = graph_launch_us(runner)
+        s.update({"graph_us_mean": g, "graph_GBps": round(nbytes / g / 1e3, 1),
+                  "graph_Gelem_per_s": round(elems / g / 1e3, 1)})
+    return case, runner, nbytes, s
 
 
-def summary(name, nbytes, elems, wall, launch_ms, steps, nb, percentiles=None, graph_us=None):
-    k = launch_ms * 1e-3
-    out = {
+def summary(name, nbytes, elems, nb, wall, region_us, kernel_us, steps):
+    k = spread(kernel_us)
+    return {
         "workload": name,
         "bytes_per_launch": nbytes,
         "elements": elems,
         "buffer_sets": nb,
-        "launch_us_mean": round(k * 1e6, 3),
-        "launch_us_each": percentiles,
-        "GBps": round(nbytes / k / 1e9, 1),
-        "frac_of_8TBps": round(nbytes / k / 1e9 / PEAK_HBM_GBS, 4),
-        "Gelem_per_s": round(elems / k / 1e9, 1),
+        "kernel_us": k,
+        "launch_span_us": round(region_us, 3),
+        "GBps": round(nbytes / k["mean"] / 1e3, 1),
+        "frac_of_8TBps": round(nbytes / k["mean"] / 1e3 / PEAK_HBM_GBS, 4),
+        "GBps_median": round(nbytes / k["median"] / 1e3, 1),
+        "Gelem_per_s": round(elems / k["mean"] / 1e3, 1),
         "wall_GBps": round(nbytes * steps / wall / 1e9, 1),
+        "wall_s": round(wall, 6),
     }
-    if graph_us is not None:  # latency-bound: the kernel's time without the host's launch cost
-        out.update({"graph_us_mean": graph_us, "graph_GBps": round(nbytes / graph_us / 1e3, 1),
-                    "graph_Gelem_per_s": round(elems / graph_us / 1e3, 1)})
-    return out
+
+
+def ceiling(runner, u, steps, warmup):
+    """The same-byte-mix trivial stream on the workload's own buffers (its
+    BF16 input and, as dense [M, K] outputs, the first rows of its code and
+    scale buffers), timed like the quantizer."""
+    bsq, torch, case = runner.bsq, runner.torch, runner.case
+    M, K = case.x.shape
+    views = [(st["x"], st["q"][:M], st["s"][:M]) for st in runner.sets]
+    fmt = case.fmt
+    armed = {}
+
+    def arm(a, b):
+        armed["ev"] = (a, b)
+
+    def launch(i):
+        x, q, s = views[i % len(views)]
+        a, b = armed.pop("ev", (None, None))
+        bsq.ceiling_stream(x, fmt, u, codes=q, scales=s, start=a, stop=b)
+
+    wall, region_us, kernel_us = timed_region(torch, arm, launch, steps, warmup)
+    nbytes = int(M * K * bytes_per_element(fmt))
+    k = spread(kernel_us)
+    return {"kernel": f"bsq::ceiling_kernel, {M}x{K}, {['MXFP4', 'MXFP8', 'NVFP4'][fmt]} "
+                      f"byte mix, {u} chunk(s) per wave",
+            "bytes_per_launch": nbytes, "kernel_us": k,
+            "GBps": round(nbytes / k["mean"] / 1e3, 1),
+            "frac_of_8TBps": round(nbytes / k["mean"] / 1e3 / PEAK_HBM_GBS, 4)}
+
+
+def roofline(s, traffic, traffic_note, ceil=None):
+    k = s["kernel_us"]
+    r = {"bound": "hbm", "achieved": s["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+         "frac": s["frac_of_8TBps"],
+         "frac_median": round(s["GBps_median"] / PEAK_HBM_GBS, 4),
+         "kernel_us_mean": k["mean"], "kernel_us_median": k["median"],
+         "bytes_per_launch": s["bytes_per_launch"],
+         "timing": "per-launch HIP events bound to the kernel dispatch (hipExtLaunchKernel) "
+                   "over the timed region",
+         "traffic": traffic, "traffic_note": traffic_note}
+    if ceil is not None:
+        r["ceiling"] = ceil
+        r["of_ceiling"] = round(ceil["kernel_us"]["mean"] / k["mean"], 4)
+    return r
 
 
 # ------------------------------------------------------------------ CPU baseline
 
-def cpu_baseline(case, runner, target_cpu_seconds=12.0, max_wall_seconds=20.0):
-    """Time the oracle (as it stands) on the same input on the host's cores:
-    whole passes over the leading rows (all of them when the input is small)
-    until about target_cpu_seconds of CPU work (wall x threads) are done;
-    check the GPU's output for those rows."""
+def _oracle_sample(case, rows, threads):
+    """The oracle on a leading sample of the workload: the first `rows`
+    routed rows (groups cut at that row).  Returns the codes and scale rows it
+    wrote, the index arrays of those rows, and their algorithmic bytes."""
     import oracle
+    import workloads as W
+    if isinstance(case, W.DenseCase):
+        q, s = oracle.quantize(case.x[:rows], case.fmt, case.tensor_sf, nthreads=threads)
+        K = case.x.shape[1]
+        return q, s, np.arange(rows), np.arange(rows), rows * K * bytes_per_element(case.fmt)
+    ro = np.minimum(case.row_offsets.astype(np.int64), rows).astype(np.uint32)
+    q, s = oracle.grouped_quantize(case.x, case.fmt, ro, case.scales_offsets, case.expert_ids,
+                                   case.tensor_sf, case.max_rows, case.num_scale_rows,
+                                   row_indices=case.row_indices, nthreads=threads)
+    code_rows = np.arange(int(ro[0]), int(ro[-1]))
+    scale_rows = np.concatenate([np.arange(int(so), int(so) + int(hi - lo)) for lo, hi, so in
+                                 zip(ro[:-1], ro[1:], case.scales_offsets[:-1])]
+                                + [np.zeros(0, np.int64)])
+    K = case.x.shape[1]
+    if case.row_indices is None:
+        reads = code_rows.size
+    else:
+        reads = np.unique(case.row_indices[code_rows]).size
+    nbytes = reads * K * 2 + code_rows.size * K * (bytes_per_element(case.fmt) - 2.0)
+    return q[code_rows], s[scale_rows], code_rows, scale_rows, nbytes
+
+
+def cpu_baseline(case, runner, cpu_seconds):
+    """Time the oracle (as it stands) on the workload's own input on the
+    host's cores: all threads over a leading sample sized for about
+    `cpu_seconds` of CPU work (wall x threads), in whole passes; then one
+    thread over a smaller leading sample.  The GPU's output for the sample
+    must equal the oracle's."""
+    import workloads as W
     torch = runner.torch
-    threads = max(1, min(16, os.cpu_count() or 1))
-    M, K = case.x.shape
-    probe = min(M, 64)
+    total = case.x.shape[0] if isinstance(case, W.DenseCase) else int(case.row_offsets[-1])
+    probe = min(total, 64)
     t = time.perf_counter()
-    oracle.quantize(case.x[:probe], case.fmt, case.tensor_sf, nthreads=threads)
-    per_row = (time.perf_counter() - t) / probe           # wall seconds per row
-    want_rows = target_cpu_seconds / threads / max(per_row, 1e-9)
-    rows = int(min(M, max(probe, want_rows)))
-    # whole passes over those rows until the CPU work (wall x threads) reaches the target
-    reps, dt = 0, 0.0
-    while reps == 0 or (dt * threads < target_cpu_seconds and dt < max_wall_seconds):
+    _oracle_sample(case, probe, CPU_THREADS)
+    per_row = max((time.perf_counter() - t) / probe, 1e-9)      # wall per row on all threads
+    rows = int(min(total, max(probe, cpu_seconds / CPU_THREADS / per_row)))
+    reps, dt, nbytes = 0, 0.0, 0.0
+    while reps == 0 or (dt * CPU_THREADS < cpu_seconds and dt < 2 * cpu_seconds / CPU_THREADS):
         t = time.perf_counter()
-        qh, sh = oracle.quantize(case.x[:rows], case.fmt, case.tensor_sf, nthreads=threads)
+        q, s, code_rows, scale_rows, b = _oracle_sample(case, rows, CPU_THREADS)
         dt += time.perf_counter() - t
+        nbytes += b
         reps += 1
-    nbytes = reps * rows * K * bytes_per_element(case.fmt)
     runner.step(0)
     torch.cuda.synchronize()
     s0 = runner.sets[0]
-    ok = bool(np.array_equal(s0["q"][:rows].cpu().numpy(), qh) and
-              np.array_equal(s0["s"][:rows].cpu().numpy(), sh))
-    # the same oracle on one thread, over a smaller leading sample (a few seconds at most)
-    rows1 = int(min(M, max(1, 3.0 / max(per_row * threads, 1e-9))))
+    idx_q = torch.from_numpy(code_rows).cuda()
+    idx_s = torch.from_numpy(scale_rows).cuda()
+    same = bool(np.array_equal(s0["q"][idx_q].cpu().numpy(), q) and
+                np.array_equal(s0["s"][idx_s].cpu().numpy(), s))
+    # one thread, on a leading sample sized for about a second
+    rows1 = int(min(total, max(1, 1.0 / (per_row * CPU_THREADS))))
     t = time.perf_counter()
-    oracle.quantize(case.x[:rows1], case.fmt, case.tensor_sf, nthreads=1)
+    _, _, _, _, b1 = _oracle_sample(case, rows1, 1)
     dt1 = time.perf_counter() - t
     return {
         "value": round(nbytes / dt / 1e9, 3),
         "unit": "GB/s",
-        "cores": threads,
+        "cores": CPU_THREADS,
         "kind": "oracle",
-        "one_thread": {"value": round(rows1 * K * bytes_per_element(case.fmt) / dt1 / 1e9, 3),
-                       "sample": f"first {rows1} rows, {dt1:.2f} s wall on 1 thread"},
-        "sample": f"first {rows} of {M} rows of the {case.name} input, {reps} pass(es) "
-                  f"({reps * rows * K} elements, {nbytes / 1e6:.1f} MB algorithmic), "
-                  f"{dt:.2f} s wall on {threads} thread(s)",
-        "parity_of_sample": "identical" if ok else "MISMATCH",
+        "sample": f"first {rows} of {total} rows of the {case.name} input, {reps} pass(es), "
+                  f"{nbytes / 1e6:.1f} MB algorithmic, {dt:.2f} s wall on {CPU_THREADS} threads",
+        "one_thread": {"value": round(b1 / dt1 / 1e9, 4), "cores": 1,
+                       "sample": f"first {rows1} rows, {dt1:.2f} s wall"},
+        "host_cpus_seen": os.cpu_count(),
+        "parity_of_sample": "identical" if same else "MISMATCH",
     }
 
 
-def traffic_from_counters(nbytes_per_launch):
-    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    counters, valid only while the kernel source is the one they were taken
-    on (sha256 recorded beside them)."""
+# ------------------------------------------------------------------ counters
+
+def source_hash():
+    """sha256 over the library's sources: counters taken on other sources do
+    not describe the kernels that run."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        h.update(os.path.basename(p).encode())
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def traffic_from_counters(name):
+    """HBM bytes per launch of workload `name` from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, valid only while the library's sources
+    are the ones they were taken on."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None, "no counter file"
-    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    if rec.get("kernel_source_sha256") != sha:
-        return None, "kernel changed since the counters were taken"
-    return int(rec["hbm_bytes_per_launch"]), rec.get("note", "")
-
-
-# ------------------------------------------------------------------ main
-
-def vendor_cast_context(runner, steps, warmup):
-    """Context for the headline: torch's own elementwise cast of the same BF16
-    buffers to float8_e4m3fn (2 bytes read and 1 written per element, the
-    MXFP8 byte mix without the scales), rotated and timed like the quantizer.
-    A vendor streaming kernel of this mix shows what such a stream reaches on
-    this chip; it computes no block scales."""
-    torch = runner.torch
-    if not hasattr(torch, "float8_e4m3fn"):
-        return None
-    xs = [st["x"].view(torch.bfloat16) for st in runner.sets]
-    outs = [torch.empty(x.shape, dtype=torch.float8_e4m3fn, device="cuda") for x in xs]
-    for i in range(warmup):
-        outs[i % len(xs)].copy_(xs[i % len(xs)])
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for i in range(steps):
-        outs[i % len(xs)].copy_(xs[i % len(xs)])
-    b.record()
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) / steps * 1e3
-    nbytes = xs[0].numel() * 3
-    return {"kernel": "torch bf16 -> float8_e4m3fn cast (same inputs, same rotation)",
-            "bytes_per_launch": nbytes, "launch_us_mean": round(us, 3),
-            "GBps": round(nbytes / us / 1e3, 1)}
+    if rec.get("source_sha256") != source_hash():
+        return None, "the kernels changed since the counters were taken"
+    v = rec.get("hbm_bytes_per_launch", {}).get(name)
+    if v is None:
+        return None, f"no counters for {name}"
+    return int(v), ("committed measurement (profiles/pmc_traffic.json), not taken in this "
+                    "run: " + rec.get("note", ""))
 
 
 def copy_calibration(nbytes, steps):
@@ -459,17 +557,89 @@ def copy_calibration(nbytes, steps):
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "steps": steps}))
 
 
+def _pmc_rows(path, counter):
+    """(kernel name, value, duration ns) of every dispatch in a rocprofv3
+    counter_collection.csv for one counter."""
+    import csv
+    out = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                out.append((r["Kernel_Name"], float(r["Counter_Value"]),
+                            int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    return out
+
+
+def _main_kernel(rows):
+    """The library kernel with the most GPU time in a run (the workload's own)."""
+    tot = {}
+    for name, _, ns in rows:
+        if "bsq::" in name:
+            tot[name] = tot.get(name, 0) + ns
+    return max(tot, key=tot.get) if tot else None
+
+
+def pmc_summary(d, copy_bytes):
+    """Turn rocprofv3 --pmc runs into HBM bytes per launch: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) of each workload's main kernel, each scaled
+    by what the counter reads for a plain copy of copy_bytes bytes.  Writes
+    profiles/pmc_traffic.json and prints a markdown table."""
+    def mean_of(stem, counter, pick=None):
+        rows = _pmc_rows(os.path.join(d, f"{stem}_counter_collection.csv"), counter)
+        k = pick or _main_kernel(rows)
+        v = [x for n, x, _ in rows if n == k]
+        return k, float(np.mean(v)), len(v)
+    _, cf, _ = mean_of("copy_fetch", "FETCH_SIZE", "__amd_rocclr_copyBuffer")
+    _, cw, _ = mean_of("copy_write", "WRITE_SIZE", "__amd_rocclr_copyBuffer")
+    ff, wf = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    table, out = [], {}
+    for p in sorted(glob.glob(os.path.join(d, "*_fetch_counter_collection.csv"))):
+        w = os.path.basename(p)[:-len("_fetch_counter_collection.csv")]
+        if w == "copy":
+            continue
+        k, f, n = mean_of(f"{w}_fetch", "FETCH_SIZE")
+        _, wr, _ = mean_of(f"{w}_write", "WRITE_SIZE", k)
+        hbm = int(round(f * 1024 * ff + wr * 1024 * wf))
+        case = load_workload(w)
+        alg = (producer_bytes(case) if w.startswith("tsf_") else algorithmic_bytes(case))[0]
+        out[w] = hbm
+        table.append(f"| {w} | `{k}` | {n} | {f:.1f} | {wr:.1f} | {hbm:,} | {alg:,} | "
+                     f"{hbm / alg:.4f} |")
+    rec = {"source_sha256": source_hash(), "fetch_factor": ff, "write_factor": wf,
+           "hbm_bytes_per_launch": out,
+           "note": f"FETCH_SIZE x {ff:.4f} + WRITE_SIZE x {wf:.4f} per dispatch of the "
+                   f"workload's main kernel; factors from a plain copy of {copy_bytes} bytes"}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(f"copy of {copy_bytes} bytes: FETCH_SIZE {cf:.1f} KiB (factor {ff:.4f}), "
+          f"WRITE_SIZE {cw:.1f} KiB (factor {wf:.4f})\n")
+    print("| workload | kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes "
+          "(calibrated) | algorithmic bytes | ratio |")
+    print("|---|---|---|---|---|---|---|---|")
+    print("\n".join(table))
+
+
+# ------------------------------------------------------------------ main
+
+LARGE = ("grouped_nvfp4", "dense_mxfp8", "dense_nvfp4")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="dense_mxfp8")
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--pmc-summary", default="")
     args = ap.parse_args()
 
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary, args.copy_bytes or 268435456)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would "
               "quantize its own shard with no exchange); run with --gpus 1.", file=sys.stderr)
@@ -485,83 +655,66 @@ def main():
 
     import fp8_quantization_amd as bsq
 
-    case, runner, nbytes, elems, nb, wall, kern = measure(args.workload, args.steps, args.warmup)
-    head = summary(args.workload, nbytes, elems, wall, kern, args.steps, nb, runner.percentiles,
-                   runner.graph_us)
-    log("[bench] headline", json.dumps(head))
-    achieved = nbytes / (kern * 1e-3) / 1e9
-    quantizer = args.workload not in PRODUCERS and not args.workload.startswith(
-        ("dequant_", "mfma_gemm", "mfma_grouped_gemm"))
-    if not quantizer:
-        traffic, traffic_note = None, "counters are taken on the quantizer only"
-    else:
-        traffic, traffic_note = traffic_from_counters(nbytes)
-
-    context = None
-    if args.workload == "dense_mxfp8":
-        context = vendor_cast_context(runner, args.steps, args.warmup)
-        log("[bench] context", json.dumps(context))
-
-    secondary = []
+    quant = quantizer_table()
+    names = [args.workload]
     if not args.no_secondary:
-        for name in ("dense_nvfp4", "grouped_nvfp4", "dense_mxfp4", "grouped_mxfp4_decode",
-                     "grouped_mxfp8_decode", "grouped_mxfp8", "grouped_mxfp4",
-                     "tsf_dense_nvfp4", "tsf_grouped_nvfp4", "dequant_mxfp8", "dequant_nvfp4",
-                     "mfma_gemm_mxfp8", "mfma_gemm_mxfp4", "mfma_gemm_mxfp4_m16",
-                     "mfma_grouped_gemm_mxfp4", "mfma_grouped_gemm_mxfp4_decode"):
-            if name == args.workload:
-                continue
-            c2, r2, nb2, el2, nbs2, w2, k2 = measure(name, args.steps, args.warmup)
-            s = summary(name, nb2, el2, w2, k2, args.steps, nbs2, r2.percentiles, r2.graph_us)
-            if name.startswith(("mfma_gemm", "mfma_grouped_gemm")):
-                tf = gemm_flops(c2) / (k2 * 1e-3) / 1e12
-                peak = PEAK_MFMA_TFLOPS[c2.fmt]
-                # the bound is whichever ideal time is longer: flops at the peak or bytes at 8 TB/s
-                hbm_bound = nb2 / PEAK_HBM_GBS / 1e9 > gemm_flops(c2) / peak / 1e12
-                s.update({"bound": "hbm" if hbm_bound else "mfma", "TFLOPs": round(tf, 1),
-                          "peak_TFLOPs": peak, "frac_of_peak": round(tf / peak, 4)})
-            log("[bench] secondary", json.dumps(s))
-            secondary.append(s)
-            del r2, c2
-            torch.cuda.empty_cache()
+        names += [n for n in list(quant) + list(consumer_table()) if n != args.workload]
+    results, head = {}, None
+    for name in names:
+        case, runner, nbytes, s = measure(name, args.steps, args.warmup)
+        if name.startswith(("mfma_gemm", "mfma_grouped_gemm")):
+            tf = gemm_flops(case) / s["kernel_us"]["mean"] / 1e6
+            peak = PEAK_MFMA_TFLOPS[case.fmt]
+            # the bound is whichever ideal time is longer: flops at the peak or bytes at 8 TB/s
+            hbm_bound = nbytes / PEAK_HBM_GBS / 1e9 > gemm_flops(case) / peak / 1e12
+            s.update({"bound": "hbm" if hbm_bound else "mfma", "TFLOPs": round(tf, 1),
+                      "peak_TFLOPs": peak, "frac_of_peak": round(tf / peak, 4)})
+        if name in quant:
+            ceil = None
+            u = quant[name][1]
+            if name in LARGE and u and not args.no_ceiling:
+                ceil = ceiling(runner, u, args.steps, args.warmup)
+                log("[bench] ceiling", name, json.dumps(ceil))
+            if name in LARGE:
+                s["roofline"] = roofline(s, *traffic_from_counters(name), ceil)
+            if not args.no_cpu_baseline:
+                s["cpu_baseline"] = cpu_baseline(case, runner, 12.0 if name == args.workload
+                                                 else 4.0)
+        log("[bench]", json.dumps(s))
+        if name == args.workload:
+            head = (case, s)
+        results[name] = s
+        del runner, case
+        torch.cuda.empty_cache()
 
-    cpu = None
-    if not args.no_cpu_baseline and quantizer:
-        cpu = cpu_baseline(case, runner)
-        log("[bench] cpu_baseline", json.dumps(cpu))
-
+    case, s = head
     fmt_name = {0: "MXFP4", 1: "MXFP8", 2: "NVFP4"}[case.fmt]
-    if hasattr(case, "a_codes"):
-        rows, K = case.a_codes.shape[0], case.K
-    elif hasattr(case, "codes"):
-        rows, K = case.codes.shape[0], case.K
-    else:
-        rows, K = case.x.shape
+    config = {"workload": getattr(case, "name", args.workload), "format": fmt_name,
+              "input": "bf16", "bytes_per_step": s["bytes_per_launch"],
+              "buffer_sets_rotated": s["buffer_sets"], "version": bsq.version()}
+    if hasattr(case, "x"):
+        config.update({"rows": int(case.x.shape[0]), "K": int(case.x.shape[1]),
+                       "block": bsq.BLOCK_SIZE[case.fmt]})
+    if hasattr(case, "expert_ids"):
+        config["groups"] = int(case.expert_ids.shape[0])
+    rl = s.get("roofline") or roofline(s, None, "counters are taken on the large quantizers")
     line = {
         "metric": METRIC,
-        "value": round(nbytes * args.steps / wall / 1e9, 1),
+        "value": s["wall_GBps"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "ms_per_step": round(s["wall_s"] / args.steps * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "fp32" if case.fmt == 2 else "int32",
         "data": "synthetic",
-        "config": {"workload": case.name, "format": fmt_name, "rows": int(rows),
-                   "K": int(K), "block": bsq.BLOCK_SIZE[case.fmt],
-                   "bytes_per_step": nbytes, "buffer_sets_rotated": nb,
-                   "version": bsq.version()},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic, "traffic_note": traffic_note,
-                     "launch_us_mean": head["launch_us_mean"],
-                     "launch_us_each": head["launch_us_each"]},
-        "cpu_baseline": cpu,
-        "stream_context": context,
-        "secondary": secondary,
+        "config": config,
+        "roofline": rl,
+        "cpu_baseline": s.get("cpu_baseline"),
+        "workloads": {n: r for n, r in results.items() if n != args.workload},
     }
     print(json.dumps(line), flush=True)
 

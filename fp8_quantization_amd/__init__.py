@@ -62,6 +62,8 @@ _lib.grouped_block_scaled_matmul_mfma.argtypes = [_i32, _i32, _i32, _p, _i64, _p
                                                   _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _i64,
                                                   _i64, _i64, _p, _i64, _p]
 _lib.grouped_block_scaled_matmul_mfma.restype = _i32
+_lib.bsq_time_next_launch.argtypes = [_p, _p]
+_lib.bsq_time_next_launch.restype = _i32
 _lib.bsq_last_error.argtypes = []
 _lib.bsq_last_error.restype = ctypes.c_char_p
 _lib.bsq_version.argtypes = []
@@ -83,6 +85,21 @@ def lib() -> ctypes.CDLL:
 
 def version() -> str:
     return _lib.bsq_version().decode()
+
+
+def time_next_launch(start, stop):
+    """Arm this thread's next library call to launch its main kernel with the
+    events ``start`` / ``stop`` (``torch.cuda.Event(enable_timing=True)``,
+    already recorded once so that they exist) bound to the kernel's own
+    dispatch: ``start.elapsed_time(stop)`` is then that kernel's execution
+    time.  ``None, None`` disarms."""
+    def handle(e):
+        if e is None:
+            return None
+        if not e.cuda_event:
+            raise ValueError("record the event once before arming it (torch creates it lazily)")
+        return ctypes.c_void_p(e.cuda_event)
+    _check(_lib.bsq_time_next_launch(handle(start), handle(stop)))
 
 
 def _check(status: int):
@@ -374,3 +391,47 @@ def grouped_block_scaled_matmul_mfma(a_codes, a_scales, row_offsets, scales_offs
         num_scale_rows, _ptr(b_codes), _ld(b_codes), _ptr(b_scales), _ld(b_scales), num_experts,
         N, K, _ptr(out), _ld(out), _stream_ptr(stream, a_codes.device)))
     return out
+
+
+# ------------------------------------------------------------------ measurement aid
+
+_ceiling_lib = None
+
+
+def ceiling_stream(x: torch.Tensor, fmt, chunks_per_wave: int, codes=None, scales=None,
+                   start=None, stop=None, stream=None):
+    """The trivial stream of ``libbsq_ceiling.so`` (``include/bsq_ceiling.h``):
+    the memory traffic of a dense quantizer launch on x (BF16 [M, K], K a
+    multiple of 512) with ``chunks_per_wave`` chunks per wave, computing
+    nothing of the method.  ``start`` / ``stop``: optional recorded
+    ``torch.cuda.Event`` pair bound to the kernel's dispatch.  Returns the
+    written (codes, scales)."""
+    global _ceiling_lib
+    if _ceiling_lib is None:
+        path = os.path.join(os.path.dirname(LIB_PATH), "libbsq_ceiling.so")
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is not built; run fp8_quantization_amd/build.py")
+        lib_c = ctypes.CDLL(path)
+        lib_c.bsq_ceiling_stream.argtypes = [_i32, _p, _i64, _i64, _p, _p, _i32, _p, _p, _p]
+        lib_c.bsq_ceiling_stream.restype = _i32
+        _ceiling_lib = lib_c
+    f = _fmt(fmt)
+    x = _as_bf16_matrix(x)
+    if not x.is_contiguous():
+        raise TypeError("x must be contiguous")
+    M, K = x.shape
+    if codes is None:
+        codes = torch.empty((M, code_width(f, K)), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M, K // BLOCK_SIZE[f]), dtype=torch.uint8, device=x.device)
+    for name, t, cols in (("codes", codes, code_width(f, K)), ("scales", scales,
+                                                               K // BLOCK_SIZE[f])):
+        if not t.is_contiguous() or tuple(t.shape) != (M, cols) or t.dtype != torch.uint8:
+            raise TypeError(f"{name} must be a contiguous uint8 [{M}, {cols}] tensor")
+    ev = [None if e is None else ctypes.c_void_p(e.cuda_event) for e in (start, stop)]
+    st = _ceiling_lib.bsq_ceiling_stream(f, _ptr(x), M, K, _ptr(codes), _ptr(scales),
+                                         chunks_per_wave, ev[0], ev[1],
+                                         _stream_ptr(stream, x.device))
+    if st != 0:
+        raise BsqError(st, "bsq_ceiling_stream rejected its arguments or failed to launch")
+    return codes, scales

@@ -18,6 +18,9 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbsq.so")
 SOURCES = [os.path.join(CSRC, "bsq_api.cpp"), os.path.join(CSRC, "bsq_kernels.hip"),
            os.path.join(CSRC, "bsq_consume.hip")]
+# the same-byte-mix streaming kernel the bench compares the quantizers with
+CEILING_LIB = os.path.join(HERE, "libbsq_ceiling.so")
+CEILING_SOURCES = [os.path.join(CSRC, "bsq_ceiling.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -31,20 +34,26 @@ FLAGS = [
 
 
 def build(verbose: bool = False, extra=()) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, *SOURCES, "-o", tmp]
+    """Build libbsq.so, then libbsq_ceiling.so; returns the path of the first."""
+    _build_one(LIB, SOURCES, verbose, extra)
+    _build_one(CEILING_LIB, CEILING_SOURCES, verbose, extra)
+    return LIB
+
+
+def _build_one(lib, sources, verbose, extra):
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, *FLAGS, *extra, *sources, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libbsq.so")
+        raise RuntimeError(f"hipcc failed building {os.path.basename(lib)}")
     noise = [ln for ln in (res.stdout + res.stderr).splitlines()
              if ln.strip() and "packed-fp32-ops" not in ln]
     if verbose and noise:
         print("\n".join(noise))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

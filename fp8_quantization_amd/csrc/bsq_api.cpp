@@ -26,6 +26,15 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// Events armed by bsq_time_next_launch for this thread's next call.
+thread_local bsq::LaunchEvents g_armed;
+
+bsq::LaunchEvents take_events() {
+    const bsq::LaunchEvents e = g_armed;
+    g_armed = bsq::LaunchEvents{};
+    return e;
+}
+
 int fail(int status, const char* fmt, ...) {
     char buf[512];
     va_list ap;
@@ -49,56 +58,10 @@ bool log_enabled() {
     return on;
 }
 
-// Launch-shape knobs, read once from the environment for sweeps (0 / unset:
-// the built-in choice below):
-//   BSQ_TILE_CHUNKS   quantizer, dequantizer: chunks of 512 elements per wave (1, 2, 4)
-int env_knob(const char* name) {
-    const char* s = std::getenv(name);
-    return (s && s[0]) ? std::atoi(s) : 0;
-}
-int tile_knob() {
-    static const int v = [] {
-        const int u = env_knob("BSQ_TILE_CHUNKS");
-        return (u == 1 || u == 2 || u == 4) ? u : 0;
-    }();
-    return v;
-}
-//   BSQ_MFMA_TILED           matrix-core GEMM: two LDS stage buffers, 256 x 256 tiles where
-//                            they fill the chip and 128 x 128 otherwise (default); 2 one wave
-//                            per 16 x 16 tile (dense); 3 128 x 128 tiles, three stage
-//                            buffers; 4 128 x 128 tiles (dense)
-int mfma_tiled_knob() {
-    static const int v = env_knob("BSQ_MFMA_TILED");
-    return v;
-}
-//   BSQ_GROUPED_TILE_ROWS    grouped matrix-core GEMM: rows per tile, whatever the rows per
-//                            group: 16 or 32 (B streamed through each wave's LDS) or 128
-//                            (tiles staged through LDS)
-int grouped_tile_rows_knob() {
-    static const int v = [] {
-        const int r = env_knob("BSQ_GROUPED_TILE_ROWS");
-        return (r == 16 || r == 32 || r == 128) ? r : 0;
-    }();
-    return v;
-}
-//   BSQ_TSF_WAVES_PER_CU     tensor-scale reduction: resident waves per CU
-//   BSQ_TSF_WAVES_PER_BLOCK  tensor-scale reduction: waves per workgroup (4, 8, 16)
+// Launch shape of the tensor-scale reduction: about this many resident
+// waves per CU, in workgroups of this many waves.
 constexpr int kTsfWavesPerCu = 16;
 constexpr int kTsfWavesPerBlock = 16;
-int tsf_waves_knob() {
-    static const int v = [] {
-        const int w = env_knob("BSQ_TSF_WAVES_PER_CU");
-        return (w >= 1 && w <= 32) ? w : 0;
-    }();
-    return v;
-}
-int tsf_block_knob() {
-    static const int v = [] {
-        const int w = env_knob("BSQ_TSF_WAVES_PER_BLOCK");
-        return (w == 4 || w == 8 || w == 16) ? w : 0;
-    }();
-    return v;
-}
 
 // Compute units of the current device, read once per device (a launch-shape
 // heuristic only: a wrong count changes speed, never results).
@@ -238,8 +201,8 @@ int st_geometry(bsq::KernelArgs& a, int u, int64_t* blocks) {
 int tsf_geometry(bsq::KernelArgs& a, int64_t* blocks, int* waves_per_block,
                  uint32_t* tiles_per_wave) {
     if (st_geometry(a, bsq::kTsfChunks, blocks) != BSQ_OK) return BSQ_ERR_INVALID_ARG;
-    const int wpc = tsf_waves_knob() ? tsf_waves_knob() : kTsfWavesPerCu;
-    const int wpb = tsf_block_knob() ? tsf_block_knob() : kTsfWavesPerBlock;
+    const int wpc = kTsfWavesPerCu;
+    const int wpb = kTsfWavesPerBlock;
     const int64_t target = (int64_t)device_cus() * wpc;
     const int64_t tpw = (a.total_tiles + target - 1) / target;
     const int64_t waves = (a.total_tiles + tpw - 1) / tpw;
@@ -273,10 +236,10 @@ int tsf_geometry(bsq::KernelArgs& a, int64_t* blocks, int* waves_per_block,
 //    the 512 routed rows x 2048 decode gather 3.07 us against 3.10 with 2
 //    chunks and 3.40 with 4; dense 128 x 4096 MXFP4 2.32 us against 2.40 and
 //    2.61.
-int launch(int format, bool grouped, bsq::KernelArgs& a, hipStream_t stream) {
+int launch(int format, bool grouped, bsq::KernelArgs& a, hipStream_t stream,
+           const bsq::LaunchEvents& ev) {
     const bool small = (double)a.rows * (double)a.K <= (double)(1 << 22);
-    int u = small ? 1 : (grouped || format != BSQ_MXFP8) ? 4 : 2;
-    if (tile_knob()) u = tile_knob();
+    const int u = small ? 1 : (grouped || format != BSQ_MXFP8) ? 4 : 2;
     int64_t blocks = 0;
     if (st_geometry(a, u, &blocks) != BSQ_OK) return BSQ_ERR_INVALID_ARG;
     if (log_enabled())
@@ -286,7 +249,7 @@ int launch(int format, bool grouped, bsq::KernelArgs& a, hipStream_t stream) {
                      grouped ? "grouped" : "dense", fmt_name(format), (long long)a.rows, a.K,
                      a.chunks_per_row, a.chunks_per_tile, (long long)a.total_tiles,
                      (long long)blocks);
-    const hipError_t e = bsq::launch_quantize(format, grouped, a, blocks, stream);
+    const hipError_t e = bsq::launch_quantize(format, grouped, a, blocks, stream, ev);
     if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -298,6 +261,7 @@ extern "C" {
 int quantize_block_scaled(int format, int block_size, int scale_layout, const void* x,
                           int64_t M, int64_t K, int64_t ldx, void* codes, int64_t ldq,
                           void* scales, int64_t lds, float tensor_sf, void* stream) {
+    const bsq::LaunchEvents ev = take_events();
     const bool work = M > 0 && K > 0;
     int st = check_common(format, block_size, scale_layout, x, M, K, ldx, codes, ldq, scales, lds,
                           work);
@@ -317,7 +281,7 @@ int quantize_block_scaled(int format, int block_size, int scale_layout, const vo
     a.rows = M;
     a.K = (int32_t)K;
     a.tensor_sf = tensor_sf;
-    return launch(format, false, a, static_cast<hipStream_t>(stream));
+    return launch(format, false, a, static_cast<hipStream_t>(stream), ev);
 }
 
 int grouped_quantize_block_scaled(int format, int block_size, int scale_layout, const void* x,
@@ -328,6 +292,7 @@ int grouped_quantize_block_scaled(int format, int block_size, int scale_layout, 
                                   int64_t num_experts, int64_t max_rows, int64_t num_scale_rows,
                                   void* codes, int64_t ldq, void* scales, int64_t lds,
                                   void* stream) {
+    const bsq::LaunchEvents ev = take_events();
     if (num_groups < 0 || max_rows < 0 || num_scale_rows < 0 || num_experts < 0)
         return fail(BSQ_ERR_INVALID_ARG,
                     "negative size (num_groups=%lld max_rows=%lld num_scale_rows=%lld "
@@ -377,11 +342,12 @@ int grouped_quantize_block_scaled(int format, int block_size, int scale_layout, 
     a.num_scale_rows = num_scale_rows;
     a.num_groups = (int32_t)num_groups;
     a.num_experts = (int32_t)num_experts;
-    return launch(format, true, a, static_cast<hipStream_t>(stream));
+    return launch(format, true, a, static_cast<hipStream_t>(stream), ev);
 }
 
 int tensor_scale_nvfp4(const void* x, int64_t M, int64_t K, int64_t ldx, float* tensor_sf_out,
                        void* stream) {
+    const bsq::LaunchEvents ev = take_events();
     if (M < 0 || K < 0) return fail(BSQ_ERR_INVALID_ARG, "negative size (M=%lld K=%lld)",
                                     (long long)M, (long long)K);
     if (K % 16 != 0) return fail(BSQ_ERR_INVALID_ARG, "K=%lld is not a multiple of 16", (long long)K);
@@ -406,7 +372,7 @@ int tensor_scale_nvfp4(const void* x, int64_t M, int64_t K, int64_t ldx, float* 
     int wpb = 0;
     if (work && tsf_geometry(a, &blocks, &wpb, &tpw) != BSQ_OK) return BSQ_ERR_INVALID_ARG;
     const hipError_t e = bsq::launch_tensor_scale(false, a, blocks, wpb, tpw, tensor_sf_out, 1,
-                                                  static_cast<hipStream_t>(stream));
+                                                  static_cast<hipStream_t>(stream), ev);
     if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -415,6 +381,7 @@ int grouped_tensor_scale_nvfp4(const void* x, int64_t num_src_rows, int64_t K, i
                                const int32_t* row_indices, const uint32_t* row_offsets,
                                const int32_t* expert_ids, int64_t num_groups, int64_t num_experts,
                                int64_t max_rows, float* tensor_sf_out, void* stream) {
+    const bsq::LaunchEvents ev = take_events();
     if (num_src_rows < 0 || K < 0 || num_groups < 0 || max_rows < 0)
         return fail(BSQ_ERR_INVALID_ARG, "negative size");
     if (num_experts < 1 || num_experts > (1 << 24))
@@ -461,7 +428,7 @@ int grouped_tensor_scale_nvfp4(const void* x, int64_t num_src_rows, int64_t K, i
     if (work && tsf_geometry(a, &blocks, &wpb, &tpw) != BSQ_OK) return BSQ_ERR_INVALID_ARG;
     const hipError_t e = bsq::launch_tensor_scale(true, a, blocks, wpb, tpw, tensor_sf_out,
                                                   (int)num_experts,
-                                                  static_cast<hipStream_t>(stream));
+                                                  static_cast<hipStream_t>(stream), ev);
     if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -469,6 +436,7 @@ int grouped_tensor_scale_nvfp4(const void* x, int64_t num_src_rows, int64_t K, i
 int dequantize_block_scaled(int format, int block_size, int scale_layout, const void* codes,
                             int64_t M, int64_t K, int64_t ldq, const void* scales, int64_t lds,
                             float tensor_sf, float* out, int64_t ldo, void* stream) {
+    const bsq::LaunchEvents ev = take_events();
     int st = check_layout(format, block_size, scale_layout, M, K);
     if (st != BSQ_OK) return st;
     if (format == BSQ_NVFP4 && !tsf_in_domain(tensor_sf))
@@ -494,9 +462,9 @@ int dequantize_block_scaled(int format, int block_size, int scale_layout, const 
     a.tensor_sf = tensor_sf;
     a.scale_layout = scale_layout;
     int64_t blocks = 0;
-    a.chunks_per_tile = tile_knob() ? tile_knob() : bsq::kDequantChunks;
+    a.chunks_per_tile = bsq::kDequantChunks;
     if (tile_geometry(a, a.chunks_per_tile, &blocks) != BSQ_OK) return BSQ_ERR_INVALID_ARG;
-    const hipError_t e = bsq::launch_dequantize(format, a, blocks, static_cast<hipStream_t>(stream));
+    const hipError_t e = bsq::launch_dequantize(format, a, blocks, static_cast<hipStream_t>(stream), ev);
     if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -508,6 +476,7 @@ int block_scaled_matmul_naive(int format, int block_size, int scale_layout,
                               int64_t ldb_s, float b_tsf,
                               int64_t M, int64_t N, int64_t K, float* c, int64_t ldc,
                               void* stream) {
+    const bsq::LaunchEvents ev = take_events();
     int st = check_layout(format, block_size, scale_layout, M, K);
     if (st != BSQ_OK) return st;
     if (N < 0) return fail(BSQ_ERR_INVALID_ARG, "negative size (N=%lld)", (long long)N);
@@ -544,7 +513,7 @@ int block_scaled_matmul_naive(int format, int block_size, int scale_layout,
     a.N = N;
     a.K = (int32_t)K;
     a.scale_layout = scale_layout;
-    const hipError_t e = bsq::launch_naive_matmul(format, a, static_cast<hipStream_t>(stream));
+    const hipError_t e = bsq::launch_naive_matmul(format, a, static_cast<hipStream_t>(stream), ev);
     if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -556,6 +525,7 @@ int block_scaled_matmul_mfma(int format, int block_size, int scale_layout,
                              int64_t ldb_s,
                              int64_t M, int64_t N, int64_t K, float* c, int64_t ldc,
                              void* stream) {
+    const bsq::LaunchEvents ev = take_events();
     int st = check_layout(format, block_size, scale_layout, M, K);
     if (st != BSQ_OK) return st;
     if (format == BSQ_NVFP4)
@@ -600,8 +570,7 @@ int block_scaled_matmul_mfma(int format, int block_size, int scale_layout,
     a.N = N;
     a.K = (int32_t)K;
     a.scale_layout = scale_layout;
-    a.tiled = mfma_tiled_knob() == 2 ? 0 : mfma_tiled_knob() == 3 ? 3 : mfma_tiled_knob() == 4 ? 4 : 1;
-    const hipError_t e = bsq::launch_mfma_matmul(format, a, static_cast<hipStream_t>(stream));
+    const hipError_t e = bsq::launch_mfma_matmul(format, a, static_cast<hipStream_t>(stream), ev);
     if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -615,6 +584,7 @@ int grouped_block_scaled_matmul_mfma(int format, int block_size, int scale_layou
                                      const void* b_codes, int64_t ldb_q, const void* b_scales,
                                      int64_t ldb_s, int64_t num_experts,
                                      int64_t N, int64_t K, float* c, int64_t ldc, void* stream) {
+    const bsq::LaunchEvents ev = take_events();
     int st = check_layout(format, block_size, scale_layout, max_rows, K);
     if (st != BSQ_OK) return st;
     if (format == BSQ_NVFP4)
@@ -669,8 +639,7 @@ int grouped_block_scaled_matmul_mfma(int format, int block_size, int scale_layou
     // rows per expert 90 / 92 / 106 / 117 us; at 8, 103 / 97 / 114 / 108; at
     // 16, 125 / 108 / 117 / 119; at 32, 190 / 155 / 148 / 124; at 64, 339 /
     // 229 / 224 / 130.
-    int tile_m = max_rows <= 4 * num_groups ? 16 : max_rows <= 16 * num_groups ? 32 : 128;
-    if (grouped_tile_rows_knob()) tile_m = grouped_tile_rows_knob();
+    const int tile_m = max_rows <= 4 * num_groups ? 16 : max_rows <= 16 * num_groups ? 32 : 128;
     g.row_blocks = tile_m < 128 ? tile_m / 16 : 0;
     const int64_t tile_n = g.row_blocks ? bsq::kDecodeTileCols : 128;
     g.m_tiles = (max_rows + tile_m - 1) / tile_m + num_groups;  // each group adds at most one
@@ -692,10 +661,19 @@ int grouped_block_scaled_matmul_mfma(int format, int block_size, int scale_layou
     a.N = N;
     a.K = (int32_t)K;
     a.scale_layout = scale_layout;
-    a.tiled = mfma_tiled_knob() == 3 ? 3 : 1;
     const hipError_t e = bsq::launch_mfma_grouped_matmul(format, a, g,
-                                                         static_cast<hipStream_t>(stream));
+                                                         static_cast<hipStream_t>(stream), ev);
     if (e != hipSuccess) return fail(BSQ_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int bsq_time_next_launch(void* start_event, void* stop_event) {
+    if ((start_event == nullptr) != (stop_event == nullptr)) {
+        g_armed = bsq::LaunchEvents{};
+        return fail(BSQ_ERR_INVALID_ARG, "start_event and stop_event must both be given, or neither");
+    }
+    g_armed.start = static_cast<hipEvent_t>(start_event);
+    g_armed.stop = static_cast<hipEvent_t>(stop_event);
     return ok();
 }
 

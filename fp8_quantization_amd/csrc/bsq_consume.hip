@@ -195,9 +195,7 @@ __global__ void __launch_bounds__(kThreadsPerBlock) naive_matmul_kernel(const Ge
 // v_mfma_scale_f32_16x16x128_f8f6f4, reading the quantizers' MX output as
 // is: codes row-major, scales in the MFMA layout.  Per 512 elements of K each
 // lane takes one scale dword per operand, whose byte t feeds K step t
-// (opsel = t).  Two forms: the simple one below (one wave per 16 x 16 tile
-// of c, fragments loaded straight from the code rows; kept behind a knob)
-// and the LDS-tiled one after it, which the library uses.
+// (opsel = t).
 //
 // Operand fragments (measured with one-wave probes of known operands):
 // lane l serves row l % 16 of its operand and group g = l / 16;
@@ -222,52 +220,6 @@ __device__ __forceinline__ mfma_v8i load_fragment(const uint8_t* row, int k0, in
         v = (mfma_v8i){q.x, q.y, q.z, q.w, 0, 0, 0, 0};
     }
     return v;
-}
-
-template <int FMT, int T>
-__device__ __forceinline__ mfma_v4f mfma_step(const uint8_t* arow, const uint8_t* brow, int k0,
-                                             int g, bool va, bool vb, uint32_t sa, uint32_t sb,
-                                             mfma_v4f acc) {
-    constexpr int kFmt = FMT == 1 ? 0 : 4;  // instruction format codes: 0 E4M3, 4 E2M1
-    const mfma_v8i fa = load_fragment<FMT>(arow, k0, g, va);
-    const mfma_v8i fb = load_fragment<FMT>(brow, k0, g, vb);
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb, acc, kFmt, kFmt, T, (int)sa, T,
-                                                            (int)sb);
-}
-
-template <int FMT>
-__global__ void __launch_bounds__(kThreadsPerBlock) mfma_matmul_kernel(const GemmArgs a,
-                                                                         int64_t tiles_n,
-                                                                         int64_t tiles) {
-    const int lane = (int)(threadIdx.x & (kWaveSize - 1));
-    const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWaveSize;
-    if (t >= tiles) return;
-    const int64_t m0 = (t / tiles_n) * 16, n0 = (t % tiles_n) * 16;
-    const int r = lane & 15, g = lane >> 4;
-    const bool va = m0 + r < a.M, vb = n0 + r < a.N;
-    const uint8_t* arow = a.a_codes + (m0 + r) * a.lda_q;
-    const uint8_t* brow = a.b_codes + (n0 + r) * a.ldb_q;
-    // this lane's dword of each 256-byte scale record of the tile's row groups
-    const uint8_t* as = a.a_scales + (m0 >> 4) * a.lda_s + 4 * lane;
-    const uint8_t* bs = a.b_scales + (n0 >> 4) * a.ldb_s + 4 * lane;
-    mfma_v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k0 = 0; k0 < a.K; k0 += 512) {
-        // rows past M / N: zero codes under scale 2^0, so no unwritten byte enters
-        const uint32_t sa = va ? *reinterpret_cast<const uint32_t*>(as + (k0 / 512) * 256)
-                               : 0x7F7F7F7Fu;
-        const uint32_t sb = vb ? *reinterpret_cast<const uint32_t*>(bs + (k0 / 512) * 256)
-                               : 0x7F7F7F7Fu;
-        acc = mfma_step<FMT, 0>(arow, brow, k0, g, va, vb, sa, sb, acc);
-        if (k0 + 128 < a.K) acc = mfma_step<FMT, 1>(arow, brow, k0 + 128, g, va, vb, sa, sb, acc);
-        if (k0 + 256 < a.K) acc = mfma_step<FMT, 2>(arow, brow, k0 + 256, g, va, vb, sa, sb, acc);
-        if (k0 + 384 < a.K) acc = mfma_step<FMT, 3>(arow, brow, k0 + 384, g, va, vb, sa, sb, acc);
-    }
-    const int64_t col = n0 + r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t row = m0 + 4 * g + i;
-        if (row < a.M && col < a.N) a.c[row * a.ldc + col] = acc[i];
-    }
 }
 
 // Tiled form: a workgroup computes a TM x TN tile of c with a WAVES_M x
@@ -594,39 +546,30 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const 
 // The stage buffers are separate LDS objects: the compiler then knows which
 // buffer each LDS read and each direct load touches, and waits only for the
 // loads into the buffer being read.
-#define BSQ_STAGE_BUFFERS(NBUF, BYTES)                                                     \
+// Two stage buffers (a third leaves one 128 x 128 workgroup per CU and
+// measured slower).
+#define BSQ_STAGE_BUFFERS(BYTES)                                                           \
     __shared__ __attribute__((aligned(16))) uint8_t stage0[BYTES];                         \
-    __shared__ __attribute__((aligned(16))) uint8_t stage1[BYTES];                         \
-    __shared__ __attribute__((aligned(16))) uint8_t stage2[(NBUF) >= 3 ? (BYTES) : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t stage1[BYTES];
 
-template <int FMT, int NBUF, class Cfg>
-__device__ __forceinline__ void run_tile(const GemmTile& d, uint8_t* b0, uint8_t* b1,
-                                         uint8_t* b2) {
-    if constexpr (NBUF == 2) {
-        uint8_t* const bufs[2] = {b0, b1};
-        gemm_tile_dma<FMT, 2, Cfg>(d, bufs);
-    } else {
-        uint8_t* const bufs[3] = {b0, b1, b2};
-        gemm_tile_dma<FMT, 3, Cfg>(d, bufs);
-    }
-}
-
-template <int FMT, int NBUF, class Cfg>
+template <int FMT, class Cfg>
 __global__ void __launch_bounds__(64 * Cfg::NW) mfma_gemm_tiled_kernel(const GemmArgs a,
                                                                         int64_t tiles_n) {
-    BSQ_STAGE_BUFFERS(NBUF, Cfg::kStageBytes)
+    BSQ_STAGE_BUFFERS(Cfg::kStageBytes)
     GemmTile d;
     dense_desc<Cfg::TM, Cfg::TN>(a, tiles_n, d);
-    run_tile<FMT, NBUF, Cfg>(d, stage0, stage1, stage2);
+    uint8_t* const bufs[2] = {stage0, stage1};
+    gemm_tile_dma<FMT, 2, Cfg>(d, bufs);
 }
 
-template <int FMT, int NBUF>
+template <int FMT>
 __global__ void __launch_bounds__(64 * Tile128::NW)
 mfma_gemm_grouped_kernel(const GemmArgs a, const GroupedGemmArgs g) {
-    BSQ_STAGE_BUFFERS(NBUF, Tile128::kStageBytes)
+    BSQ_STAGE_BUFFERS(Tile128::kStageBytes)
     GemmTile d;
     if (!grouped_desc<kTileM, kTileN>(a, g, d)) return;
-    run_tile<FMT, NBUF, Tile128>(d, stage0, stage1, stage2);
+    uint8_t* const bufs[2] = {stage0, stage1};
+    gemm_tile_dma<FMT, 2, Tile128>(d, bufs);
 }
 
 // ------------------------------------------------------------ decode regime
@@ -861,154 +804,111 @@ mfma_gemm_skinny_kernel(const GemmArgs a, int64_t tiles_n) {
 }
 
 template <int FMT, class Cfg>
-hipError_t launch_tiles(const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_tiles(const GemmArgs& a, hipStream_t stream, const LaunchEvents& ev) {
     const int64_t tiles_n = (a.N + Cfg::TN - 1) / Cfg::TN;
     const int64_t tiles = ((a.M + Cfg::TM - 1) / Cfg::TM) * tiles_n;
-    const dim3 grid((uint32_t)tiles), block(64 * Cfg::NW);
-    // two stage buffers; three (128 x 128 only) leave one workgroup per CU and
-    // measured slower
-    if constexpr (Cfg::kStageBytes * 3 <= 160 * 1024) {
-        if (a.tiled == 3) {
-            hipLaunchKernelGGL((mfma_gemm_tiled_kernel<FMT, 3, Cfg>), grid, block, 0, stream, a,
-                               tiles_n);
-            return hipGetLastError();
-        }
-    }
-    hipLaunchKernelGGL((mfma_gemm_tiled_kernel<FMT, 2, Cfg>), grid, block, 0, stream, a, tiles_n);
-    return hipGetLastError();
+    return launch_kernel(mfma_gemm_tiled_kernel<FMT, Cfg>, dim3((uint32_t)tiles),
+                         dim3(64 * Cfg::NW), 0, stream, ev, a, tiles_n);
 }
 
 template <int FMT, int MB>
-hipError_t launch_mfma_skinny_mb(const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_mfma_skinny_mb(const GemmArgs& a, hipStream_t stream, const LaunchEvents& ev) {
     using Sh = DenseSkinnyShape<FMT, MB>;
     const int64_t tiles_n = (a.N + Sh::kCols - 1) / Sh::kCols;
     const int64_t tiles = ((a.M + 16 * MB - 1) / (16 * MB)) * tiles_n;
-    hipLaunchKernelGGL((mfma_gemm_skinny_kernel<FMT, MB>), dim3((uint32_t)tiles),
-                       dim3(64 * Sh::kWaves), 0, stream, a, tiles_n);
-    return hipGetLastError();
+    return launch_kernel(mfma_gemm_skinny_kernel<FMT, MB>, dim3((uint32_t)tiles),
+                         dim3(64 * Sh::kWaves), 0, stream, ev, a, tiles_n);
 }
 
+// Few rows (M <= 32): 16- or 32-row tiles streaming B.  Measured on
+// N = 16384, K = 7168 against 128 x 128 tiles: MXFP4 15.0 / 19.9 us at
+// M = 16 / 32 against 23.4 / 23.8; MXFP8 21.4 / 34.1 against 39.6 / 40.3.
+// Otherwise 256 x 256 tiles (8 waves, 144 KiB of LDS in two stages, one
+// workgroup per CU) once they alone fill the chip; 128 x 128 ones otherwise.
 template <int FMT>
-hipError_t launch_mfma_skinny(const GemmArgs& a, hipStream_t stream) {
-    return a.M <= 16 ? launch_mfma_skinny_mb<FMT, 1>(a, stream)
-                     : launch_mfma_skinny_mb<FMT, 2>(a, stream);
-}
-
-// Few rows (M <= 32, by default): 16- or 32-row tiles streaming B.
-// Measured on N = 16384, K = 7168 against 128 x 128 tiles: MXFP4 15.0 /
-// 19.9 us at M = 16 / 32 against 23.4 / 23.8; MXFP8 21.4 / 34.1 against
-// 39.6 / 40.3.  Otherwise 256 x 256 tiles (8 waves, 144 KiB of LDS in two
-// stages, one workgroup per CU) once they alone fill the chip; 128 x 128
-// ones otherwise, or on request.
-template <int FMT>
-hipError_t launch_mfma_tiled(const GemmArgs& a, hipStream_t stream) {
-    if (a.tiled == 1 && a.M <= 32) return launch_mfma_skinny<FMT>(a, stream);
+hipError_t launch_mfma_tiled(const GemmArgs& a, hipStream_t stream, const LaunchEvents& ev) {
+    if (a.M <= 32)
+        return a.M <= 16 ? launch_mfma_skinny_mb<FMT, 1>(a, stream, ev)
+                         : launch_mfma_skinny_mb<FMT, 2>(a, stream, ev);
     const int64_t big = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-    if (a.tiled != 3 && a.tiled != 4 && big >= 256) return launch_tiles<FMT, Tile256>(a, stream);
-    return launch_tiles<FMT, Tile128>(a, stream);
+    if (big >= 256) return launch_tiles<FMT, Tile256>(a, stream, ev);
+    return launch_tiles<FMT, Tile128>(a, stream, ev);
 }
 
 template <int FMT>
-hipError_t launch_mfma_mm(const GemmArgs& a, hipStream_t stream) {
-    const int64_t tiles_n = (a.N + 15) / 16;
-    const int64_t tiles = ((a.M + 15) / 16) * tiles_n;
-    const int64_t blocks = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((mfma_matmul_kernel<FMT>), dim3((uint32_t)blocks), dim3(kThreadsPerBlock), 0,
-                       stream, a, tiles_n, tiles);
-    return hipGetLastError();
+hipError_t launch_dq(const DequantArgs& a, int64_t blocks, hipStream_t stream,
+                     const LaunchEvents& ev) {
+    if (a.chunks_per_tile != kDequantChunks) return hipErrorInvalidValue;
+    return launch_kernel(dequant_kernel<FMT, kDequantChunks>, dim3((uint32_t)blocks),
+                         dim3(kThreadsPerBlock), 0, stream, ev, a);
 }
 
 template <int FMT>
-hipError_t launch_dq(const DequantArgs& a, int64_t blocks, hipStream_t stream) {
-    switch (a.chunks_per_tile) {
-        case 1:
-            hipLaunchKernelGGL((dequant_kernel<FMT, 1>), dim3((uint32_t)blocks),
-                               dim3(kThreadsPerBlock), 0, stream, a);
-            break;
-        case 2:
-            hipLaunchKernelGGL((dequant_kernel<FMT, 2>), dim3((uint32_t)blocks),
-                               dim3(kThreadsPerBlock), 0, stream, a);
-            break;
-        case 4:
-            hipLaunchKernelGGL((dequant_kernel<FMT, 4>), dim3((uint32_t)blocks),
-                               dim3(kThreadsPerBlock), 0, stream, a);
-            break;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
-
-template <int FMT>
-hipError_t launch_mm(const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_mm(const GemmArgs& a, hipStream_t stream, const LaunchEvents& ev) {
     const int64_t blocks = (a.M * a.N + kThreadsPerBlock - 1) / kThreadsPerBlock;
-    hipLaunchKernelGGL((naive_matmul_kernel<FMT>), dim3((uint32_t)blocks), dim3(kThreadsPerBlock),
-                       0, stream, a);
-    return hipGetLastError();
+    return launch_kernel(naive_matmul_kernel<FMT>, dim3((uint32_t)blocks),
+                         dim3(kThreadsPerBlock), 0, stream, ev, a);
 }
 
 }  // namespace
 
-hipError_t launch_dequantize(int fmt, const DequantArgs& a, int64_t blocks, hipStream_t stream) {
+hipError_t launch_dequantize(int fmt, const DequantArgs& a, int64_t blocks, hipStream_t stream,
+                             const LaunchEvents& ev) {
     switch (fmt) {
-        case 0: return launch_dq<0>(a, blocks, stream);
-        case 1: return launch_dq<1>(a, blocks, stream);
-        case 2: return launch_dq<2>(a, blocks, stream);
+        case 0: return launch_dq<0>(a, blocks, stream, ev);
+        case 1: return launch_dq<1>(a, blocks, stream, ev);
+        case 2: return launch_dq<2>(a, blocks, stream, ev);
         default: return hipErrorInvalidValue;
     }
 }
 
 namespace {
 template <int FMT>
-hipError_t launch_mfma_grouped(const GemmArgs& a, const GroupedGemmArgs& g, hipStream_t stream) {
+hipError_t launch_mfma_grouped(const GemmArgs& a, const GroupedGemmArgs& g, hipStream_t stream,
+                               const LaunchEvents& ev) {
     if (g.row_blocks > 0) {
         const dim3 grid((uint32_t)g.m_tiles,
                         (uint32_t)((a.N + kDecodeTileCols - 1) / kDecodeTileCols));
         switch (g.row_blocks) {
             case 1:
-                hipLaunchKernelGGL((mfma_gemm_grouped_skinny_kernel<FMT, 1>), grid,
-                                   dim3(64 * SkinnyShape<FMT, 1>::kWaves), 0, stream, a, g);
-                break;
+                return launch_kernel(mfma_gemm_grouped_skinny_kernel<FMT, 1>, grid,
+                                     dim3(64 * SkinnyShape<FMT, 1>::kWaves), 0, stream, ev, a, g);
             case 2:
-                hipLaunchKernelGGL((mfma_gemm_grouped_skinny_kernel<FMT, 2>), grid,
-                                   dim3(64 * SkinnyShape<FMT, 2>::kWaves), 0, stream, a, g);
-                break;
+                return launch_kernel(mfma_gemm_grouped_skinny_kernel<FMT, 2>, grid,
+                                     dim3(64 * SkinnyShape<FMT, 2>::kWaves), 0, stream, ev, a, g);
             default: return hipErrorInvalidValue;
         }
-        return hipGetLastError();
     }
     const dim3 grid((uint32_t)g.m_tiles, (uint32_t)((a.N + kTileN - 1) / kTileN));
-    const dim3 block(64 * Tile128::NW);
-    if (a.tiled == 3)
-        hipLaunchKernelGGL((mfma_gemm_grouped_kernel<FMT, 3>), grid, block, 0, stream, a, g);
-    else
-        hipLaunchKernelGGL((mfma_gemm_grouped_kernel<FMT, 2>), grid, block, 0, stream, a, g);
-    return hipGetLastError();
+    return launch_kernel(mfma_gemm_grouped_kernel<FMT>, grid, dim3(64 * Tile128::NW), 0, stream,
+                         ev, a, g);
 }
 }  // namespace
 
 hipError_t launch_mfma_grouped_matmul(int fmt, const GemmArgs& a, const GroupedGemmArgs& g,
-                                      hipStream_t stream) {
+                                      hipStream_t stream, const LaunchEvents& ev) {
     switch (fmt) {
-        case 0: return launch_mfma_grouped<0>(a, g, stream);
-        case 1: return launch_mfma_grouped<1>(a, g, stream);
+        case 0: return launch_mfma_grouped<0>(a, g, stream, ev);
+        case 1: return launch_mfma_grouped<1>(a, g, stream, ev);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_mfma_matmul(int fmt, const GemmArgs& a, hipStream_t stream) {
-    const bool tiled = a.tiled != 0;
+hipError_t launch_mfma_matmul(int fmt, const GemmArgs& a, hipStream_t stream,
+                              const LaunchEvents& ev) {
     switch (fmt) {
-        case 0: return tiled ? launch_mfma_tiled<0>(a, stream) : launch_mfma_mm<0>(a, stream);
-        case 1: return tiled ? launch_mfma_tiled<1>(a, stream) : launch_mfma_mm<1>(a, stream);
+        case 0: return launch_mfma_tiled<0>(a, stream, ev);
+        case 1: return launch_mfma_tiled<1>(a, stream, ev);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_naive_matmul(int fmt, const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_naive_matmul(int fmt, const GemmArgs& a, hipStream_t stream,
+                               const LaunchEvents& ev) {
     switch (fmt) {
-        case 0: return launch_mm<0>(a, stream);
-        case 1: return launch_mm<1>(a, stream);
-        case 2: return launch_mm<2>(a, stream);
+        case 0: return launch_mm<0>(a, stream, ev);
+        case 1: return launch_mm<1>(a, stream, ev);
+        case 2: return launch_mm<2>(a, stream, ev);
         default: return hipErrorInvalidValue;
     }
 }

@@ -2,12 +2,32 @@
 // (bsq_api.cpp) and the gfx950 kernels (bsq_kernels.hip).  Not installed.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace bsq {
 
-// Work is cut into tiles: up to chunks_per_tile (1, 2, 4 or 8) consecutive
+// Events a caller armed for the main kernel of its next call (both null: none).
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+
+// Launch `kernel`; with events, through hipExtLaunchKernel, which binds them to
+// the kernel's own dispatch: their elapsed time is the kernel's execution,
+// without the gaps that events recorded around the launch would add.
+template <typename F, typename... Args>
+inline hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t lds_bytes,
+                                hipStream_t stream, const LaunchEvents& ev, Args... args) {
+    if (ev.start)
+        hipExtLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, ev.start, ev.stop, 0u,
+                              args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, args...);
+    return hipGetLastError();
+}
+
+// Work is cut into tiles: up to chunks_per_tile (1, 2 or 4) consecutive
 // chunks of one row, a chunk being 512 BF16 elements (64 lanes x one 16-byte
 // load).  One wave converts one tile.
 constexpr int kWaveSize = 64;
@@ -102,14 +122,15 @@ struct GemmArgs {
     int64_t M, N;
     int32_t K;
     int32_t scale_layout;   // as in KernelArgs
-    int32_t tiled;          // MFMA GEMM: 1 workgroup tiles sized to the problem, 3 128 x 128 with
-                            // three LDS stage buffers, 4 128 x 128; 0 one wave per 16 x 16
 };
 
-hipError_t launch_dequantize(int fmt, const DequantArgs& a, int64_t blocks, hipStream_t stream);
-hipError_t launch_naive_matmul(int fmt, const GemmArgs& a, hipStream_t stream);
+hipError_t launch_dequantize(int fmt, const DequantArgs& a, int64_t blocks, hipStream_t stream,
+                             const LaunchEvents& ev);
+hipError_t launch_naive_matmul(int fmt, const GemmArgs& a, hipStream_t stream,
+                               const LaunchEvents& ev);
 // MX formats, scales in the MFMA layout, K % 128 == 0, 16-byte aligned code rows.
-hipError_t launch_mfma_matmul(int fmt, const GemmArgs& a, hipStream_t stream);
+hipError_t launch_mfma_matmul(int fmt, const GemmArgs& a, hipStream_t stream,
+                              const LaunchEvents& ev);
 
 // Grouped per-expert GEMM: A rows grouped by row_offsets (scale rows by
 // scales_offsets), B = num_experts stacked [N, K] operands; GemmArgs.M unused.
@@ -130,19 +151,20 @@ struct GroupedGemmArgs {
                                      // 128-row tiles staged through LDS
 };
 hipError_t launch_mfma_grouped_matmul(int fmt, const GemmArgs& a, const GroupedGemmArgs& g,
-                                      hipStream_t stream);
+                                      hipStream_t stream, const LaunchEvents& ev);
 
 // Launch the dense (grouped = false) or grouped kernel for format fmt
 // (0 MXFP4, 1 MXFP8, 2 NVFP4).  Returns the launch status.
 hipError_t launch_quantize(int fmt, bool grouped, const KernelArgs& a, int64_t blocks,
-                           hipStream_t stream);
+                           hipStream_t stream, const LaunchEvents& ev);
 
 // NVFP4 tensor scale(s) into out[0 .. n_out): zero it, fold in the amax of
 // every tile of a (kTsfChunks chunks per tile; blocks workgroups of
 // waves_per_block waves, each wave taking tiles_per_wave consecutive tiles;
 // blocks = 0 skips this pass), and turn each amax into its tensor scale.
+// Events, when armed, time the amax pass.
 hipError_t launch_tensor_scale(bool grouped, const KernelArgs& a, int64_t blocks,
                                int waves_per_block, uint32_t tiles_per_wave, float* out, int n_out,
-                               hipStream_t stream);
+                               hipStream_t stream, const LaunchEvents& ev);
 
 }  // namespace bsq

@@ -729,18 +729,21 @@ tsf_amax_kernel(const KernelArgs a, uint32_t* acc, uint32_t tiles_per_wave, int 
 }
 
 template <int FMT, bool GROUPED, int U>
-hipError_t launch(const KernelArgs& a, int64_t blocks, hipStream_t stream) {
-    hipLaunchKernelGGL((quantize_kernel<FMT, GROUPED, U>), dim3((uint32_t)blocks),
-                       dim3(kThreadsPerBlock), 0, stream, a);
-    return hipGetLastError();
+hipError_t launch(const KernelArgs& a, int64_t blocks, hipStream_t stream, const LaunchEvents& ev) {
+    return launch_kernel(quantize_kernel<FMT, GROUPED, U>, dim3((uint32_t)blocks),
+                         dim3(kThreadsPerBlock), 0, stream, ev, a);
 }
 
+// The tile sizes the host picks: 1 chunk for small problems; for large ones
+// 2 (dense MXFP8) or 4 (the FP4 formats, and every grouped form).  Only
+// those are built.
 template <int FMT, bool GROUPED>
-hipError_t launch_u(const KernelArgs& a, int64_t blocks, hipStream_t stream) {
+hipError_t launch_u(const KernelArgs& a, int64_t blocks, hipStream_t stream,
+                    const LaunchEvents& ev) {
+    constexpr int kLarge = (FMT == 1 && !GROUPED) ? 2 : 4;
     switch (a.chunks_per_tile) {
-        case 1: return launch<FMT, GROUPED, 1>(a, blocks, stream);
-        case 2: return launch<FMT, GROUPED, 2>(a, blocks, stream);
-        case 4: return launch<FMT, GROUPED, 4>(a, blocks, stream);
+        case 1: return launch<FMT, GROUPED, 1>(a, blocks, stream, ev);
+        case kLarge: return launch<FMT, GROUPED, kLarge>(a, blocks, stream, ev);
         default: return hipErrorInvalidValue;
     }
 }
@@ -749,39 +752,34 @@ hipError_t launch_u(const KernelArgs& a, int64_t blocks, hipStream_t stream) {
 
 hipError_t launch_tensor_scale(bool grouped, const KernelArgs& a, int64_t blocks,
                                int waves_per_block, uint32_t tiles_per_wave, float* out, int n_out,
-                               hipStream_t stream) {
+                               hipStream_t stream, const LaunchEvents& ev) {
     uint32_t* acc = reinterpret_cast<uint32_t*>(out);
     const uint32_t small_blocks = (uint32_t)((n_out + kThreadsPerBlock - 1) / kThreadsPerBlock);
-    hipLaunchKernelGGL(tsf_zero_kernel, dim3(small_blocks), dim3(kThreadsPerBlock), 0, stream, acc,
-                       n_out);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_kernel(tsf_zero_kernel, dim3(small_blocks), dim3(kThreadsPerBlock), 0,
+                                 stream, LaunchEvents{}, acc, n_out);
     if (e != hipSuccess) return e;
     if (blocks > 0) {
-        const size_t lds_bytes = ((n_out <= kTsfLdsSlots) ? (size_t)n_out : 0u) * 4u + 8u;
+        const uint32_t lds_bytes = ((n_out <= kTsfLdsSlots) ? (uint32_t)n_out : 0u) * 4u + 8u;
         const dim3 block((uint32_t)(waves_per_block * kWaveSize));
-        if (grouped)
-            hipLaunchKernelGGL((tsf_amax_kernel<true>), dim3((uint32_t)blocks), block, lds_bytes,
-                               stream, a, acc, tiles_per_wave, n_out);
-        else
-            hipLaunchKernelGGL((tsf_amax_kernel<false>), dim3((uint32_t)blocks), block, lds_bytes,
-                               stream, a, acc, tiles_per_wave, n_out);
-        e = hipGetLastError();
+        e = grouped ? launch_kernel(tsf_amax_kernel<true>, dim3((uint32_t)blocks), block,
+                                    lds_bytes, stream, ev, a, acc, tiles_per_wave, n_out)
+                    : launch_kernel(tsf_amax_kernel<false>, dim3((uint32_t)blocks), block,
+                                    lds_bytes, stream, ev, a, acc, tiles_per_wave, n_out);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(tsf_finish_kernel, dim3(small_blocks), dim3(kThreadsPerBlock), 0, stream,
-                       acc, n_out);
-    return hipGetLastError();
+    return launch_kernel(tsf_finish_kernel, dim3(small_blocks), dim3(kThreadsPerBlock), 0, stream,
+                         LaunchEvents{}, acc, n_out);
 }
 
 hipError_t launch_quantize(int fmt, bool grouped, const KernelArgs& a, int64_t blocks,
-                           hipStream_t stream) {
+                           hipStream_t stream, const LaunchEvents& ev) {
     switch (fmt * 2 + (grouped ? 1 : 0)) {
-        case 0: return launch_u<0, false>(a, blocks, stream);
-        case 1: return launch_u<0, true>(a, blocks, stream);
-        case 2: return launch_u<1, false>(a, blocks, stream);
-        case 3: return launch_u<1, true>(a, blocks, stream);
-        case 4: return launch_u<2, false>(a, blocks, stream);
-        case 5: return launch_u<2, true>(a, blocks, stream);
+        case 0: return launch_u<0, false>(a, blocks, stream, ev);
+        case 1: return launch_u<0, true>(a, blocks, stream, ev);
+        case 2: return launch_u<1, false>(a, blocks, stream, ev);
+        case 3: return launch_u<1, true>(a, blocks, stream, ev);
+        case 4: return launch_u<2, false>(a, blocks, stream, ev);
+        case 5: return launch_u<2, true>(a, blocks, stream, ev);
         default: return hipErrorInvalidValue;
     }
 }

@@ -147,7 +147,13 @@ int quantize_block_scaled(int format, int block_size, int scale_layout,
  *   num_groups       >= 0.  num_experts >= 1 for NVFP4.
  *   max_rows         host-side bound on routed rows; sizes the grid, so the
  *                    device offsets are never read on the host.  <= 2^32.
- *   num_scale_rows   rows in the scales buffer.
+ *   num_scale_rows   rows in the scales buffer.  This argument is the one
+ *                    deliberate addition to the grouped kernel page's
+ *                    argument list (offsets, ids, per-expert scale and gather
+ *                    carry no buffer sizes there): with it the kernel skips a
+ *                    routed row whose scale row would fall outside the buffer,
+ *                    so violated device-side preconditions cannot make it
+ *                    write out of bounds.
  *   codes, ldq       uint8 [max_rows, ldq], as for the dense form.
  *   scales, lds      uint8 [num_scale_rows, lds] (row-major), or the MFMA
  *                    layout over num_scale_rows rows.
@@ -338,6 +344,22 @@ int grouped_block_scaled_matmul_mfma(int format, int block_size, int scale_layou
                                      const void* b_codes, int64_t ldb_q, const void* b_scales,
                                      int64_t ldb_s, int64_t num_experts,
                                      int64_t N, int64_t K, float* c, int64_t ldc, void* stream);
+
+/*
+ * Kernel timing, a measurement aid (no counterpart on the pages).  Arms the
+ * calling thread's next call into this library that takes a stream: that call
+ * launches its main kernel -- the quantizer, the amax pass of the tensor
+ * scale, the dequantizer or the GEMM -- through hipExtLaunchKernel with these
+ * events bound to the kernel's own dispatch, so hipEventElapsedTime(start,
+ * stop) is that kernel's execution time on the GPU, without the gaps between
+ * launches that events recorded around the call would include.  Both are
+ * hipEvent_t created with timing enabled, owned by the caller.  The next such
+ * call consumes the pair whatever it returns; if it launches nothing (a no-op
+ * or an error), the events are not recorded.  Both NULL disarms.
+ *   Returns BSQ_OK, or BSQ_ERR_INVALID_ARG (and disarms) when exactly one is
+ *   NULL.
+ */
+int bsq_time_next_launch(void* start_event, void* stop_event);
 
 /* Message of the calling thread's most recent call into this library when
    that call returned a non-OK status ("" after a call that returned

@@ -179,6 +179,26 @@ def block_scaled_matmul(a_codes, a_scales, b_codes, b_scales, fmt, K, a_tsf=1.0,
     return c
 
 
+def block_scaled_matmul_blas(a_codes, a_scales, b_codes, b_scales, fmt, K, a_tsf=1.0, b_tsf=1.0,
+                             bs=None):
+    """The same c = A @ B.T as ``block_scaled_matmul`` (fp32-rounded
+    dequantized operands, products and sums in float64, a NaN anywhere in row
+    m of A or row n of B making c[m, n] NaN), with numpy's float64 matrix
+    product as the summation step instead of the C loop: the sums are taken
+    in another order, so the two agree to within the float64 rounding of K
+    additions (about K * 2^-53 of sum |a b|), far below any float32 error.
+    For full-size checks, where the C loop would take minutes."""
+    A = dequantize(a_codes, a_scales, fmt, K, a_tsf, bs).astype(np.float32).astype(np.float64)
+    B = dequantize(b_codes, b_scales, fmt, K, b_tsf, bs).astype(np.float32).astype(np.float64)
+    nan_a, nan_b = np.isnan(A).any(axis=1), np.isnan(B).any(axis=1)
+    A[nan_a] = 0.0
+    B[nan_b] = 0.0
+    c = A @ B.T
+    c[nan_a, :] = np.nan
+    c[:, nan_b] = np.nan
+    return c
+
+
 def mfma16_scale_bytes(rows: int, nblk: int) -> int:
     """Row-group stride (bytes) of the packed MFMA scale layout: 256 bytes per
     16 rows x 512 elements record."""

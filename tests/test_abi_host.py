@@ -61,7 +61,8 @@ def test_header_declares_the_abi():
                                            "dequantize_block_scaled",
                                            "block_scaled_matmul_naive",
                                            "block_scaled_matmul_mfma",
-                                           "grouped_block_scaled_matmul_mfma"])
+                                           "grouped_block_scaled_matmul_mfma",
+                                           "bsq_time_next_launch"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -92,6 +93,21 @@ def test_last_error_is_cleared_by_a_successful_call(lib):
     assert b"K=48" in lib.bsq_last_error()
     assert dense(lib, M=0, x=None, codes=None, scales=None) == OK   # no-op, returns BSQ_OK
     assert lib.bsq_last_error() == b""
+
+
+def test_time_next_launch_needs_both_events_or_neither(lib):
+    """Arming takes a start and a stop event; one alone is rejected (and
+    disarms), none disarms.  No event is touched on the host."""
+    lib.bsq_time_next_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.bsq_time_next_launch(FAKE, None) == INVALID
+    assert b"both" in lib.bsq_last_error()
+    assert lib.bsq_time_next_launch(None, FAKE) == INVALID
+    assert lib.bsq_time_next_launch(None, None) == OK
+    assert lib.bsq_last_error() == b""
+    # armed events are consumed by the next call, even one that fails validation
+    assert lib.bsq_time_next_launch(FAKE, FAKE) == OK
+    assert dense(lib, K=48) == INVALID
+    assert dense(lib, M=0, x=None, codes=None, scales=None) == OK
 
 
 def test_unsupported_layout(lib):

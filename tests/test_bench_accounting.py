@@ -73,12 +73,45 @@ def test_dense_decode_gemm_bytes():
     """16 rows against 16384 x 7168 MXFP4 weights: operands and their scale
     records read once, c written; HBM-bound (bytes at 8 TB/s outlast the
     flops at the fp4 matrix peak)."""
-    c = bench.load_workload("mfma_gemm_mxfp4_m16")
+    c = W.gemm_random_operands(W.MXFP4, 16, 16384, 7168, seed=1205)
     nb, elems = bench.algorithmic_bytes(c)
     rec = (7168 // 512) * 256
     assert nb == 16 * 3584 + 16384 * 3584 + (1 + 1024) * rec + 4 * 16 * 16384
     assert elems == 16 * 16384
     assert nb / bench.PEAK_HBM_GBS / 1e9 > bench.gemm_flops(c) / bench.PEAK_MFMA_TFLOPS[0] / 1e12
+
+
+def test_headline_is_the_grouped_nvfp4_prefill():
+    """The line's headline is the largest single-GPU workload: grouped NVFP4
+    prefill, 16384 routed rows x 7168 over 128 experts."""
+    assert bench.HEADLINE == "grouped_nvfp4"
+    c = bench.load_workload(bench.HEADLINE)
+    assert c.fmt == W.NVFP4 and c.x.shape == (16384, 7168) and c.G == 128
+    for name in ("dense_mxfp8", "dense_nvfp4", "grouped_nvfp4"):
+        assert name in bench.LARGE and bench.quantizer_table()[name][1] in (2, 4)
+
+
+def test_oracle_sample_of_a_grouped_workload():
+    """The CPU baseline's sample of a grouped workload: the first R routed
+    rows, each group cut at R; the codes rows and scale rows it reports are
+    exactly those the oracle wrote, and its bytes count them."""
+    c = W.grouped_mx_decode(W.MXFP4)
+    R = 100
+    q, s, code_rows, scale_rows, nbytes = bench._oracle_sample(c, R, 1)
+    assert np.array_equal(code_rows, np.arange(R))
+    counts = np.diff(np.minimum(c.row_offsets.astype(np.int64), R))
+    assert scale_rows.size == R and q.shape[0] == R and s.shape[0] == R
+    starts = c.scales_offsets[:-1].astype(np.int64)
+    want = np.concatenate([np.arange(a, a + n) for a, n in zip(starts, counts)])
+    assert np.array_equal(scale_rows, want)
+    distinct = np.unique(c.row_indices[:R]).size
+    assert nbytes == distinct * 2048 * 2 + R * 2048 * (bench.bytes_per_element(W.MXFP4) - 2)
+
+
+def test_rotation_exceeds_the_last_level_cache():
+    for nb in (1_327_104, 177_995_776, 300_943_368):
+        sets = bench.rotation(nb)
+        assert sets >= 2 and (sets * nb > 3 * bench.MALL_BYTES or sets == 64)
 
 
 @pytest.mark.parametrize("n", [2, 8])

@@ -43,3 +43,60 @@ def test_c_client_matches_oracle(tmp_path, fmt, M, K, specials):
     qh, sh = oracle.quantize(x, fmt, tsf)
     assert np.array_equal(np.fromfile(paths["q"], np.uint8).reshape(qh.shape), qh)
     assert np.array_equal(np.fromfile(paths["s"], np.uint8).reshape(sh.shape), sh)
+
+
+def routing(rng, S, G, E, rows, gather, first):
+    """Random groups (some empty) over `rows` routed rows starting at row
+    `first`, expert ids drawn with repeats, scale rows padded to 16 with some
+    extra padding; with gather, routed rows read random source rows."""
+    w = rng.random(G) * (rng.random(G) > 0.3)
+    w[0] += 1e-3
+    counts = rng.multinomial(rows, w / w.sum())
+    ro = (first + np.concatenate([[0], np.cumsum(counts)])).astype(np.uint32)
+    pads = -(-counts // 16) * 16 + 16 * rng.integers(0, 2, G)
+    so = np.concatenate([[0], np.cumsum(pads)]).astype(np.uint32)
+    ids = rng.integers(0, E, G).astype(np.int32)
+    max_rows = int(ro[-1]) + 5
+    ri = rng.integers(0, S, max_rows).astype(np.int32) if gather else None
+    return ro, so, ids, max_rows, int(so[-1]) + 16, ri
+
+
+@pytest.mark.parametrize("fmt,S,K,G,E,rows,gather,first", [
+    (oracle.MXFP4, 64, 2048, 256, 256, 512, True, 0),       # decode gather shape
+    (oracle.MXFP8, 40, 1056, 30, 7, 300, True, 3),          # ragged K, rows before the first group
+    (oracle.NVFP4, 900, 1024, 9, 12, 880, False, 0),        # per-expert tensor scales on the device
+    (oracle.NVFP4, 50, 512, 40, 16, 400, True, 2)])
+def test_c_client_grouped_matches_oracle(tmp_path, fmt, S, K, G, E, rows, gather, first):
+    """grouped_tensor_scale_nvfp4 then grouped_quantize_block_scaled from C:
+    codes, scales (padding and rows no group owns included: they keep 0xA5)
+    and the per-expert tensor scales all equal the oracle's."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    if not os.path.exists(CLIENT):
+        pytest.fail(f"{CLIENT} is not built; run __graft_entry__.build()")
+    rng = np.random.default_rng(S + K + G + fmt)
+    x = W.random_bf16((S, K), seed=S * K + fmt, scale_log2_range=(-10, 10), special_frac=0.001)
+    ro, so, ids, max_rows, nsr, ri = routing(rng, S, G, E, rows, gather, first)
+    if not gather:
+        assert max_rows <= S
+    for name, a in (("x", x), ("ro", ro), ("so", so), ("ids", ids), ("ri", ri)):
+        if a is not None:
+            a.tofile(str(tmp_path / f"{name}.bin"))
+    res = subprocess.run([CLIENT, "grouped", str(fmt), str(S), str(K), str(G), str(E),
+                          str(max_rows), str(nsr), "1" if gather else "0", str(tmp_path)],
+                         capture_output=True, text=True, timeout=120)
+    print(res.stdout, res.stderr)
+    assert res.returncode == 0
+    assert "without tensor scales: status 1, message: NVFP4 needs" in res.stdout
+    tsf = None
+    if fmt == oracle.NVFP4:
+        tsf = np.fromfile(str(tmp_path / "tsf.bin"), np.float32)
+        want = oracle.grouped_tensor_scale(x, ro, ids, E, row_indices=ri)
+        assert np.array_equal(tsf.view(np.uint32), np.asarray(want, np.float32).view(np.uint32))
+    width = K if fmt == oracle.MXFP8 else K // 2
+    bs = oracle.BLOCK[fmt]
+    qh, sh = oracle.grouped_quantize(x, fmt, ro, so, ids, tsf, max_rows, nsr, row_indices=ri,
+                                     codes=np.full((max_rows, width), 0xA5, np.uint8),
+                                     scales=np.full((nsr, K // bs), 0xA5, np.uint8))
+    assert np.array_equal(np.fromfile(str(tmp_path / "q.bin"), np.uint8).reshape(qh.shape), qh)
+    assert np.array_equal(np.fromfile(str(tmp_path / "s.bin"), np.uint8).reshape(sh.shape), sh)
