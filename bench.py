@@ -305,26 +305,35 @@ def spread(us):
 
 
 def timed_region(torch, arm, launch, steps, warmup):
-    """Warm up, then time `steps` launches between two device
-    synchronisations.  Before launch i, arm(start_i, stop_i) binds a recorded
-    event pair to that launch's kernel.  Returns the wall time of the region,
-    the per-launch span of one event pair around the whole loop (kernel times
-    plus the gaps between launches), and every kernel's own time (µs)."""
+    """Warm up, then two passes of `steps` launches.
+
+    The timed region: the launches between two device synchronisations, with
+    one event pair around them -- its wall time and the events' span per
+    launch (kernel time plus the gap between launches).
+
+    Then the same launches with a recorded event pair bound to each kernel's
+    dispatch (arm(start_i, stop_i) before launch i): every kernel's own time
+    in µs.  Binding events to a dispatch adds a few µs between launches on
+    this runtime, so this pass is kept out of the timed region."""
     for i in range(warmup):
         launch(i)
-    pairs = recorded_events(torch, steps)
     outer = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     outer[0].record()
     for i in range(steps):
-        arm(*pairs[i])
         launch(warmup + i)
     outer[1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    span = outer[0].elapsed_time(outer[1]) * 1e3 / steps
+    pairs = recorded_events(torch, steps)
+    for i in range(steps):
+        arm(*pairs[i])
+        launch(warmup + steps + i)
+    torch.cuda.synchronize()
     kernel_us = [a.elapsed_time(b) * 1e3 for a, b in pairs]
-    return wall, outer[0].elapsed_time(outer[1]) * 1e3 / steps, kernel_us
+    return wall, span, kernel_us
 
 
 def graph_launch_us(runner, n_launch=64, replays=20):
@@ -358,9 +367,10 @@ def rotation(nbytes):
     return min(64, max(2, -(-3 * MALL_BYTES // max(nbytes, 1)) + 1))
 
 
-def measure(name, steps, warmup):
+def measure(name, steps, warmup, ceiling_u=None):
     """One workload: its runner, algorithmic bytes and elements per launch,
-    and its timing summary."""
+    its timing summary, and (with ceiling_u) the same-byte-mix stream timed on
+    its buffers just before it."""
     import workloads as W
     producer = name.startswith("tsf_")
     case = load_workload(name)
@@ -368,6 +378,7 @@ def measure(name, steps, warmup):
     reuse = isinstance(case, (W.GemmCase, W.GroupedGemmCase))   # one set: reuse is the point
     nb = 1 if reuse else rotation(nbytes)
     runner = Runner(case, nb, producer)
+    ceil = ceiling(runner, ceiling_u, steps, warmup) if ceiling_u else None
     wall, region_us, kernel_us = timed_region(runner.torch, runner.bsq.time_next_launch,
                                               runner.step, steps, warmup)
     s = summary(name, nbytes, elems, nb, wall, region_us, kernel_us, steps)
@@ -375,7 +386,7 @@ def measure(name, steps, warmup):
         g = graph_launch_us(runner)
         s.update({"graph_us_mean": g, "graph_GBps": round(nbytes / g / 1e3, 1),
                   "graph_Gelem_per_s": round(elems / g / 1e3, 1)})
-    return case, runner, nbytes, s
+    return case, runner, nbytes, s, ceil
 
 
 def summary(name, nbytes, elems, nb, wall, region_us, kernel_us, steps):
@@ -386,7 +397,7 @@ def summary(name, nbytes, elems, nb, wall, region_us, kernel_us, steps):
         "elements": elems,
         "buffer_sets": nb,
         "kernel_us": k,
-        "launch_span_us": round(region_us, 3),
+        "timed_region_us_per_launch": round(region_us, 3),
         "GBps": round(nbytes / k["mean"] / 1e3, 1),
         "frac_of_8TBps": round(nbytes / k["mean"] / 1e3 / PEAK_HBM_GBS, 4),
         "GBps_median": round(nbytes / k["median"] / 1e3, 1),
@@ -399,29 +410,40 @@ def summary(name, nbytes, elems, nb, wall, region_us, kernel_us, steps):
 def ceiling(runner, u, steps, warmup):
     """The same-byte-mix trivial stream on the workload's own buffers (its
     BF16 input and, as dense [M, K] outputs, the first rows of its code and
-    scale buffers), timed like the quantizer."""
+    scale buffers), timed like the quantizer, at the quantizer's own tile of u
+    chunks per wave and at the other tile sizes; the fastest is the
+    ceiling.  It runs right before the quantizer's own timing."""
     bsq, torch, case = runner.bsq, runner.torch, runner.case
     M, K = case.x.shape
     views = [(st["x"], st["q"][:M], st["s"][:M]) for st in runner.sets]
+    # at least 300 launches per tile size: together about 50 ms of streaming,
+    # which also brings the GPU to its steady clocks before the quantizer
+    steps = max(steps, 300)
     fmt = case.fmt
-    armed = {}
-
-    def arm(a, b):
-        armed["ev"] = (a, b)
-
-    def launch(i):
-        x, q, s = views[i % len(views)]
-        a, b = armed.pop("ev", (None, None))
-        bsq.ceiling_stream(x, fmt, u, codes=q, scales=s, start=a, stop=b)
-
-    wall, region_us, kernel_us = timed_region(torch, arm, launch, steps, warmup)
     nbytes = int(M * K * bytes_per_element(fmt))
-    k = spread(kernel_us)
+    by_u = {}
+    for uu in (1, 2, 4):
+        armed = {}
+
+        def arm(a, b):
+            armed["ev"] = (a, b)
+
+        def launch(i):
+            x, q, s = views[i % len(views)]
+            a, b = armed.pop("ev", (None, None))
+            bsq.ceiling_stream(x, fmt, uu, codes=q, scales=s, start=a, stop=b)
+
+        _, _, kernel_us = timed_region(torch, arm, launch, steps, warmup)
+        by_u[uu] = spread(kernel_us)
+    best = min(by_u, key=lambda k: by_u[k]["mean"])
+    k = by_u[best]
     return {"kernel": f"bsq::ceiling_kernel, {M}x{K}, {['MXFP4', 'MXFP8', 'NVFP4'][fmt]} "
-                      f"byte mix, {u} chunk(s) per wave",
-            "bytes_per_launch": nbytes, "kernel_us": k,
+                      f"byte mix, best of 1 / 2 / 4 chunks per wave",
+            "bytes_per_launch": nbytes, "chunks_per_wave": best, "kernel_us": k,
             "GBps": round(nbytes / k["mean"] / 1e3, 1),
-            "frac_of_8TBps": round(nbytes / k["mean"] / 1e3 / PEAK_HBM_GBS, 4)}
+            "frac_of_8TBps": round(nbytes / k["mean"] / 1e3 / PEAK_HBM_GBS, 4),
+            "kernel_us_mean_by_chunks_per_wave": {str(a): b["mean"] for a, b in by_u.items()},
+            "quantizer_chunks_per_wave": u}
 
 
 def roofline(s, traffic, traffic_note, ceil=None):
@@ -436,6 +458,7 @@ def roofline(s, traffic, traffic_note, ceil=None):
          "traffic": traffic, "traffic_note": traffic_note}
     if ceil is not None:
         r["ceiling"] = ceil
+        # the kernel's speed as a fraction of the trivial stream's (above 1: faster than it)
         r["of_ceiling"] = round(ceil["kernel_us"]["mean"] / k["mean"], 4)
     return r
 
@@ -518,31 +541,43 @@ def cpu_baseline(case, runner, cpu_seconds):
 
 # ------------------------------------------------------------------ counters
 
-def source_hash():
-    """sha256 over the library's sources: counters taken on other sources do
-    not describe the kernels that run."""
+# the sources each workload's kernels are built from (host launch code included)
+FAMILY_SOURCES = {
+    "quantize": ("bsq_kernels.hip", "bsq_internal.h", "bsq_api.cpp"),
+    "consume": ("bsq_consume.hip", "bsq_internal.h", "bsq_api.cpp"),
+}
+
+
+def family(name):
+    return "consume" if name.startswith(("dequant_", "mfma_")) else "quantize"
+
+
+def source_hash(fam):
+    """sha256 over the sources of one kernel family: counters taken on other
+    sources do not describe the kernels that run."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
-        h.update(os.path.basename(p).encode())
-        h.update(open(p, "rb").read())
+    for f in FAMILY_SOURCES[fam]:
+        h.update(f.encode())
+        h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()
 
 
 def traffic_from_counters(name):
     """HBM bytes per launch of workload `name` from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary, valid only while the library's sources
-    are the ones they were taken on."""
+    FETCH_SIZE / WRITE_SIZE summary, valid only while its kernel family's
+    sources are the ones they were taken on."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None, "no counter file"
-    if rec.get("source_sha256") != source_hash():
+    fam = rec.get(family(name), {})
+    if fam.get("source_sha256") != source_hash(family(name)):
         return None, "the kernels changed since the counters were taken"
-    v = rec.get("hbm_bytes_per_launch", {}).get(name)
+    v = fam.get("hbm_bytes_per_launch", {}).get(name)
     if v is None:
         return None, f"no counters for {name}"
     return int(v), ("committed measurement (profiles/pmc_traffic.json), not taken in this "
-                    "run: " + rec.get("note", ""))
+                    "run: " + fam.get("note", ""))
 
 
 def copy_calibration(nbytes, steps):
@@ -605,10 +640,17 @@ def pmc_summary(d, copy_bytes):
         out[w] = hbm
         table.append(f"| {w} | `{k}` | {n} | {f:.1f} | {wr:.1f} | {hbm:,} | {alg:,} | "
                      f"{hbm / alg:.4f} |")
-    rec = {"source_sha256": source_hash(), "fetch_factor": ff, "write_factor": wf,
-           "hbm_bytes_per_launch": out,
-           "note": f"FETCH_SIZE x {ff:.4f} + WRITE_SIZE x {wf:.4f} per dispatch of the "
-                   f"workload's main kernel; factors from a plain copy of {copy_bytes} bytes"}
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        rec = {}
+    note = (f"FETCH_SIZE x {ff:.4f} + WRITE_SIZE x {wf:.4f} per dispatch of the workload's main "
+            f"kernel; factors from a plain copy of {copy_bytes} bytes")
+    for fam in FAMILY_SOURCES:      # replace what this run measured, keep the other family
+        mine = {w: b for w, b in out.items() if family(w) == fam}
+        if mine:
+            rec[fam] = {"source_sha256": source_hash(fam), "hbm_bytes_per_launch": mine,
+                        "fetch_factor": ff, "write_factor": wf, "note": note}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
     print(f"copy of {copy_bytes} bytes: FETCH_SIZE {cf:.1f} KiB (factor {ff:.4f}), "
@@ -617,6 +659,28 @@ def pmc_summary(d, copy_bytes):
           "(calibrated) | algorithmic bytes | ratio |")
     print("|---|---|---|---|---|---|---|---|")
     print("\n".join(table))
+    sq = sorted(glob.glob(os.path.join(d, "*_sq_counter_collection.csv")))
+    if sq:
+        print("\n| workload | kernel | dispatches | counters (mean per dispatch) | per wave |")
+        print("|---|---|---|---|---|")
+    for p in sq:
+        w = os.path.basename(p)[:-len("_sq_counter_collection.csv")]
+        import csv
+        per = {}
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                if "bsq::" in r["Kernel_Name"]:
+                    per.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(
+                        float(r["Counter_Value"]))
+        for k, cs in sorted(per.items()):
+            means = {c: float(np.mean(v)) for c, v in cs.items()}
+            n = max(len(v) for v in cs.values())
+            waves = means.get("SQ_WAVES", 0.0)
+            pw = ", ".join(f"{c[8:] if c.startswith('SQ_INSTS') else c} {v / waves:.1f}"
+                           for c, v in sorted(means.items())
+                           if waves and c.startswith("SQ_INSTS"))
+            print(f"| {w} | `{k}` | {n} | " +
+                  ", ".join(f"{c} {v:.0f}" for c, v in sorted(means.items())) + f" | {pw} |")
 
 
 # ------------------------------------------------------------------ main
@@ -656,12 +720,20 @@ def main():
     import fp8_quantization_amd as bsq
 
     quant = quantizer_table()
-    names = [args.workload]
+    # The headline is measured last: the GPU needs tens of milliseconds of
+    # sustained work to reach its steady clocks, and the other workloads (and
+    # the headline's own ceiling legs, on its buffers, right before it)
+    # provide them without adding warm-up launches beyond --warmup.
+    names = []
     if not args.no_secondary:
         names += [n for n in list(quant) + list(consumer_table()) if n != args.workload]
+    names.append(args.workload)
     results, head = {}, None
     for name in names:
-        case, runner, nbytes, s = measure(name, args.steps, args.warmup)
+        u = quant[name][1] if name in quant and name in LARGE and not args.no_ceiling else None
+        case, runner, nbytes, s, ceil = measure(name, args.steps, args.warmup, u)
+        if ceil is not None:
+            log("[bench] ceiling", name, json.dumps(ceil))
         if name.startswith(("mfma_gemm", "mfma_grouped_gemm")):
             tf = gemm_flops(case) / s["kernel_us"]["mean"] / 1e6
             peak = PEAK_MFMA_TFLOPS[case.fmt]
@@ -670,11 +742,6 @@ def main():
             s.update({"bound": "hbm" if hbm_bound else "mfma", "TFLOPs": round(tf, 1),
                       "peak_TFLOPs": peak, "frac_of_peak": round(tf / peak, 4)})
         if name in quant:
-            ceil = None
-            u = quant[name][1]
-            if name in LARGE and u and not args.no_ceiling:
-                ceil = ceiling(runner, u, args.steps, args.warmup)
-                log("[bench] ceiling", name, json.dumps(ceil))
             if name in LARGE:
                 s["roofline"] = roofline(s, *traffic_from_counters(name), ceil)
             if not args.no_cpu_baseline:

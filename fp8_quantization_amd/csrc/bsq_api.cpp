@@ -304,8 +304,10 @@ int grouped_quantize_block_scaled(int format, int block_size, int scale_layout, 
                           scales, lds, work);
     if (st != BSQ_OK) return st;
     if (!work) return ok();
-    if (num_groups > 0x7FFFFFFFLL - 64)
-        return fail(BSQ_ERR_INVALID_ARG, "num_groups=%lld too large", (long long)num_groups);
+    // the lane-parallel search addresses the offsets with 32-bit byte offsets
+    if (num_groups > (int64_t(1) << 28))
+        return fail(BSQ_ERR_INVALID_ARG, "num_groups=%lld too large (at most 2^28)",
+                    (long long)num_groups);
     if (max_rows > (int64_t(1) << 32))
         return fail(BSQ_ERR_INVALID_ARG, "max_rows=%lld exceeds the uint32 offset range",
                     (long long)max_rows);

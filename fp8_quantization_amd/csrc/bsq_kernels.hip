@@ -13,8 +13,10 @@
 //  * a wave owns a tile of one row: up to chunks_per_tile chunks of 512
 //    elements; lane l holds elements [8l, 8l + 8) of a chunk, fetched with one
 //    16-byte load, so every wave-wide load is 1 KiB contiguous;
-//  * a wave issues all of its tile's loads before converting any chunk, so
-//    each lane keeps one 16-byte load per chunk in flight;
+//  * a wave issues all of its tile's loads back to back (no per-lane
+//    condition: lanes past the row's end read an in-row address and their
+//    stores are dropped), then converts each chunk as soon as its own load
+//    has landed;
 //  * a block spans 4 lanes (MX, 32 elements) or 2 lanes (NVFP4, 16); its
 //    amax is an integer max over |BF16| bit patterns, reduced across those
 //    lanes with DPP quad permutes (no LDS, no barrier);
@@ -23,7 +25,8 @@
 //    scale byte, and one byte-store instruction writes the scales of up to
 //    4 (MX) or 2 (NVFP4) chunks;
 //  * grouped form: each wave finds its group (last g with row_offsets[g] <=
-//    r) by a binary search on the scalar unit, after its loads are in flight;
+//    r) from one 16-byte load of four offsets per lane and four ballots,
+//    issued ahead of its data loads;
 //  * the NVFP4 tensor-scale producer is a separate reduction: persistent
 //    waves over contiguous tile ranges, a per-workgroup LDS table, and one
 //    device atomic max per workgroup and expert.
@@ -260,12 +263,6 @@ __device__ __forceinline__ LaneOut quantize_lane(const uint4& w, const Nvfp4Wave
 }
 
 // ---------------------------------------------------------------- kernel
-//
-// One wave converts one tile: U consecutive chunks (U * 512 elements) of one
-// row.  Loads carry the non-temporal hint: the data streams through once, so
-// it should not displace anything from the caches.  Stores take the cache
-// policy measured best for the code width and problem size (kStoreStream,
-// kStoreWriteThrough below).
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
@@ -289,20 +286,9 @@ constexpr int kBufferNontemporal = 2;
 constexpr int kStoreStream = 2;         // nt
 constexpr int kStoreWriteThrough = 16;  // sc1
 
-__device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 // The owning group of routed row r and its metadata.  The last g with
-// row_offsets[g] <= r owns r (empty groups repeat an offset and never win).
-// It is found by a binary search over row_offsets on the scalar unit, then
-// scalar loads of the group's entries: about log2(G) dependent scalar-cache
-// reads, overlapped with the wave's data loads, and no vector memory
-// instruction.  Loading the metadata across the wave's lanes in one round
-// trip (a ballot over 256 or 512 offsets) measured slower at every size: on
-// this chip a wave's vector memory instructions cost more than a short chain
-// of scalar reads.
+// row_offsets[g] <= r owns r (empty groups repeat an offset and never win),
+// so g + 1 is the number of offsets <= r.
 struct GroupInfo {
     int g;             // -1: r is before the first or at/after the last group
     uint32_t ro, so;   // row_offsets[g], scales_offsets[g]
@@ -310,27 +296,72 @@ struct GroupInfo {
     float sf;          // expert_sf[id] (NVFP4 only, when id is in range)
 };
 
-// How many of row_offsets[0..G] are <= r (wave-uniform): an upper-bound
-// binary search on the scalar unit.  For nondecreasing offsets this is one
-// more than the last group starting at or before r.  Every probe index lies
-// in [0, G], whatever the offsets hold.
+// How many of row_offsets[0..G] are <= r (wave-uniform), on the scalar unit:
+// an upper-bound search that halves the range twice per round trip -- the
+// probe of the second halving is loaded for both outcomes of the first, so
+// the three loads of a round are independent.  For nondecreasing offsets
+// this is one more than the last group starting at or before r.  Every probe
+// index lies in [0, G], whatever the offsets hold.  (The tensor-scale
+// reduction places its cursor with it once per wave.)
 __device__ __forceinline__ int offsets_at_or_below(const KernelArgs& a, uint32_t r) {
     const uint32_t* __restrict__ ro = a.row_offsets;
-    int lo = 0, hi = a.num_groups + 1;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (ro[mid] <= r)
-            lo = mid + 1;
-        else
-            hi = mid;
+    uint32_t base = 0, n = (uint32_t)a.num_groups + 1;
+    const uint32_t first = ro[0];
+    while (n > 1) {
+        const uint32_t h1 = n >> 1, n1 = n - h1, h2 = n1 >> 1;
+        const uint32_t v_mid = ro[base + h1], v_lo = ro[base + h2], v_hi = ro[base + h1 + h2];
+        const bool up = v_mid <= r;
+        const uint32_t b1 = up ? base + h1 : base;
+        base = ((up ? v_hi : v_lo) <= r) ? b1 + h2 : b1;
+        n = n1 - h2;
     }
-    return lo;
+    return (int)(base + ((base > 0 || first <= r) ? 1u : 0u));
+}
+
+// Lane-parallel group lookup, the quantizers' search: the wave loads
+// row_offsets 256 entries at a time, four per lane (one 16-byte buffer load,
+// issued ahead of the data loads so it lands first); entries past G read as
+// zeros and are masked by index.  Offsets are nondecreasing, so the entries
+// <= r form a prefix, whose length is the number of set bits of four ballots.
+// Then scalar loads of the group's entries.  Against a binary search on the
+// scalar unit (about 100 scalar instructions and 8 dependent round trips per
+// wave) this took grouped NVFP4 on the 16384 x 7168 prefill routing from
+// 47.2-47.9 us to 45.5-46.0 and grouped MXFP4 from 44.8-45.0 to 44.2-44.3
+// (grouped MXFP8 56.3 -> 56.5-56.8), timed in alternation on one box.
+struct OffsetsLoad {
+    __amdgpu_buffer_rsrc_t rsrc;
+    u32x4_t v;
+};
+__device__ __forceinline__ OffsetsLoad issue_offsets(const KernelArgs& a, int lane) {
+    OffsetsLoad o;
+    o.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(a.row_offsets), (short)0,
+                                               (a.num_groups + 1) * 4, kBufferWord3);
+    o.v = __builtin_amdgcn_raw_buffer_load_b128(o.rsrc, lane * 16, 0, 0);
+    return o;
+}
+__device__ __forceinline__ int count_at_or_below(const KernelArgs& a, const OffsetsLoad& o,
+                                                 uint32_t r, int lane) {
+    const int G1 = a.num_groups + 1;
+    u32x4_t v = o.v;
+    int cnt = 0;
+    for (int base = 0;; base += 256) {
+        const int i0 = base + 4 * lane;
+        const uint32_t c = (uint32_t)__builtin_popcountll(__ballot(i0 < G1 && v.x <= r)) +
+                           (uint32_t)__builtin_popcountll(__ballot(i0 + 1 < G1 && v.y <= r)) +
+                           (uint32_t)__builtin_popcountll(__ballot(i0 + 2 < G1 && v.z <= r)) +
+                           (uint32_t)__builtin_popcountll(__ballot(i0 + 3 < G1 && v.w <= r));
+        cnt += (int)c;
+        if (c < 256u || base + 256 >= G1) break;
+        v = __builtin_amdgcn_raw_buffer_load_b128(o.rsrc, (base + 256) * 4 + lane * 16, 0, 0);
+    }
+    return cnt;
 }
 
 template <bool NEED_SF>
-__device__ __forceinline__ GroupInfo find_group_scalar(const KernelArgs& a, uint32_t r) {
+__device__ __forceinline__ GroupInfo find_group_vec(const KernelArgs& a, const OffsetsLoad& o,
+                                                    uint32_t r, int lane) {
     const int G = a.num_groups;
-    const int cnt = offsets_at_or_below(a, r);
+    const int cnt = __builtin_amdgcn_readfirstlane(count_at_or_below(a, o, r, lane));
     GroupInfo gi{-1, 0u, 0u, 0, 1.0f};
     if (cnt == 0 || cnt > G) return gi;
     gi.g = cnt - 1;
@@ -353,18 +384,16 @@ __device__ __forceinline__ uint32_t div_tiles(uint32_t t, const KernelArgs& a) {
     return (uint32_t)(hi >> 32);
 }
 
-template <int FMT, bool GROUPED, int U>
-__global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const KernelArgs a) {
+// One tile of N chunks (N <= U; fewer only for the last tile of a row).  Its
+// N 16-byte loads are issued back to back with no per-lane condition (lanes
+// past the row's end load the row's last 8 elements instead), so the wave
+// converts chunk u as soon as its own load has landed while the later ones
+// are still in flight.  Code stores go through a descriptor over the row's
+// codes, which drops lanes past K.
+template <int FMT, bool GROUPED, int N, int POLICY>
+__device__ __forceinline__ void quantize_tile(const KernelArgs& a, uint32_t row, int c0,
+                                              int lane) {
     using T = FormatTraits<FMT>;
-    const int lane = (int)(threadIdx.x & (kWaveSize - 1));
-    // the tile index is wave-uniform: keep it (and all row arithmetic) scalar
-    const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock +
-                                                      (threadIdx.x / kWaveSize));
-    if (t >= (uint32_t)a.total_tiles) return;
-    const uint32_t row = div_tiles(t, a);
-    const int c0 = (int)(t - row * (uint32_t)a.tiles_per_row) * U;
-    const int nch = min(U, a.chunks_per_row - c0);  // chunks in this tile (>= 1)
-
     int64_t src = row;
     if constexpr (GROUPED) {
         if (a.row_indices) {
@@ -373,20 +402,19 @@ __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const Kernel
         }
     }
     const uint16_t* xrow = a.x + src * a.ldx;
-
-    // issue this tile's loads before anything that waits on memory
-    uint4 w[U];
+    OffsetsLoad offs{};
+    if constexpr (GROUPED) offs = issue_offsets(a, lane);
+    u32x4_t w[N];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const uint32_t col = (uint32_t)((c0 + u) * kChunkElems + lane * kElemsPerLane);
-        w[u] = make_uint4(0u, 0u, 0u, 0u);
-        if (u < nch && col < (uint32_t)a.K) w[u] = load_stream(xrow + col);
+    for (int u = 0; u < N; ++u) {
+        const int col = min((c0 + u) * kChunkElems + lane * kElemsPerLane, a.K - kElemsPerLane);
+        w[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(xrow + col));
     }
 
     int64_t scale_row = row;
     float tsf = a.tensor_sf;
     if constexpr (GROUPED) {
-        const GroupInfo gi = find_group_scalar<FMT == 2>(a, row);
+        const GroupInfo gi = find_group_vec<FMT == 2>(a, offs, row, lane);
         if (gi.g < 0) return;
         scale_row = (int64_t)gi.so + ((int64_t)row - (int64_t)gi.ro);
         if (scale_row < 0 || scale_row >= a.num_scale_rows) return;
@@ -396,8 +424,8 @@ __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const Kernel
         }
     }
     uint8_t* qrow = a.codes + (int64_t)row * a.ldq;
-    // row-major: the scale row; MFMA layout (MX only): the row's place in
-    // its 16-row group, to which each block adds its record and lane offset
+    // row-major: the scale row; MFMA layout (MX only): the row's place in its
+    // 16-row group, to which each block adds its record and lane offset
     const bool mfma_layout = FMT != 2 && a.scale_layout == 1;
     uint8_t* srow = mfma_layout ? a.scales + (scale_row >> 4) * a.lds + 4 * (scale_row & 15)
                                 : a.scales + scale_row * a.lds;
@@ -406,7 +434,6 @@ __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const Kernel
 
     // store descriptors over this row's codes and its scale bytes (the
     // offsets below stay inside them; a store outside would be dropped)
-    constexpr int kPolicy = (T::kFp4 && U > 1) ? kStoreWriteThrough : kStoreStream;
     const int code_bytes = T::kFp4 ? a.K / 2 : a.K;
     const int scale_bytes = mfma_layout ? a.chunks_per_row * 256 - 4 * (int)(scale_row & 15)
                                         : a.K / T::kBlock;
@@ -415,48 +442,67 @@ __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const Kernel
     const __amdgpu_buffer_rsrc_t srsrc =
         __builtin_amdgcn_make_buffer_rsrc(srow, (short)0, scale_bytes, kBufferWord3);
 
-    uint32_t sb[U], q0[U], q1[U];  // per chunk: scale byte, packed codes (FP4: q0 only)
+    uint32_t sb[N];  // per chunk: the block's scale byte
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        sb[u] = q0[u] = q1[u] = 0;
-        if (u >= nch) continue;  // wave-uniform
-        const LaneOut o = quantize_lane<FMT>(w[u], nw);
+    for (int u = 0; u < N; ++u) {
+        const LaneOut o = quantize_lane<FMT>(make_uint4(w[u].x, w[u].y, w[u].z, w[u].w), nw);
         sb[u] = o.scale;
-        q0[u] = o.c0;
-        q1[u] = o.c1;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        if (u >= nch) continue;  // wave-uniform
-        const uint32_t col = (uint32_t)((c0 + u) * kChunkElems + lane * kElemsPerLane);
-        if (col < (uint32_t)a.K) {
-            if constexpr (T::kFp4) {
-                __builtin_amdgcn_raw_buffer_store_b32(q0[u], qrsrc, (int)(col / 2), 0, kPolicy);
-            } else {
-                const u32x2_t v = {q0[u], q1[u]};
-                __builtin_amdgcn_raw_buffer_store_b64(v, qrsrc, (int)col, 0, kPolicy);
-            }
+        const int col = (c0 + u) * kChunkElems + lane * kElemsPerLane;
+        if constexpr (T::kFp4) {
+            __builtin_amdgcn_raw_buffer_store_b32(o.c0, qrsrc, col / 2, 0, POLICY);
+        } else {
+            const u32x2_t v = {o.c0, o.c1};
+            __builtin_amdgcn_raw_buffer_store_b64(v, qrsrc, col, 0, POLICY);
         }
     }
     // Scale bytes: every lane of a block holds its byte, so one store
     // instruction covers up to kLanesPerBlock chunks -- lane (block * L + j)
-    // writes chunk (g + j)'s byte for that block.
+    // writes chunk (g + j)'s byte for that block.  Blocks past K are not
+    // stored (in the MFMA layout they would land inside a record).
     constexpr int L = T::kLanesPerBlock;
 #pragma unroll
-    for (int g = 0; g < U; g += L) {
+    for (int g = 0; g < N; g += L) {
         const int j = lane & (L - 1);
         const int u = g + j;
         uint32_t v = sb[g];
 #pragma unroll
-        for (int k = 1; k < L && g + k < U; ++k) v = (j == k) ? sb[g + k] : v;
-        const uint32_t col = (uint32_t)((c0 + u) * kChunkElems + (lane - j) * kElemsPerLane);
+        for (int k = 1; k < L && g + k < N; ++k) v = (j == k) ? sb[g + k] : v;
+        const int col = (c0 + u) * kChunkElems + (lane - j) * kElemsPerLane;
         // block b = lane / L of chunk c0 + u; in the MFMA layout a chunk is one
         // record and block b goes to lane-dword 16 (b % 4), byte b / 4
         const int b = lane / L;
-        const int off = mfma_layout ? (c0 + u) * 256 + 64 * (b & 3) + (b >> 2)
-                                    : (int)(col / T::kBlock);
-        if (u < nch && u < U && col < (uint32_t)a.K)
-            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, srsrc, off, 0, kPolicy);
+        const int off = mfma_layout ? (c0 + u) * 256 + 64 * (b & 3) + (b >> 2) : col / T::kBlock;
+        if (u < N && col < a.K)
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, srsrc, off, 0, POLICY);
+    }
+}
+
+// One wave converts one tile: U consecutive chunks (U * 512 elements) of one
+// row.  Loads carry the non-temporal hint: the data streams through once, so
+// it should not displace anything from the caches.  Stores take the cache
+// policy measured best for the code width and problem size (kStoreStream,
+// kStoreWriteThrough above).  The last tile of a row may hold fewer chunks; it
+// takes the tile body built for its count, so every body is straight-line.
+template <int FMT, bool GROUPED, int U>
+__global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const KernelArgs a) {
+    using T = FormatTraits<FMT>;
+    constexpr int kPolicy = (T::kFp4 && U > 1) ? kStoreWriteThrough : kStoreStream;
+    const int lane = (int)(threadIdx.x & (kWaveSize - 1));
+    // the tile index is wave-uniform: keep it (and all row arithmetic) scalar
+    const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock +
+                                                      (threadIdx.x / kWaveSize));
+    if (t >= (uint32_t)a.total_tiles) return;
+    const uint32_t row = div_tiles(t, a);
+    const int c0 = (int)(t - row * (uint32_t)a.tiles_per_row) * U;
+    const int nch = min(U, a.chunks_per_row - c0);  // chunks in this tile (>= 1)
+    if (nch == U) {
+        quantize_tile<FMT, GROUPED, U, kPolicy>(a, row, c0, lane);
+    } else if constexpr (U > 1) {
+        if (nch == 1) quantize_tile<FMT, GROUPED, 1, kPolicy>(a, row, c0, lane);
+        if constexpr (U > 2) {
+            if (nch == 2) quantize_tile<FMT, GROUPED, 2, kPolicy>(a, row, c0, lane);
+            if (nch == 3) quantize_tile<FMT, GROUPED, 3, kPolicy>(a, row, c0, lane);
+        }
     }
 }
 

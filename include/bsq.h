@@ -144,7 +144,7 @@ int quantize_block_scaled(int format, int block_size, int scale_layout,
  *   expert_ids       int32 [num_groups], values in [0, num_experts).
  *   tensor_sf        fp32 [num_experts] for NVFP4 (each value obeying the
  *                    dense tensor_sf domain); ignored (may be NULL) for MX.
- *   num_groups       >= 0.  num_experts >= 1 for NVFP4.
+ *   num_groups       >= 0 and at most 2^28.  num_experts >= 1 for NVFP4.
  *   max_rows         host-side bound on routed rows; sizes the grid, so the
  *                    device offsets are never read on the host.  <= 2^32.
  *   num_scale_rows   rows in the scales buffer.  This argument is the one

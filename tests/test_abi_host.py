@@ -324,3 +324,12 @@ def test_oracle_and_product_share_no_code():
             for bad in ("import fp8_quantization_amd", "from fp8_quantization_amd", "bsq.h",
                         "libbsq", "bsq_internal"):
                 assert bad not in text, (f, bad)
+
+
+def test_grouped_num_groups_limit(lib):
+    """At most 2^28 groups (the search addresses the offsets in 32 bits)."""
+    def call(G):
+        return lib.grouped_quantize_block_scaled(MXFP4, 32, 0, FAKE, 64, 64, 64, None, FAKE, FAKE,
+                                                 FAKE, None, G, 1, 64, 64, FAKE, 32, FAKE, 2, None)
+    assert call((1 << 28) + 1) == INVALID
+    assert b"2^28" in lib.bsq_last_error()

@@ -152,7 +152,7 @@ def check_every_group(got, c, fmt, K, N):
     nblk = K // 32
     ro, so, ids = c.row_offsets, c.scales_offsets, c.expert_ids
     worst = 0.0
-    for g in range(c.G):
+    for g in range(len(c.expert_ids)):
         lo, hi, e = int(ro[g]), int(ro[g + 1]), int(ids[g])
         if hi == lo:
             continue
