@@ -287,25 +287,45 @@ __device__ __forceinline__ void dense_desc(const GemmArgs& a, int64_t tiles_n, G
     d.K = a.K;
 }
 
-// Grouped per-expert form: blockIdx.y is the TN-column tile of c, blockIdx.x
-// a TM-row tile counted across the groups in order (group g has ceil(m_g /
-// TM) of them); each wave finds its group from the offsets.
-// Group g multiplies its routed rows (codes row r, scale row
-// scales_offsets[g] + r - row_offsets[g]) by the B of expert expert_ids[g]
-// ([N, K] codes from row e N, scales from row group e ceil(N / 16)).  A group
-// whose metadata falls outside the buffers, or whose scale offset is not a
-// multiple of 16 (the layout's row groups), is skipped: returns false.
+// Grouped per-expert form.  Row tiles of TM rows are counted across the
+// groups in order (group g has ceil(m_g / TM) of them).  Group g multiplies
+// its routed rows (codes row r, scale row scales_offsets[g] + r -
+// row_offsets[g]) by the B of expert expert_ids[g] ([N, K] codes from row
+// e N, scales from row group e ceil(N / 16)).
+
+// Total row tiles over all groups (wave-uniform): each lane takes one
+// group's tile count, 64 groups per step, summed across the lanes.
+template <int TM>
+__device__ __forceinline__ uint32_t total_row_tiles(const GroupedGemmArgs& g) {
+    const int lane = (int)(threadIdx.x & 63);
+    uint32_t total = 0;
+    for (int h0 = 0; h0 < g.num_groups; h0 += 64) {
+        const int h = h0 + lane;
+        uint32_t tiles = 0;
+        if (h < g.num_groups) {
+            const uint32_t l = g.row_offsets[h], u = g.row_offsets[h + 1];
+            tiles = u > l ? (uint32_t)(((uint64_t)u - l + TM - 1) / TM) : 0u;
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) tiles += (uint32_t)__shfl_xor((int)tiles, off);
+        total += tiles;
+    }
+    return total;
+}
+
+// The tile descriptor of row tile t and TN-column tile col: the wave reads 64
+// groups' offsets at a time and finds the group holding tile t from the
+// prefix sum of their tile counts across the lanes (t and every sum are
+// wave-uniform).  A group-by-group walk measured 29 us on its own for the
+// 128-expert prefill routing.  A group whose metadata falls outside the
+// buffers, or whose scale offset is not a multiple of 16 (the layout's row
+// groups), is skipped: returns false, as does a t past the last group's tiles.
 template <int TM, int TN>
-__device__ __forceinline__ bool grouped_desc(const GemmArgs& a, const GroupedGemmArgs& g,
-                                             GemmTile& d) {
-    const int64_t n0 = (int64_t)blockIdx.y * TN;
-    int64_t t = blockIdx.x;
+__device__ __forceinline__ bool grouped_tile_desc(const GemmArgs& a, const GroupedGemmArgs& g,
+                                                  int64_t t, int64_t col, GemmTile& d) {
+    const int64_t n0 = col * TN;
     int grp = -1;
     int64_t lo = 0, hi = 0;
-    // The wave reads 64 groups' offsets at a time and finds the group holding
-    // tile t from the prefix sum of their tile counts across the lanes (t and
-    // every sum are wave-uniform).  A group-by-group walk measured 29 us on its
-    // own for the 128-expert prefill routing.
     const int lane = (int)(threadIdx.x & 63);
     for (int h0 = 0; h0 < g.num_groups; h0 += 64) {
         const int h = h0 + lane;
@@ -359,6 +379,32 @@ __device__ __forceinline__ bool grouped_desc(const GemmArgs& a, const GroupedGem
     d.c_cols = a.N - n0;
     d.K = a.K;
     return true;
+}
+
+// Decode form: blockIdx.x is the row tile, blockIdx.y the column tile.
+template <int TM, int TN>
+__device__ __forceinline__ bool grouped_desc(const GemmArgs& a, const GroupedGemmArgs& g,
+                                             GemmTile& d) {
+    return grouped_tile_desc<TM, TN>(a, g, blockIdx.x, blockIdx.y, d);
+}
+
+// 128-row form: the work items (row tile t, column tile c), numbered t major,
+// are dealt to the XCDs in contiguous runs.  The hardware hands workgroup w
+// to XCD w % 8, so workgroup w takes item (w % 8) * per_xcd + w / 8: an XCD
+// runs the column tiles of a row tile, and the row tiles of an expert, one
+// after another, and serves their shared A rows and B weights from its own
+// L2.  The grid holds at least 8 * per_xcd workgroups; the rest return.
+constexpr int kXcds = 8;
+template <int TM, int TN>
+__device__ __forceinline__ bool grouped_desc_xcd(const GemmArgs& a, const GroupedGemmArgs& g,
+                                                 GemmTile& d) {
+    const int64_t n_col = (a.N + TN - 1) / TN;
+    const int64_t items = (int64_t)total_row_tiles<TM>(g) * n_col;
+    const int64_t per_xcd = (items + kXcds - 1) / kXcds;
+    const int64_t w = blockIdx.x, slot = w / kXcds;
+    const int64_t item = (w % kXcds) * per_xcd + slot;
+    if (slot >= per_xcd || item >= items) return false;
+    return grouped_tile_desc<TM, TN>(a, g, item / n_col, item % n_col, d);
 }
 
 // Pipelined form of the tile: the stages of A and B go straight from global
@@ -567,7 +613,7 @@ __global__ void __launch_bounds__(64 * Tile128::NW)
 mfma_gemm_grouped_kernel(const GemmArgs a, const GroupedGemmArgs g) {
     BSQ_STAGE_BUFFERS(Tile128::kStageBytes)
     GemmTile d;
-    if (!grouped_desc<kTileM, kTileN>(a, g, d)) return;
+    if (!grouped_desc_xcd<kTileM, kTileN>(a, g, d)) return;
     uint8_t* const bufs[2] = {stage0, stage1};
     gemm_tile_dma<FMT, 2, Tile128>(d, bufs);
 }
@@ -879,7 +925,9 @@ hipError_t launch_mfma_grouped(const GemmArgs& a, const GroupedGemmArgs& g, hipS
             default: return hipErrorInvalidValue;
         }
     }
-    const dim3 grid((uint32_t)g.m_tiles, (uint32_t)((a.N + kTileN - 1) / kTileN));
+    // one workgroup per work item, rounded up to a whole number per XCD
+    const int64_t items = g.m_tiles * ((a.N + kTileN - 1) / kTileN);
+    const dim3 grid((uint32_t)((items + kXcds - 1) / kXcds * kXcds));
     return launch_kernel(mfma_gemm_grouped_kernel<FMT>, grid, dim3(64 * Tile128::NW), 0, stream,
                          ev, a, g);
 }
