@@ -452,6 +452,9 @@ def roofline(s, traffic, traffic_note, ceil=None):
          "frac": s["frac_of_8TBps"],
          "frac_median": round(s["GBps_median"] / PEAK_HBM_GBS, 4),
          "kernel_us_mean": k["mean"], "kernel_us_median": k["median"],
+         # back to back, one event pair around the timed region: kernels plus the gaps
+         "frac_timed_region": round(s["bytes_per_launch"] / s["timed_region_us_per_launch"] / 1e3
+                                    / PEAK_HBM_GBS, 4),
          "bytes_per_launch": s["bytes_per_launch"],
          "timing": "per-launch HIP events bound to the kernel dispatch (hipExtLaunchKernel) "
                    "over the timed region",
@@ -640,6 +643,13 @@ def pmc_summary(d, copy_bytes):
         out[w] = hbm
         table.append(f"| {w} | `{k}` | {n} | {f:.1f} | {wr:.1f} | {hbm:,} | {alg:,} | "
                      f"{hbm / alg:.4f} |")
+        # the run's other library kernels (the tensor scale's zero and finish passes)
+        others = {x for x, _, _ in _pmc_rows(p, "FETCH_SIZE") if "bsq::" in x and x != k}
+        for k2 in sorted(others):
+            _, f2, n2 = mean_of(f"{w}_fetch", "FETCH_SIZE", k2)
+            _, w2, _ = mean_of(f"{w}_write", "WRITE_SIZE", k2)
+            table.append(f"| {w} | `{k2}` | {n2} | {f2:.2f} | {w2:.2f} | "
+                         f"{int(round(f2 * 1024 * ff + w2 * 1024 * wf)):,} | | |")
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
