@@ -323,11 +323,12 @@ __device__ __forceinline__ int offsets_at_or_below(const KernelArgs& a, uint32_t
 // issued ahead of the data loads so it lands first); entries past G read as
 // zeros and are masked by index.  Offsets are nondecreasing, so the entries
 // <= r form a prefix, whose length is the number of set bits of four ballots.
-// Then scalar loads of the group's entries.  Against a binary search on the
-// scalar unit (about 100 scalar instructions and 8 dependent round trips per
-// wave) this took grouped NVFP4 on the 16384 x 7168 prefill routing from
-// 47.2-47.9 us to 45.5-46.0 and grouped MXFP4 from 44.8-45.0 to 44.2-44.3
-// (grouped MXFP8 56.3 -> 56.5-56.8), timed in alternation on one box.
+// Then scalar loads of the group's entries, under the data loads.  Against a
+// binary search on the scalar unit (about 100 scalar instructions and 8
+// dependent round trips per wave) this took grouped NVFP4 on the 16384 x 7168
+// prefill routing from 47.2-47.9 us to 45.4-45.9 and grouped MXFP4 from
+// 44.8-45.0 to 44.2-44.5 (grouped MXFP8 56.3 -> 56.4-56.6), timed in
+// alternation on one box.
 struct OffsetsLoad {
     __amdgpu_buffer_rsrc_t rsrc;
     u32x4_t v;
@@ -339,35 +340,62 @@ __device__ __forceinline__ OffsetsLoad issue_offsets(const KernelArgs& a, int la
     o.v = __builtin_amdgcn_raw_buffer_load_b128(o.rsrc, lane * 16, 0, 0);
     return o;
 }
+// Offsets <= r among entries [base, base + 256) held four per lane in v.
+__device__ __forceinline__ uint32_t count_round(const u32x4_t& v, int base, int G1, uint32_t r,
+                                                int lane) {
+    const int i0 = base + 4 * lane;
+    return (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(i0 < G1 && v.x <= r)) +
+           (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(i0 + 1 < G1 && v.y <= r)) +
+           (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(i0 + 2 < G1 && v.z <= r)) +
+           (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(i0 + 3 < G1 && v.w <= r));
+}
+
+// Number of offsets <= r.  A second and later round (more than 255 groups, r
+// at or past entry 256) loads and counts the next 256 entries.  PEEL takes the
+// first round out of the loop, so the wait before it covers the offsets load
+// alone, not the data loads issued after it: grouped NVFP4 45.99 -> 45.47 us;
+// for the MX formats, whose stores wait for every data load anyway, the loop
+// form measured faster (MXFP4 44.39 against 44.73, MXFP8 56.41 against 56.63;
+// best of four alternated runs each, one box).
+template <bool PEEL>
 __device__ __forceinline__ int count_at_or_below(const KernelArgs& a, const OffsetsLoad& o,
                                                  uint32_t r, int lane) {
     const int G1 = a.num_groups + 1;
-    u32x4_t v = o.v;
-    int cnt = 0;
-    for (int base = 0;; base += 256) {
-        const int i0 = base + 4 * lane;
-        const uint32_t c = (uint32_t)__builtin_popcountll(__ballot(i0 < G1 && v.x <= r)) +
-                           (uint32_t)__builtin_popcountll(__ballot(i0 + 1 < G1 && v.y <= r)) +
-                           (uint32_t)__builtin_popcountll(__ballot(i0 + 2 < G1 && v.z <= r)) +
-                           (uint32_t)__builtin_popcountll(__ballot(i0 + 3 < G1 && v.w <= r));
-        cnt += (int)c;
-        if (c < 256u || base + 256 >= G1) break;
-        v = __builtin_amdgcn_raw_buffer_load_b128(o.rsrc, (base + 256) * 4 + lane * 16, 0, 0);
+    if constexpr (PEEL) {
+        uint32_t c = count_round(o.v, 0, G1, r, lane);
+        int cnt = (int)c;
+        for (int base = 256; c == 256u && base < G1; base += 256) {
+            const u32x4_t v =
+                __builtin_amdgcn_raw_buffer_load_b128(o.rsrc, base * 4 + lane * 16, 0, 0);
+            c = count_round(v, base, G1, r, lane);
+            cnt += (int)c;
+        }
+        return cnt;
+    } else {
+        u32x4_t v = o.v;
+        int cnt = 0;
+        for (int base = 0;; base += 256) {
+            const uint32_t c = count_round(v, base, G1, r, lane);
+            cnt += (int)c;
+            if (c < 256u || base + 256 >= G1) break;
+            v = __builtin_amdgcn_raw_buffer_load_b128(o.rsrc, (base + 256) * 4 + lane * 16, 0, 0);
+        }
+        return cnt;
     }
-    return cnt;
 }
 
-template <bool NEED_SF>
+// NVFP4 needs the expert's tensor scale and takes the peeled count.
+template <bool NVFP4>
 __device__ __forceinline__ GroupInfo find_group_vec(const KernelArgs& a, const OffsetsLoad& o,
                                                     uint32_t r, int lane) {
     const int G = a.num_groups;
-    const int cnt = __builtin_amdgcn_readfirstlane(count_at_or_below(a, o, r, lane));
+    const int cnt = __builtin_amdgcn_readfirstlane(count_at_or_below<NVFP4>(a, o, r, lane));
     GroupInfo gi{-1, 0u, 0u, 0, 1.0f};
     if (cnt == 0 || cnt > G) return gi;
     gi.g = cnt - 1;
     gi.ro = a.row_offsets[gi.g];
     gi.so = a.scales_offsets[gi.g];
-    if constexpr (NEED_SF) {
+    if constexpr (NVFP4) {
         gi.id = a.expert_ids[gi.g];
         if (gi.id >= 0 && gi.id < a.num_experts) gi.sf = a.expert_sf[gi.id];
     }
