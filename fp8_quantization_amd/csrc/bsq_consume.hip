@@ -429,15 +429,21 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-template <int FMT, int NBUF, class Cfg>
+// SKIP_PAD (the grouped form, whose partial row tiles average a third padding):
+// chunks of A wholly past the rows are not loaded and 16-row blocks past them
+// not multiplied; the dense form keeps straight-line stages (the skip costs its
+// 256 x 256 MXFP8 tile registers enough to spill).
+template <int FMT, int NBUF, class Cfg, bool SKIP_PAD>
 __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const (&bufs)[NBUF]) {
     constexpr int kFmt = FMT == 1 ? 0 : 4;
     constexpr int kStepBytes = FMT == 1 ? 128 : 64;
     constexpr int kSteps = 128 / kStepBytes;                 // K steps per stage
     constexpr int kStageElems = kSteps * 128;
-    constexpr int kPerWave = Cfg::kPerWave;
     constexpr int TM = Cfg::TM, IM = Cfg::IM, JN = Cfg::JN;
     constexpr int kPerRecord = 4 / kSteps;                   // stages per 512-element scale record
+    // with two buffers a wave waits for all its loads (vmcnt 0) at the top of a stage, so
+    // waves may issue different numbers of them (SKIP_PAD)
+    static_assert(NBUF == 2, "the stage wait assumes two buffers");
     // the stage loop is unrolled by a multiple of both the buffer count and the stages per
     // record, so each unrolled stage's buffer and opsel byte are constants
     constexpr int kUnroll = NBUF % kPerRecord == 0 ? NBUF
@@ -460,9 +466,12 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const 
         const int kb0 = s * 128;
         int kb = kb0 + 16 * (cpiece ^ crow);
         kb = kb < row_bytes ? kb : 0;
+        // with SKIP_PAD a chunk wholly past the operand's rows is not loaded (its rows'
+        // products are never stored, so the stale bytes there are harmless)
 #pragma unroll
         for (int i = 0; i < Cfg::kChunksA; ++i) {
             const int chunk = wave + Cfg::NW * i, row = 8 * chunk + crow;
+            if (SKIP_PAD && 8 * chunk >= d.a_rows) break;
             const int64_t ra = row < d.a_rows ? row : d.a_rows - 1;
             dma16(d.a + ra * d.lda_q + kb, buf + chunk * 1024);
         }
@@ -505,13 +514,11 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const 
     for (int u = 0; u < kUnroll; ++u) {
         const int s = s0 + u;
         if (s >= nstages) break;
-        // this wave's loads of stage s are done once at most the later-issued stages'
-        // loads are outstanding; after the barrier every wave's are, and every wave has
-        // finished reading stage s - 1 (its MFMAs consumed those reads), so its buffer
-        // can be refilled.  No fence: the loads write LDS directly and the explicit
-        // count is the wait they need.
-        if (s + NBUF - 2 < nstages) wait_vm<kPerWave * (NBUF - 2)>();
-        else wait_vm<0>();
+        // this wave's loads of stage s are done after the wait; after the barrier every
+        // wave's are, and every wave has finished reading stage s - 1 (its MFMAs
+        // consumed those reads), so its buffer can be refilled.  No fence: the loads
+        // write LDS directly and the explicit wait is the one they need.
+        wait_vm<0>();
         asm volatile("s_barrier" ::: "memory");
         if (s + NBUF - 1 < nstages) issue(s + NBUF - 1, bufs[(u + NBUF - 1) % NBUF]);
         const uint8_t* buf = bufs[u % NBUF];
@@ -554,6 +561,7 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const 
             for (int jn = 0; jn < JN; ++jn) fb[jn] = fragment(TM * 128, 16 * (JN * wn + jn), j);
 #pragma unroll
             for (int im = 0; im < IM; ++im) {
+                if (SKIP_PAD && 16 * (IM * wm + im) >= d.a_rows) break;  // past the rows
                 const mfma_v8i fa = fragment(0, 16 * (IM * wm + im), j);
 #pragma unroll
                 for (int jn = 0; jn < JN; ++jn) {
@@ -605,9 +613,17 @@ __global__ void __launch_bounds__(64 * Cfg::NW) mfma_gemm_tiled_kernel(const Gem
     GemmTile d;
     dense_desc<Cfg::TM, Cfg::TN>(a, tiles_n, d);
     uint8_t* const bufs[2] = {stage0, stage1};
-    gemm_tile_dma<FMT, 2, Cfg>(d, bufs);
+    gemm_tile_dma<FMT, 2, Cfg, false>(d, bufs);
 }
 
+// The grouped form for groups of more than 16 rows on average.  Measured on
+// the prefill routing (16384 rows over 128 experts, N = 512, K = 7168,
+// MXFP4), these 128 x 128 tiles of 4 waves with both operands staged through
+// two LDS buffers ran 77-80 us; the alternatives tried ran slower: 128 x 256
+// tiles of 8 waves (88.6 us), B straight to registers with three LDS stages
+// for A (92), 64 x 128 tiles (91).  Copies of this kernel that skip the LDS
+// fragment reads, or the MFMAs, ran within 3% of it, and one that loads only
+// its first stage ran 40.7 us; one workgroup per CU instead of two ran 116.
 template <int FMT>
 __global__ void __launch_bounds__(64 * Tile128::NW)
 mfma_gemm_grouped_kernel(const GemmArgs a, const GroupedGemmArgs g) {
@@ -615,7 +631,7 @@ mfma_gemm_grouped_kernel(const GemmArgs a, const GroupedGemmArgs g) {
     GemmTile d;
     if (!grouped_desc_xcd<kTileM, kTileN>(a, g, d)) return;
     uint8_t* const bufs[2] = {stage0, stage1};
-    gemm_tile_dma<FMT, 2, Tile128>(d, bufs);
+    gemm_tile_dma<FMT, 2, Tile128, true>(d, bufs);
 }
 
 // ------------------------------------------------------------ decode regime

@@ -228,9 +228,13 @@ def grouped_case(fmt, G, E, N, K, rows, seed, misaligned=None):
 @pytest.mark.parametrize("fmt", [MXFP4, MXFP8])
 @pytest.mark.parametrize("G,E,N,K,rows", [(1, 1, 128, 256, 128), (5, 3, 100, 512, 300),
                                           (40, 16, 160, 1024, 900), (9, 4, 256, 7168, 700),
-                                          (130, 20, 96, 512, 3000), (200, 7, 48, 256, 9000)])
+                                          (130, 20, 96, 512, 3000), (200, 7, 48, 256, 9000),
+                                          (3, 2, 200, 128, 400), (4, 3, 130, 384, 500),
+                                          (6, 5, 272, 1664, 800)])
 def test_grouped_mfma_matches_oracle(bsq, fmt, G, E, N, K, rows):
-    """Groups of more than 16 rows on average: 128-row tiles staged in LDS."""
+    """Groups of more than 16 rows on average: 128-row tiles, A through LDS and
+    B into registers, three stages in flight.  K = 128 and 384 end on a half
+    stage in MXFP4 (256 elements a stage); 1664 is 13 K steps."""
     d = grouped_case(fmt, G, E, N, K, rows, seed=G + N + K + fmt)
     assert d["max_rows"] > 16 * G
     check_grouped_run(bsq, fmt, d, G, E, N, K)
@@ -367,6 +371,26 @@ def test_grouped_mfma_skips_bad_expert_ids_and_rows_past_max_rows(bsq):
         qb, sb = d["qb"][e * N:(e + 1) * N], d["sb"][e * N:(e + 1) * N]
         want = oracle.block_scaled_matmul(qa, sa, qb, sb, fmt, K)
         gemm_bound.check(got[lo:hi], qa, sa, qb, sb, fmt, K, want)
+
+
+@pytest.mark.parametrize("rows", [300, 30])
+def test_grouped_zero_k_writes_zeros(bsq, rows):
+    """K = 0 with 128-row (300 rows over 2 groups) and 32-row tiles: every
+    routed row of c is an empty sum, 0; rows no group owns keep 7.0.  No
+    operand is read (none is passed)."""
+    ro = np.array([0, rows // 3, rows - 5], np.uint32)
+    so = np.array([0, -(-(rows // 3) // 16) * 16, 0], np.uint32)
+    so[2] = so[1] + -(-(rows - 5 - rows // 3) // 16) * 16
+    out = torch.full((rows, 96), 7.0, dtype=torch.float32, device="cuda")
+    empty = torch.zeros((rows, 0), dtype=torch.uint8, device="cuda")
+    bsq.grouped_block_scaled_matmul_mfma(
+        empty, torch.zeros((int(so[2]) // 16, 0), dtype=torch.uint8, device="cuda"),
+        dev(ro.view(np.int32)), dev(so.view(np.int32)), dev(np.array([1, 0], np.int32)), rows,
+        int(so[2]), torch.zeros((2 * 96, 0), dtype=torch.uint8, device="cuda"),
+        torch.zeros((2 * 96 // 16, 0), dtype=torch.uint8, device="cuda"), 2, MXFP4, 0, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(got[:rows - 5] == 0.0) and np.all(got[rows - 5:] == 7.0)
 
 
 def test_zero_k_and_empty(bsq):
