@@ -17,14 +17,16 @@ Protocol.  Inputs are resident in HBM before timing starts.  Each workload's
 loop rotates over several copies of its buffers whose combined size is well
 above the 256 MB last-level (MALL) cache, so every step streams from HBM.
 The timed region is K back-to-back launches between two device
-synchronisations.  Every launch in it carries a pair of HIP events bound to
-its kernel's dispatch (``bsq_time_next_launch``, hipExtLaunchKernel on the
-launch stream): their elapsed time is the kernel's own execution, the figure
+synchronisations; the headline ``value`` is its host wall clock.  The same K
+launches then run again, each with a pair of HIP events bound to its kernel's
+dispatch (``bsq_time_next_launch``, hipExtLaunchKernel on the launch stream;
+kept out of the timed region because binding adds a few µs between
+launches): their elapsed time is the kernel's own execution, the figure
 rocprofv3's kernel trace reports, and the roofline fraction is computed from
-it (mean, and median beside it).  The headline ``value`` is the host wall
-clock of the same region.  For the large dense and grouped workloads the same
-job also times the same-byte-mix trivial stream of ``libbsq_ceiling.so`` on
-the same buffers (``ceiling``).  The CPU oracle is timed on a bounded sample
+it (mean, and median beside it).  For the large dense and grouped quantizer
+workloads and the two dequantizations the same job also times the
+same-byte-mix trivial stream of ``libbsq_ceiling.so`` on the same buffers
+(``ceiling``).  The CPU oracle is timed on a bounded sample
 of every quantizer workload on the host's cores, on one thread and on all of
 them, and its output is compared with the GPU's for that sample.
 
@@ -414,13 +416,27 @@ def ceiling(runner, u, steps, warmup):
     chunks per wave and at the other tile sizes; the fastest is the
     ceiling.  It runs right before the quantizer's own timing."""
     bsq, torch, case = runner.bsq, runner.torch, runner.case
-    M, K = case.x.shape
-    views = [(st["x"], st["q"][:M], st["s"][:M]) for st in runner.sets]
-    # at least 300 launches per tile size: together about 50 ms of streaming,
-    # which also brings the GPU to its steady clocks before the quantizer
-    steps = max(steps, 300)
     fmt = case.fmt
-    nbytes = int(M * K * bytes_per_element(fmt))
+    if runner.dequant:                   # the dequantizer's mix: codes and scales in, fp32 out
+        M, K = case.codes.shape[0], case.K
+        nbytes = algorithmic_bytes(case)[0]
+        kernel = "bsq::expand_kernel"
+        what = "dequantizer"
+
+        def run(st, uu, a, b):
+            bsq.ceiling_expand(st["q"], st["s"], fmt, K, uu, out=st["out"], start=a, stop=b)
+    else:
+        M, K = case.x.shape
+        nbytes = int(M * K * bytes_per_element(fmt))
+        kernel = "bsq::ceiling_kernel"
+        what = "quantizer"
+
+        def run(st, uu, a, b):
+            bsq.ceiling_stream(st["x"], fmt, uu, codes=st["q"][:M], scales=st["s"][:M],
+                               start=a, stop=b)
+    # at least 300 launches per tile size: together about 50 ms of streaming,
+    # which also brings the GPU to its steady clocks before the kernel
+    steps = max(steps, 300)
     by_u = {}
     for uu in (1, 2, 4):
         armed = {}
@@ -429,21 +445,20 @@ def ceiling(runner, u, steps, warmup):
             armed["ev"] = (a, b)
 
         def launch(i):
-            x, q, s = views[i % len(views)]
             a, b = armed.pop("ev", (None, None))
-            bsq.ceiling_stream(x, fmt, uu, codes=q, scales=s, start=a, stop=b)
+            run(runner.sets[i % len(runner.sets)], uu, a, b)
 
         _, _, kernel_us = timed_region(torch, arm, launch, steps, warmup)
         by_u[uu] = spread(kernel_us)
     best = min(by_u, key=lambda k: by_u[k]["mean"])
     k = by_u[best]
-    return {"kernel": f"bsq::ceiling_kernel, {M}x{K}, {['MXFP4', 'MXFP8', 'NVFP4'][fmt]} "
+    return {"kernel": f"{kernel}, {M}x{K}, {['MXFP4', 'MXFP8', 'NVFP4'][fmt]} {what} "
                       f"byte mix, best of 1 / 2 / 4 chunks per wave",
             "bytes_per_launch": nbytes, "chunks_per_wave": best, "kernel_us": k,
             "GBps": round(nbytes / k["mean"] / 1e3, 1),
             "frac_of_8TBps": round(nbytes / k["mean"] / 1e3 / PEAK_HBM_GBS, 4),
             "kernel_us_mean_by_chunks_per_wave": {str(a): b["mean"] for a, b in by_u.items()},
-            "quantizer_chunks_per_wave": u}
+            f"{what}_chunks_per_wave": u}
 
 
 def roofline(s, traffic, traffic_note, ceil=None):
@@ -696,6 +711,9 @@ def pmc_summary(d, copy_bytes):
 # ------------------------------------------------------------------ main
 
 LARGE = ("grouped_nvfp4", "dense_mxfp8", "dense_nvfp4")
+# the dequantizations, timed against their own trivial stream; the library's
+# dequantizer takes one 512-element chunk per wave
+DEQUANT = {"dequant_mxfp8": 1, "dequant_nvfp4": 1}
 
 
 def main():
@@ -740,7 +758,8 @@ def main():
     names.append(args.workload)
     results, head = {}, None
     for name in names:
-        u = quant[name][1] if name in quant and name in LARGE and not args.no_ceiling else None
+        u = None if args.no_ceiling else (quant[name][1] if name in quant and name in LARGE
+                                          else DEQUANT.get(name))
         case, runner, nbytes, s, ceil = measure(name, args.steps, args.warmup, u)
         if ceil is not None:
             log("[bench] ceiling", name, json.dumps(ceil))
@@ -751,6 +770,8 @@ def main():
             hbm_bound = nbytes / PEAK_HBM_GBS / 1e9 > gemm_flops(case) / peak / 1e12
             s.update({"bound": "hbm" if hbm_bound else "mfma", "TFLOPs": round(tf, 1),
                       "peak_TFLOPs": peak, "frac_of_peak": round(tf / peak, 4)})
+        if name in DEQUANT:
+            s["roofline"] = roofline(s, *traffic_from_counters(name), ceil)
         if name in quant:
             if name in LARGE:
                 s["roofline"] = roofline(s, *traffic_from_counters(name), ceil)

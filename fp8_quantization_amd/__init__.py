@@ -406,15 +406,7 @@ def ceiling_stream(x: torch.Tensor, fmt, chunks_per_wave: int, codes=None, scale
     nothing of the method.  ``start`` / ``stop``: optional recorded
     ``torch.cuda.Event`` pair bound to the kernel's dispatch.  Returns the
     written (codes, scales)."""
-    global _ceiling_lib
-    if _ceiling_lib is None:
-        path = os.path.join(os.path.dirname(LIB_PATH), "libbsq_ceiling.so")
-        if not os.path.exists(path):
-            raise ImportError(f"{path} is not built; run fp8_quantization_amd/build.py")
-        lib_c = ctypes.CDLL(path)
-        lib_c.bsq_ceiling_stream.argtypes = [_i32, _p, _i64, _i64, _p, _p, _i32, _p, _p, _p]
-        lib_c.bsq_ceiling_stream.restype = _i32
-        _ceiling_lib = lib_c
+    lib_c = _ceiling()
     f = _fmt(fmt)
     x = _as_bf16_matrix(x)
     if not x.is_contiguous():
@@ -429,9 +421,49 @@ def ceiling_stream(x: torch.Tensor, fmt, chunks_per_wave: int, codes=None, scale
         if not t.is_contiguous() or tuple(t.shape) != (M, cols) or t.dtype != torch.uint8:
             raise TypeError(f"{name} must be a contiguous uint8 [{M}, {cols}] tensor")
     ev = [None if e is None else ctypes.c_void_p(e.cuda_event) for e in (start, stop)]
-    st = _ceiling_lib.bsq_ceiling_stream(f, _ptr(x), M, K, _ptr(codes), _ptr(scales),
-                                         chunks_per_wave, ev[0], ev[1],
-                                         _stream_ptr(stream, x.device))
+    st = lib_c.bsq_ceiling_stream(f, _ptr(x), M, K, _ptr(codes), _ptr(scales), chunks_per_wave,
+                                  ev[0], ev[1], _stream_ptr(stream, x.device))
     if st != 0:
         raise BsqError(st, "bsq_ceiling_stream rejected its arguments or failed to launch")
     return codes, scales
+
+
+def ceiling_expand(codes: torch.Tensor, scales: torch.Tensor, fmt, K: int,
+                   chunks_per_wave: int, out=None, start=None, stop=None, stream=None):
+    """The dequantizer-mix trivial stream of ``libbsq_ceiling.so``
+    (``include/bsq_ceiling.h``): reads dense codes [M, K/2 or K] and row-major
+    scales [M, K/32 or K/16] and writes fp32 [M, K] with the dequantizer's
+    tiles and instructions, decoding nothing.  Returns out."""
+    lib_c = _ceiling()
+    f = _fmt(fmt)
+    M = codes.shape[0]
+    for name, t, cols in (("codes", codes, code_width(f, K)),
+                          ("scales", scales, K // BLOCK_SIZE[f])):
+        if not t.is_contiguous() or tuple(t.shape) != (M, cols) or t.dtype != torch.uint8:
+            raise TypeError(f"{name} must be a contiguous uint8 [{M}, {cols}] tensor")
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float32, device=codes.device)
+    if not out.is_contiguous() or tuple(out.shape) != (M, K) or out.dtype != torch.float32:
+        raise TypeError(f"out must be a contiguous float32 [{M}, {K}] tensor")
+    ev = [None if e is None else ctypes.c_void_p(e.cuda_event) for e in (start, stop)]
+    st = lib_c.bsq_ceiling_expand(f, _ptr(codes), _ptr(scales), M, K, _ptr(out), chunks_per_wave,
+                                  ev[0], ev[1], _stream_ptr(stream, codes.device))
+    if st != 0:
+        raise BsqError(st, "bsq_ceiling_expand rejected its arguments or failed to launch")
+    return out
+
+
+def _ceiling():
+    """libbsq_ceiling.so, loaded on first use."""
+    global _ceiling_lib
+    if _ceiling_lib is None:
+        path = os.path.join(os.path.dirname(LIB_PATH), "libbsq_ceiling.so")
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is not built; run fp8_quantization_amd/build.py")
+        lib_c = ctypes.CDLL(path)
+        lib_c.bsq_ceiling_stream.argtypes = [_i32, _p, _i64, _i64, _p, _p, _i32, _p, _p, _p]
+        lib_c.bsq_ceiling_stream.restype = _i32
+        lib_c.bsq_ceiling_expand.argtypes = [_i32, _p, _p, _i64, _i64, _p, _i32, _p, _p, _p]
+        lib_c.bsq_ceiling_expand.restype = _i32
+        _ceiling_lib = lib_c
+    return _ceiling_lib

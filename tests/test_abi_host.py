@@ -21,8 +21,8 @@ MXFP4, MXFP8, NVFP4 = 0, 1, 2
 FAKE = 0x10000  # aligned, never dereferenced
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, re.M)))
 
@@ -69,6 +69,32 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
     assert lib.bsq_version().decode().count(".") == 2
+
+
+def test_ceiling_library_exports_its_header_and_rejects_bad_arguments():
+    """libbsq_ceiling.so (the measurement streams) exports what
+    include/bsq_ceiling.h declares, and refuses bad arguments before any HIP
+    call (return 1), with M = 0 a no-op (0)."""
+    header = os.path.join(ROOT, "include", "bsq_ceiling.h")
+    assert declared_functions(header) == ["bsq_ceiling_expand", "bsq_ceiling_stream"]
+    path = os.path.join(ROOT, "fp8_quantization_amd", "libbsq_ceiling.so")
+    if not os.path.exists(path):
+        from fp8_quantization_amd import build
+
+        build.build()
+    c = ctypes.CDLL(path)
+    i64, i32, p = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    c.bsq_ceiling_stream.argtypes = [i32, p, i64, i64, p, p, i32, p, p, p]
+    c.bsq_ceiling_expand.argtypes = [i32, p, p, i64, i64, p, i32, p, p, p]
+    assert c.bsq_ceiling_stream(0, FAKE, 4, 700, FAKE, FAKE, 1, None, None, None) == 1
+    assert c.bsq_ceiling_stream(0, FAKE, 4, 512, FAKE, FAKE, 3, None, None, None) == 1
+    assert c.bsq_ceiling_stream(3, FAKE, 4, 512, FAKE, FAKE, 1, None, None, None) == 1
+    assert c.bsq_ceiling_stream(0, FAKE, 0, 512, FAKE, FAKE, 1, None, None, None) == 0
+    assert c.bsq_ceiling_expand(0, FAKE, FAKE, 4, 700, FAKE, 1, None, None, None) == 1
+    assert c.bsq_ceiling_expand(1, FAKE, FAKE, 4, 512, FAKE, 8, None, None, None) == 1
+    assert c.bsq_ceiling_expand(2, FAKE, FAKE, 4, 512, FAKE + 4, 1, None, None, None) == 1
+    assert c.bsq_ceiling_expand(2, FAKE, FAKE, 4, 512, FAKE, 1, FAKE, None, None) == 1
+    assert c.bsq_ceiling_expand(2, FAKE, FAKE, 0, 512, FAKE, 1, None, None, None) == 0
 
 
 def dense(lib, fmt=MXFP4, bs=32, layout=0, x=FAKE, M=4, K=64, ldx=64, codes=FAKE, ldq=None,

@@ -1,10 +1,10 @@
 """The measurement aids: kernel events bound to a launch's dispatch
-(``bsq_time_next_launch``) and the same-byte-mix trivial stream of
-``libbsq_ceiling.so``.
+(``bsq_time_next_launch``) and the same-byte-mix trivial streams of
+``libbsq_ceiling.so`` (the quantizer's and the dequantizer's).
 
 The events must time the kernel alone and leave its results unchanged; the
-trivial stream must write exactly the bytes its header documents, so that its
-time is that of a stream moving the quantizer's bytes."""
+trivial streams must write exactly the bytes their header documents, so that
+their times are those of streams moving the kernels' bytes."""
 import numpy as np
 import pytest
 import torch
@@ -123,3 +123,38 @@ def test_ceiling_stream_rejects_bad_arguments(bsq):
     x = torch.zeros((4, 512), dtype=torch.int16, device="cuda")
     with pytest.raises(bsq.BsqError):
         bsq.ceiling_stream(x, oracle.MXFP8, 3)                 # 3 chunks per wave
+
+
+@pytest.mark.parametrize("fmt", [oracle.MXFP4, oracle.MXFP8, oracle.NVFP4])
+@pytest.mark.parametrize("u", [1, 2, 4])
+@pytest.mark.parametrize("M,K", [(5, 7168), (3, 1536), (9, 512)])
+def test_ceiling_expand_writes_the_documented_words(bsq, fmt, u, M, K):
+    rng = np.random.default_rng(M * K + u + fmt + 99)
+    width = K if fmt == oracle.MXFP8 else K // 2
+    bs = 16 if fmt == oracle.NVFP4 else 32
+    codes = rng.integers(0, 256, (M, width), dtype=np.uint8)
+    scales = rng.integers(0, 256, (M, K // bs), dtype=np.uint8)
+    lanes = K // 8                                              # lane-slots of 8 elements
+    if fmt == oracle.MXFP8:
+        w = codes.view(np.uint32).reshape(M, lanes, 2)
+        q0, q1 = w[:, :, 0], w[:, :, 1]
+    else:
+        q0, q1 = codes.view(np.uint32).reshape(M, lanes), np.zeros((M, lanes), np.uint32)
+    s = scales[:, (8 * np.arange(lanes)) // bs].astype(np.uint32)
+    want = np.concatenate([np.repeat((q0 ^ s)[:, :, None], 4, 2),
+                           np.repeat((q1 ^ s)[:, :, None], 4, 2)], axis=2).reshape(M, K)
+    out = bsq.ceiling_expand(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
+                             fmt, K, u)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), want)
+
+
+def test_ceiling_expand_rejects_bad_arguments(bsq):
+    q = torch.zeros((4, 256), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((4, 16), dtype=torch.uint8, device="cuda")
+    with pytest.raises(bsq.BsqError):
+        bsq.ceiling_expand(q, s, oracle.MXFP4, 512, 3)            # 3 chunks per wave
+    q = torch.zeros((4, 350), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((4, 21), dtype=torch.uint8, device="cuda")
+    with pytest.raises(bsq.BsqError):
+        bsq.ceiling_expand(q, s, oracle.MXFP4, 700, 1)            # K not a multiple of 512
