@@ -34,6 +34,9 @@ Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 10]
        [--workload grouped_nvfp4] [--no-secondary] [--no-cpu-baseline] [--no-ceiling]
        python bench.py --copy-bytes N          (plain copy, for counter calibration)
        python bench.py --pmc-summary DIR       (counters of rocprofv3 --pmc runs -> traffic)
+       python bench.py --pmc-gemm-summary DIR  (matrix-core counters of the GEMM workloads)
+       python bench.py --trace-summary DIR [--bench-line FILE]
+                                               (a rocprofv3 kernel trace of this script)
 """
 import argparse
 import glob
@@ -632,6 +635,102 @@ def _main_kernel(rows):
     return max(tot, key=tot.get) if tot else None
 
 
+# each workload's main kernel in a trace of this script, by name
+TRACE_KERNELS = {
+    "grouped_nvfp4": "quantize_kernel<2, true, 4>", "dense_nvfp4": "quantize_kernel<2, false, 4>",
+    "dense_mxfp8": "quantize_kernel<1, false, 2>", "grouped_mxfp4": "quantize_kernel<0, true, 4>",
+    "grouped_mxfp8": "quantize_kernel<1, true, 4>", "tsf_dense_nvfp4": "tsf_amax_kernel<false>",
+    "tsf_grouped_nvfp4": "tsf_amax_kernel<true>", "dequant_mxfp8": "dequant_kernel<1, 1>",
+    "dequant_nvfp4": "dequant_kernel<2, 1>",
+    "mfma_grouped_gemm_mxfp4": "mfma_gemm_grouped_kernel<0>",
+    "mfma_grouped_gemm_mxfp4_decode": "mfma_gemm_grouped_skinny_kernel<0, 1>"}
+
+
+def trace_summary(d, bench_line=None):
+    """Markdown tables of a rocprofv3 --kernel-trace --stats run of this
+    script in d (output name "bench"): per library kernel, calls and average /
+    median / min / max duration; then, per large workload, the mean duration
+    of its main kernel's back-to-back dispatches (the timed region) and of its
+    event-bound ones, beside the events' own mean from the bench line printed
+    under the profiler (bench_line, optional)."""
+    import csv
+    by = {}
+    with open(os.path.join(d, "bench_kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            by.setdefault(r["Kernel_Name"], []).append(
+                (int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    print("| kernel | calls | average us | median us | min us | max us |")
+    print("|---|---|---|---|---|---|")
+    with open(os.path.join(d, "bench_kernel_stats.csv")) as f:
+        for r in csv.DictReader(f):
+            n = r["Name"]
+            if "bsq::" not in n and "ceiling_kernel" not in n and "expand_kernel" not in n:
+                continue                                 # library and ceiling kernels only
+            med = float(np.median([(e - b) / 1e3 for b, e in by[n]]))
+            short = n.replace("(anonymous namespace)::", "").replace("bsq::", "")
+            print(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {med:.2f} | "
+                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    ev = {}
+    if bench_line:
+        line = json.loads(open(bench_line).read().strip().splitlines()[-1])
+        ev[HEADLINE] = line["roofline"]["kernel_us_mean"]     # a run with the default headline
+        for n, w in line.get("workloads", {}).items():
+            ev[n] = w["kernel_us"]["mean"]
+    print("\n| workload | trace, dispatches 11-110 (back to back) | trace, dispatches 111-210 "
+          "(event-bound) | events under the profiler |")
+    print("|---|---|---|---|")
+    for w, k in TRACE_KERNELS.items():
+        names = [n for n in by if k in n]
+        if not names:
+            continue
+        t = np.array([(e - b) / 1e3 for b, e in sorted(by[names[0]])])
+        e = f"{ev[w]:.2f}" if w in ev else ""
+        print(f"| {w} | {t[10:110].mean():.2f} | {t[110:210].mean():.2f} | {e} |")
+
+
+GEMM_COUNTERS = ("SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS",
+                 "SQ_LDS_BANK_CONFLICT", "SQ_VALU_MFMA_BUSY_CYCLES")
+
+
+def pmc_gemm_summary(d):
+    """A markdown table of the matrix-core counters of each GEMM workload's
+    run in d (rocprofv3 --kernel-trace --pmc output named <workload>_p1):
+    means per dispatch after the first, the kernel's duration under the
+    profiler, and the committed HBM bytes (profiles/pmc_traffic.json) against
+    the algorithmic bytes."""
+    import csv
+    traffic = {}
+    try:
+        traffic = json.load(open(TRAFFIC_FILE)).get("consume", {}).get("hbm_bytes_per_launch", {})
+    except (OSError, ValueError):
+        pass
+    print("| workload | kernel | kernel µs (profiled) | GRBM_GUI_ACTIVE / µs | " +
+          " | ".join(GEMM_COUNTERS) + " | HBM bytes | algorithmic bytes | ratio |")
+    print("|" + "---|" * (len(GEMM_COUNTERS) + 7))
+    for p in sorted(glob.glob(os.path.join(d, "*_p1_counter_collection.csv"))):
+        w = os.path.basename(p)[:-len("_p1_counter_collection.csv")]
+        per, dur = {}, {}
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                if "bsq::" not in r["Kernel_Name"]:
+                    continue
+                key = (r["Kernel_Name"], int(r["Dispatch_Id"]))
+                c = per.setdefault(key, {})
+                c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                dur[key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        keys = sorted(per, key=lambda k: k[1])[1:]       # after the first profiled dispatch
+        if not keys:
+            continue
+        us = float(np.mean([dur[k] for k in keys]))
+        mean = {c: float(np.mean([per[k].get(c, 0.0) for k in keys]))
+                for c in GEMM_COUNTERS + ("GRBM_GUI_ACTIVE",)}
+        alg = algorithmic_bytes(load_workload(w))[0]
+        hbm = traffic.get(w)
+        tail = f"{hbm:,} | {alg:,} | {hbm / alg:.3f}" if hbm else f"| {alg:,} |"
+        print(f"| {w} | `{keys[0][0]}` | {us:.1f} | {mean['GRBM_GUI_ACTIVE'] / us:.0f} | " +
+              " | ".join(f"{mean[c]:.4g}" for c in GEMM_COUNTERS) + f" | {tail} |")
+
+
 def pmc_summary(d, copy_bytes):
     """Turn rocprofv3 --pmc runs into HBM bytes per launch: FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch) of each workload's main kernel, each scaled
@@ -727,8 +826,17 @@ def main():
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--pmc-summary", default="")
+    ap.add_argument("--pmc-gemm-summary", default="")
+    ap.add_argument("--trace-summary", default="")
+    ap.add_argument("--bench-line", default="")
     args = ap.parse_args()
 
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.bench_line or None)
+        return
+    if args.pmc_gemm_summary:
+        pmc_gemm_summary(args.pmc_gemm_summary)
+        return
     if args.pmc_summary:
         pmc_summary(args.pmc_summary, args.copy_bytes or 268435456)
         return
