@@ -273,6 +273,33 @@ def test_grouped_random_offsets(bsq, fmt, G, gather, first, extra):
 
 @pytest.mark.parametrize("fmt", [oracle.MXFP4, oracle.MXFP8, oracle.NVFP4],
                          ids=["mxfp4", "mxfp8", "nvfp4"])
+@pytest.mark.parametrize("G", [255, 256, 257, 511, 512, 513])
+@pytest.mark.parametrize("gather", [False, True], ids=["direct", "gather"])
+def test_grouped_search_round_boundaries(bsq, fmt, G, gather):
+    """The group lookup counts row_offsets 256 entries at a time: G + 1 =
+    256, 257, 258 entries (one round, a second round of one and of two
+    entries) and 512, 513, 514.  Every group owns at least one row, so the
+    last groups' rows sit at each round's edge, and 5 rows past the last group
+    are owned by none (left as they were)."""
+    rng = np.random.default_rng(G * 7 + fmt + gather)
+    K = 512
+    counts = 1 + rng.multinomial(G, np.full(G, 1.0 / G))
+    rows = int(counts.sum())
+    S = rows + 5
+    x = W.random_bf16((S, K), seed=G + 3, scale_log2_range=(-10, 10))
+    ro, so = W.offsets_from_counts(counts, 8)
+    E = G + 5
+    ids = rng.integers(0, E, G).astype(np.int32)
+    sf = (np.exp2(rng.uniform(-12, 2, E)) * 0.37).astype(np.float32) \
+        if fmt == oracle.NVFP4 else None
+    ri = rng.integers(0, S, rows + 5).astype(np.int32) if gather else None
+    c = W.GroupedCase(f"g{G}_boundary", fmt, x, ro, so, ids, sf, ri, max_rows=rows + 5,
+                      num_scale_rows=int(so[-1]) + 2)
+    assert_same(*grouped_pair(bsq, c, pad_rows=2, pad_scale_rows=3), c.name)
+
+
+@pytest.mark.parametrize("fmt", [oracle.MXFP4, oracle.MXFP8, oracle.NVFP4],
+                         ids=["mxfp4", "mxfp8", "nvfp4"])
 @pytest.mark.parametrize("G,gather,K", [(5, False, 4608), (129, True, 4608), (600, False, 4608),
                                          (129, True, 4544), (7, False, 4544)])
 def test_grouped_large_problem_path(bsq, fmt, G, gather, K):
