@@ -329,16 +329,42 @@ __device__ __forceinline__ int offsets_at_or_below(const KernelArgs& a, uint32_t
 // prefill routing from 47.2-47.9 us to 45.4-45.9 and grouped MXFP4 from
 // 44.8-45.0 to 44.2-44.5 (grouped MXFP8 56.3 -> 56.4-56.6), timed in
 // alternation on one box.
+// With REGS the same 256 entries of scales_offsets (and, for NVFP4,
+// expert_ids) are loaded beside them, so a group among the first 256 takes its
+// entries from these registers (v_readlane) instead of scalar loads issued
+// after the search.  Measured on the 16384 x 7168 prefill routing it saves
+// 0.2-0.7 us per format (NVFP4 45.4-45.8 -> 45.0-45.1 in two alternated
+// runs); on the decode gathers (one chunk per wave, latency-bound) the extra
+// load cost 0.07 us per launch where the scalar loads overlap the arithmetic,
+// so one-chunk tiles keep them.
+template <bool NVFP4>
 struct OffsetsLoad {
     __amdgpu_buffer_rsrc_t rsrc;
-    u32x4_t v;
+    u32x4_t v, so, ids;
 };
-__device__ __forceinline__ OffsetsLoad issue_offsets(const KernelArgs& a, int lane) {
-    OffsetsLoad o;
+template <bool NVFP4, bool REGS>
+__device__ __forceinline__ OffsetsLoad<NVFP4> issue_offsets(const KernelArgs& a, int lane) {
+    OffsetsLoad<NVFP4> o;
+    const int G = a.num_groups;
     o.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(a.row_offsets), (short)0,
-                                               (a.num_groups + 1) * 4, kBufferWord3);
+                                               (G + 1) * 4, kBufferWord3);
     o.v = __builtin_amdgcn_raw_buffer_load_b128(o.rsrc, lane * 16, 0, 0);
+    o.so = o.ids = (u32x4_t){0u, 0u, 0u, 0u};
+    if constexpr (REGS)
+        o.so = __builtin_amdgcn_raw_buffer_load_b128(
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(a.scales_offsets), (short)0,
+                                              (G + 1) * 4, kBufferWord3), lane * 16, 0, 0);
+    if constexpr (REGS && NVFP4)
+        o.ids = __builtin_amdgcn_raw_buffer_load_b128(
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(a.expert_ids), (short)0,
+                                              G * 4, kBufferWord3), lane * 16, 0, 0);
     return o;
+}
+// Entry g (< 256) of the four-per-lane registers w: lane g / 4, component g % 4.
+__device__ __forceinline__ uint32_t entry_of(const u32x4_t& w, int g) {
+    const int c = g & 3;
+    const uint32_t x = c == 0 ? w.x : c == 1 ? w.y : c == 2 ? w.z : w.w;
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, g >> 2);
 }
 // Offsets <= r among entries [base, base + 256) held four per lane in v.
 __device__ __forceinline__ uint32_t count_round(const u32x4_t& v, int base, int G1, uint32_t r,
@@ -358,8 +384,9 @@ __device__ __forceinline__ uint32_t count_round(const u32x4_t& v, int base, int 
 // form measured faster (MXFP4 44.39 against 44.73, MXFP8 56.41 against 56.63;
 // best of four alternated runs each, one box).
 template <bool PEEL>
-__device__ __forceinline__ int count_at_or_below(const KernelArgs& a, const OffsetsLoad& o,
-                                                 uint32_t r, int lane) {
+__device__ __forceinline__ int count_at_or_below(const KernelArgs& a,
+                                                 const OffsetsLoad<PEEL>& o, uint32_t r,
+                                                 int lane) {
     const int G1 = a.num_groups + 1;
     if constexpr (PEEL) {
         uint32_t c = count_round(o.v, 0, G1, r, lane);
@@ -385,23 +412,28 @@ __device__ __forceinline__ int count_at_or_below(const KernelArgs& a, const Offs
 }
 
 // NVFP4 needs the expert's tensor scale and takes the peeled count.
-template <bool NVFP4>
-__device__ __forceinline__ GroupInfo find_group_vec(const KernelArgs& a, const OffsetsLoad& o,
-                                                    uint32_t r, int lane) {
+template <bool NVFP4, bool REGS>
+__device__ __forceinline__ GroupInfo find_group_vec(const KernelArgs& a,
+                                                    const OffsetsLoad<NVFP4>& o, uint32_t r,
+                                                    int lane) {
     const int G = a.num_groups;
     const int cnt = __builtin_amdgcn_readfirstlane(count_at_or_below<NVFP4>(a, o, r, lane));
     GroupInfo gi{-1, 0u, 0u, 0, 1.0f};
     if (cnt == 0 || cnt > G) return gi;
     gi.g = cnt - 1;
-    gi.ro = a.row_offsets[gi.g];
-    gi.so = a.scales_offsets[gi.g];
-    if constexpr (NVFP4) {
-        gi.id = a.expert_ids[gi.g];
-        if (gi.id >= 0 && gi.id < a.num_experts) gi.sf = a.expert_sf[gi.id];
+    if (REGS && gi.g < 256) {            // in the registers loaded with the first round
+        gi.ro = entry_of(o.v, gi.g);
+        gi.so = entry_of(o.so, gi.g);
+        if constexpr (NVFP4) gi.id = (int32_t)entry_of(o.ids, gi.g);
+    } else {
+        gi.ro = a.row_offsets[gi.g];
+        gi.so = a.scales_offsets[gi.g];
+        if constexpr (NVFP4) gi.id = a.expert_ids[gi.g];
     }
+    if constexpr (NVFP4)
+        if (gi.id >= 0 && gi.id < a.num_experts) gi.sf = a.expert_sf[gi.id];
     return gi;
 }
-
 // t / tiles_per_row by multiply-high with the host's magic constant
 // M = ceil(2^64 / d): for t < 2^32, floor(t * M / 2^64) = floor(t / d)
 // because t * (M - 2^64 / d) / 2^64 < 2^-32 <= 1/d.  d = 1 is sent as M = 0.
@@ -418,7 +450,7 @@ __device__ __forceinline__ uint32_t div_tiles(uint32_t t, const KernelArgs& a) {
 // converts chunk u as soon as its own load has landed while the later ones
 // are still in flight.  Code stores go through a descriptor over the row's
 // codes, which drops lanes past K.
-template <int FMT, bool GROUPED, int N, int POLICY>
+template <int FMT, bool GROUPED, int N, int POLICY, bool REGS>
 __device__ __forceinline__ void quantize_tile(const KernelArgs& a, uint32_t row, int c0,
                                               int lane) {
     using T = FormatTraits<FMT>;
@@ -430,8 +462,8 @@ __device__ __forceinline__ void quantize_tile(const KernelArgs& a, uint32_t row,
         }
     }
     const uint16_t* xrow = a.x + src * a.ldx;
-    OffsetsLoad offs{};
-    if constexpr (GROUPED) offs = issue_offsets(a, lane);
+    OffsetsLoad<FMT == 2> offs{};
+    if constexpr (GROUPED) offs = issue_offsets<FMT == 2, REGS>(a, lane);
     u32x4_t w[N];
 #pragma unroll
     for (int u = 0; u < N; ++u) {
@@ -442,7 +474,7 @@ __device__ __forceinline__ void quantize_tile(const KernelArgs& a, uint32_t row,
     int64_t scale_row = row;
     float tsf = a.tensor_sf;
     if constexpr (GROUPED) {
-        const GroupInfo gi = find_group_vec<FMT == 2>(a, offs, row, lane);
+        const GroupInfo gi = find_group_vec<FMT == 2, REGS>(a, offs, row, lane);
         if (gi.g < 0) return;
         scale_row = (int64_t)gi.so + ((int64_t)row - (int64_t)gi.ro);
         if (scale_row < 0 || scale_row >= a.num_scale_rows) return;
@@ -515,6 +547,7 @@ template <int FMT, bool GROUPED, int U>
 __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const KernelArgs a) {
     using T = FormatTraits<FMT>;
     constexpr int kPolicy = (T::kFp4 && U > 1) ? kStoreWriteThrough : kStoreStream;
+    constexpr bool kRegs = U > 1;        // group entries from registers (large problems)
     const int lane = (int)(threadIdx.x & (kWaveSize - 1));
     // the tile index is wave-uniform: keep it (and all row arithmetic) scalar
     const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock +
@@ -524,12 +557,12 @@ __global__ void __launch_bounds__(kThreadsPerBlock) quantize_kernel(const Kernel
     const int c0 = (int)(t - row * (uint32_t)a.tiles_per_row) * U;
     const int nch = min(U, a.chunks_per_row - c0);  // chunks in this tile (>= 1)
     if (nch == U) {
-        quantize_tile<FMT, GROUPED, U, kPolicy>(a, row, c0, lane);
+        quantize_tile<FMT, GROUPED, U, kPolicy, kRegs>(a, row, c0, lane);
     } else if constexpr (U > 1) {
-        if (nch == 1) quantize_tile<FMT, GROUPED, 1, kPolicy>(a, row, c0, lane);
+        if (nch == 1) quantize_tile<FMT, GROUPED, 1, kPolicy, kRegs>(a, row, c0, lane);
         if constexpr (U > 2) {
-            if (nch == 2) quantize_tile<FMT, GROUPED, 2, kPolicy>(a, row, c0, lane);
-            if (nch == 3) quantize_tile<FMT, GROUPED, 3, kPolicy>(a, row, c0, lane);
+            if (nch == 2) quantize_tile<FMT, GROUPED, 2, kPolicy, kRegs>(a, row, c0, lane);
+            if (nch == 3) quantize_tile<FMT, GROUPED, 3, kPolicy, kRegs>(a, row, c0, lane);
         }
     }
 }
