@@ -126,3 +126,56 @@ def test_bench_refuses_more_than_one_gpu(n):
                          capture_output=True, text=True, timeout=120, cwd=root)
     assert res.returncode == 2
     assert "one GPU" in res.stderr and res.stdout == ""
+
+
+def _write_csv(path, header, rows):
+    import csv
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_trace_summary_tables(tmp_path, capsys):
+    """--trace-summary: per-kernel calls and durations of the library and ceiling
+    kernels only, and per workload the means over the back-to-back and the
+    event-bound dispatch windows (dispatches 11-110 and 111-210)."""
+    k = "void bsq::(anonymous namespace)::quantize_kernel<2, true, 4>(bsq::KernelArgs)"
+    rows = [[k, 1000 * i, 1000 * i + (40_000 if i < 110 else 41_000)] for i in range(210)]
+    rows += [["__amd_rocclr_copyBuffer", 0, 5000]]
+    _write_csv(tmp_path / "bench_kernel_trace.csv",
+               ["Kernel_Name", "Start_Timestamp", "End_Timestamp"], rows)
+    _write_csv(tmp_path / "bench_kernel_stats.csv",
+               ["Name", "Calls", "AverageNs", "MinNs", "MaxNs"],
+               [[k, 210, 40476.2, 40000, 41000], ["__amd_rocclr_copyBuffer", 1, 5000, 5000, 5000]])
+    bench.trace_summary(str(tmp_path))
+    out = capsys.readouterr().out
+    assert "quantize_kernel<2, true, 4>" in out and "rocclr" not in out
+    assert "| 210 | 40.48 |" in out
+    assert "| grouped_nvfp4 | 40.00 | 41.00 |" in out
+
+
+def test_pmc_gemm_summary_table(tmp_path, capsys, monkeypatch):
+    """--pmc-gemm-summary: means per dispatch after the first, against the
+    committed HBM bytes and the workload's algorithmic bytes."""
+    k = "void bsq::(anonymous namespace)::mfma_gemm_grouped_kernel<0>(x)"
+    rows = []
+    for d in range(1, 4):
+        for c, v in (("SQ_INSTS_MFMA", 100.0 * d), ("GRBM_GUI_ACTIVE", 2000.0)) + tuple(
+                (c, 1.0) for c in bench.GEMM_COUNTERS if c != "SQ_INSTS_MFMA"):
+            rows.append([k, d, c, v, 0, 2000 * 1000])          # 2000 us each
+    _write_csv(tmp_path / "mfma_grouped_gemm_mxfp4_p1_counter_collection.csv",
+               ["Kernel_Name", "Dispatch_Id", "Counter_Name", "Counter_Value", "Start_Timestamp",
+                "End_Timestamp"], rows)
+    alg = bench.algorithmic_bytes(W.grouped_gemm_prefill(W.MXFP4))[0]
+    tf = tmp_path / "traffic.json"
+    tf.write_text('{"consume": {"hbm_bytes_per_launch": {"mfma_grouped_gemm_mxfp4": %d}}}'
+                  % (2 * alg))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tf))
+    bench.pmc_gemm_summary(str(tmp_path))
+    out = capsys.readouterr().out
+    line = [ln for ln in out.splitlines() if ln.startswith("| mfma_grouped_gemm_mxfp4 |")][0]
+    cells = [c.strip() for c in line.split("|")]
+    assert cells[3] == "2000.0"                   # kernel µs, dispatches 2 and 3
+    assert cells[5] == "250"                      # SQ_INSTS_MFMA: mean of 200 and 300
+    assert cells[-2] == "2.000"                   # HBM over algorithmic bytes
