@@ -298,6 +298,41 @@ def test_grouped_search_round_boundaries(bsq, fmt, G, gather):
     assert_same(*grouped_pair(bsq, c, pad_rows=2, pad_scale_rows=3), c.name)
 
 
+@pytest.mark.parametrize("fmt", [oracle.MXFP4, oracle.NVFP4], ids=["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("M,K,pad_q,pad_s", [(1100, 4032, 4, 1), (700, 6160, 8, 0),
+                                             (700, 6144, 4, 2), (1030, 4096, 12, 3)])
+def test_large_path_misaligned_rows_and_partial_tiles(bsq, fmt, M, K, pad_q, pad_s):
+    """FP4 over 2^22 elements (tiles of 4 chunks, write-through code stores)
+    into code rows only 4- or 8-byte aligned (strides K/2 + 4, + 8, + 12
+    bytes) and scale rows at alternating even and odd addresses.  K = 4032 is
+    7 whole chunks and a partial one, so a row's second tile is full but holds
+    the partial chunk; K = 6160 (NVFP4 only) is 12 whole chunks and a
+    16-element one."""
+    if fmt == oracle.MXFP4 and K % 32:
+        pytest.skip("MXFP4 needs K a multiple of 32")
+    assert M * K > (1 << 22)
+    x = W.random_bf16((M, K), seed=M + K + pad_q, scale_log2_range=(-20, 20),
+                      special_frac=0.001)
+    tsf = 0.02 if fmt == oracle.NVFP4 else 1.0
+    assert_same(*dense_pair(bsq, x, fmt, tsf, pad_x=8, pad_q=pad_q, pad_s=pad_s), f"{M}x{K}")
+
+
+@pytest.mark.parametrize("fmt", [oracle.MXFP4, oracle.NVFP4], ids=["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("K", [4048, 6144])
+def test_grouped_large_path_odd_scale_rows_with_gather(bsq, fmt, K):
+    """The grouped FP4 path over 2^22 elements with gather and unpadded scale
+    offsets.  K = 4048 (NVFP4 only): 253 scale bytes per row, so scale rows
+    alternate between even and odd addresses, and a row's second tile holds
+    its partial chunk."""
+    if fmt == oracle.MXFP4 and K % 32:
+        pytest.skip("MXFP4 needs K a multiple of 32")
+    rows = 1100
+    assert rows * K > (1 << 22)
+    c = make_grouped(fmt, S=1200, K=K, G=40, E=50, rows=rows, gather=True, seed=K + fmt,
+                     first_row=3, extra_rows=4, pad=1)
+    assert_same(*grouped_pair(bsq, c, pad_rows=1, pad_scale_rows=2), c.name)
+
+
 @pytest.mark.parametrize("fmt", [oracle.MXFP4, oracle.MXFP8, oracle.NVFP4],
                          ids=["mxfp4", "mxfp8", "nvfp4"])
 @pytest.mark.parametrize("G,gather,K", [(5, False, 4608), (129, True, 4608), (600, False, 4608),
