@@ -9,8 +9,9 @@
 // same code and scale store instructions and cache policies -- but computes
 // nothing: a lane's codes are an XOR fold of the words it loaded and its
 // scale byte is the low byte of its first loaded word.  Its time on a given
-// problem is the practical ceiling for a quantizer of that byte mix on this
-// chip, which is below the 8 TB/s peak.
+// problem is the bandwidth that byte mix reaches with the quantizer's own
+// instruction shape on this chip, which is below the 8 TB/s peak (a stream
+// with wider stores can do better for the FP4 mixes).
 //
 // What it writes, for chunk c of row r and lane l (elements 512 c + 8 l ..
 // 512 c + 8 l + 7, loaded as words w0..w3):

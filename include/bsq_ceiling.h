@@ -1,9 +1,10 @@
 /*
  * bsq_ceiling.h -- C ABI of libbsq_ceiling, a measurement aid beside libbsq:
  * trivial streams with the memory traffic of a dense quantizer launch and of
- * a dequantizer launch, whose times are the practical bandwidth ceilings for
- * those byte mixes on this chip.  They compute nothing of the method (no
- * block amax, scale, rounding or decoding).
+ * a dequantizer launch, with the kernels' own tiles and load and store
+ * instructions, whose times are the bandwidth those byte mixes reach with
+ * that instruction shape on this chip.  They compute nothing of the method
+ * (no block amax, scale, rounding or decoding).
  *
  * bsq_ceiling_stream reads x, BF16 [M, K] (contiguous rows, 16-byte aligned),
  * and writes codes ([M, K/2] bytes for format 0 or 2, [M, K] for format 1;
