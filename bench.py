@@ -341,6 +341,41 @@ def timed_region(torch, arm, launch, steps, warmup):
     return wall, span, kernel_us
 
 
+COLD_FLUSH_BYTES = 1 << 30
+
+
+def cold_launches(runner, nbytes, flush_kind, launches=50, warmup=5):
+    """The cold-cache protocol: before each launch a kernel on the same stream
+    streams a 1 GiB buffer (more than the 256 MB MALL and the L2 together),
+    then the launch runs with an event pair bound to its dispatch; `warmup`
+    such pairs untimed, then `launches` timed.  flush_kind "read" reads the
+    buffer (a reduction): every line the launch uses is evicted and the caches
+    hold clean lines.  "write" fills it (a memset): the caches then hold up to
+    the MALL's size in dirty lines, whose write-back to HBM falls inside the
+    next launch.  Returns the kernel times' spread and the bandwidth of their
+    median."""
+    torch = runner.torch
+    flush = torch.ones(COLD_FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty((), dtype=torch.int64, device="cuda")
+    pairs = recorded_events(torch, launches)
+    for i in range(warmup + launches):
+        if flush_kind == "read":
+            torch.sum(flush, dim=0, out=sink)
+        else:
+            flush.fill_(i)
+        if i >= warmup:
+            runner.bsq.time_next_launch(*pairs[i - warmup])
+        runner.step(i)
+    torch.cuda.synchronize()
+    k = spread([a.elapsed_time(b) * 1e3 for a, b in pairs])
+    del flush
+    return {"kernel_us": k, "GBps_median": round(nbytes / k["median"] / 1e3, 1),
+            "frac_median": round(nbytes / k["median"] / 1e3 / PEAK_HBM_GBS, 4),
+            "flush": f"1 GiB {'read (a reduction)' if flush_kind == 'read' else 'fill (memset)'}"
+                     " on the launch stream before each launch",
+            "launches": launches, "warmup": warmup}
+
+
 def graph_launch_us(runner, n_launch=64, replays=20):
     """Mean duration per launch (µs) when n_launch launches, rotating over the
     buffer sets, are replayed from one captured HIP graph: no host launch cost
@@ -883,6 +918,9 @@ def main():
         if name in quant:
             if name in LARGE:
                 s["roofline"] = roofline(s, *traffic_from_counters(name), ceil)
+                # the cold-cache protocol beside the rotated buffers (one flush per launch)
+                s["roofline"]["cold"] = cold_launches(runner, nbytes, "read")
+                s["roofline"]["cold_after_fill"] = cold_launches(runner, nbytes, "write")
             if not args.no_cpu_baseline:
                 s["cpu_baseline"] = cpu_baseline(case, runner, 12.0 if name == args.workload
                                                  else 4.0)
