@@ -511,7 +511,9 @@ def roofline(s, traffic, traffic_note, ceil=None):
          "bytes_per_launch": s["bytes_per_launch"],
          "timing": "per-launch HIP events bound to the kernel dispatch (hipExtLaunchKernel) "
                    "over the timed region",
-         "traffic": traffic, "traffic_note": traffic_note}
+         "traffic": traffic, "traffic_note": traffic_note,
+         # the counters' HBM bytes over the same kernel time, beside the algorithmic rate
+         "traffic_GBps": round(traffic / k["mean"] / 1e3, 1) if traffic else None}
     if ceil is not None:
         r["ceiling"] = ceil
         # the kernel's speed as a fraction of the trivial stream's (above 1: faster than it)
