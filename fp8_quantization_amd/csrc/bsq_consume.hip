@@ -227,7 +227,7 @@ __device__ __forceinline__ mfma_v8i load_fragment(const uint8_t* row, int k0, in
 // 16 x 16 tiles, stepping through K in stages of 128 bytes per operand row
 // (one 128-element K step of E4M3, two of E2M1) that are staged in LDS; its
 // scale bytes come from the 512-element records of the MFMA layout, staged
-// beside them.
+// once per record in buffers of their own.
 template <int TM_, int TN_, int WAVES_M_, int WAVES_N_>
 struct TileCfg {
     static constexpr int TM = TM_, TN = TN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -235,10 +235,10 @@ struct TileCfg {
     static constexpr int IM = TM / WAVES_M / 16, JN = TN / WAVES_N / 16;
     static constexpr int kChunksA = TM / 8 / NW;               // 1 KiB row chunks per wave
     static constexpr int kChunksB = TN / 8 / NW;
-    static constexpr int kRecords = (TM + TN) / 16;            // scale records per stage
+    static constexpr int kRecords = (TM + TN) / 16;            // scale records per 512 elements
     static constexpr int kRecordLoads = kRecords / (4 * NW);   // 1 KiB runs of records per wave
-    static constexpr int kPerWave = kChunksA + kChunksB + kRecordLoads;  // direct loads per stage
-    static constexpr int kStageBytes = (TM + TN) * 128 + kRecords * 256;
+    static constexpr int kStageBytes = (TM + TN) * 128;        // one stage of operand rows
+    static constexpr int kRecordBytes = kRecords * 256;        // one record of every row group
     // every wave moves the same number of rows and of 1 KiB runs of records
     static_assert(TM % (8 * NW) == 0 && TN % (8 * NW) == 0 && kRecords % (4 * NW) == 0,
                   "tile shape");
@@ -414,10 +414,10 @@ __device__ __forceinline__ bool grouped_desc_xcd(const GemmArgs& a, const Groupe
 // rows and TN B rows of 128 bytes each, unpadded; logical 16-byte piece c
 // of row R sits at piece c ^ (R % 8) (each lane chooses which global piece it
 // fetches for its LDS slot), so the 8 rows a fragment read serves at once
-// fall in distinct banks.  After the rows, the buffer holds the scale records
-// of the stage's 512 elements (TM / 16 A row groups, then TN / 16 B row
-// groups, 256 bytes each): every wave issues the same loads per stage, so the
-// wait for a stage is a fixed count of the loads issued after it.
+// fall in distinct banks.  The scale records of a 512-element span of K
+// (TM / 16 A row groups, then TN / 16 B row groups, 256 bytes each) go to one
+// of two record buffers, loaded with the span's first stage: an E2M1 record
+// serves two stages, an E4M3 one four.
 
 __device__ __forceinline__ void dma16(const void* g, uint8_t* lds) {
     __builtin_amdgcn_global_load_lds(const_cast<void*>(g), lds, 16, 0, 0);
@@ -433,8 +433,16 @@ __device__ __forceinline__ void wait_vm() {
 // chunks of A wholly past the rows are not loaded and 16-row blocks past them
 // not multiplied; the dense form keeps straight-line stages (the skip costs its
 // 256 x 256 MXFP8 tile registers enough to spill).
-template <int FMT, int NBUF, class Cfg, bool SKIP_PAD>
-__device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const (&bufs)[NBUF]) {
+//
+// NT_STORE: c leaves with nontemporal stores.  The grouped form's tiles end
+// throughout the launch, and written through ordinary stores they stayed
+// dirty in the XCDs' L2: nontemporal stores took 3-5 us off the 73-78 us of
+// the prefill routing.  The dense form's tiles all end together, and there
+// ordinary stores measured faster (4096 x 4096 x 7168: 68 against 74 us for
+// MXFP4, 112 against 117 for MXFP8).  Same outputs, A/B runs on one box.
+template <int FMT, int NBUF, class Cfg, bool SKIP_PAD, bool NT_STORE>
+__device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const (&bufs)[NBUF],
+                                              uint8_t* const (&recs)[2]) {
     constexpr int kFmt = FMT == 1 ? 0 : 4;
     constexpr int kStepBytes = FMT == 1 ? 128 : 64;
     constexpr int kSteps = 128 / kStepBytes;                 // K steps per stage
@@ -444,10 +452,10 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const 
     // with two buffers a wave waits for all its loads (vmcnt 0) at the top of a stage, so
     // waves may issue different numbers of them (SKIP_PAD)
     static_assert(NBUF == 2, "the stage wait assumes two buffers");
-    // the stage loop is unrolled by a multiple of both the buffer count and the stages per
-    // record, so each unrolled stage's buffer and opsel byte are constants
-    constexpr int kUnroll = NBUF % kPerRecord == 0 ? NBUF
-                          : kPerRecord % NBUF == 0 ? kPerRecord : NBUF * kPerRecord;
+    // the stage loop is unrolled over two records, so each unrolled stage's stage buffer,
+    // record buffer and opsel byte are constants
+    constexpr int kUnroll = 2 * kPerRecord;
+    static_assert(kUnroll % NBUF == 0, "stage buffers per unrolled pass");
     const int tid = (int)threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
     const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
@@ -456,10 +464,12 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const 
 
     // this lane's slot in a 1 KiB chunk: row 8 c + lane / 8, physical piece lane % 8
     const int crow = lane >> 3, cpiece = lane & 7;
-    // stage s goes to buffer s % NBUF; the caller passes that index as a constant, so
-    // every LDS access names one buffer (distinct LDS objects keep the compiler's
-    // waits for the in-flight loads to the buffer actually read)
-    auto issue = [&](int s, uint8_t* buf) {
+    // stage s goes to buffer s % NBUF and the records of its 512 elements to record
+    // buffer (s / kPerRecord) % 2; the caller passes both as constants, so every LDS
+    // access names one buffer (distinct LDS objects keep the compiler's waits for the
+    // in-flight loads to the buffer actually read).  rec is null for a stage that does
+    // not start a record.
+    auto issue = [&](int s, uint8_t* buf, uint8_t* rec) {
         // row chunk c (rows 8 c .. 8 c + 7) of an operand goes to 1 KiB at c;
         // rows past the operand load its last row, bytes past K any in-row
         // bytes: their products are never stored
@@ -481,6 +491,7 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const 
             const int64_t rb = row < d.b_rows ? row : d.b_rows - 1;
             dma16(d.b + rb * d.ldb_q + kb, buf + TM * 128 + chunk * 1024);
         }
+        if (rec == nullptr) return;
         // scale records of the stage's 512 elements (A row groups, then B row
         // groups): run j = wave + NW i holds records 4 j .. 4 j + 3, lane L moving
         // bytes 16 (L % 16) of record 4 j + L / 16
@@ -488,14 +499,14 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const 
 #pragma unroll
         for (int i = 0; i < Cfg::kRecordLoads; ++i) {
             const int run = wave + Cfg::NW * i;
-            const int rec = 4 * run + (lane >> 4);
-            const bool is_a = rec < TM / 16;
-            const int g = is_a ? rec : rec - TM / 16;
+            const int r = 4 * run + (lane >> 4);
+            const bool is_a = r < TM / 16;
+            const int g = is_a ? r : r - TM / 16;
             const int64_t groups = is_a ? d.a_groups : d.b_groups;
             const int64_t gg = g < groups ? g : groups - 1;
             const uint8_t* src = (is_a ? d.as + gg * d.lda_s : d.bs + gg * d.ldb_s) +
                                  (int64_t)k512 * 256 + 16 * (lane & 15);
-            dma16(src, buf + (TM + Cfg::TN) * 128 + run * 1024);
+            dma16(src, rec + run * 1024);
         }
     };
 
@@ -505,9 +516,7 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const 
 #pragma unroll
         for (int j = 0; j < JN; ++j) acc[i][j] = (mfma_v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
-#pragma unroll
-    for (int s = 0; s < NBUF - 1; ++s)
-        if (s < nstages) issue(s, bufs[s]);
+    if (nstages > 0) issue(0, bufs[0], recs[0]);
     const int fr = lane & 15, fg = lane >> 4;
     for (int s0 = 0; s0 < nstages; s0 += kUnroll) {
 #pragma unroll
@@ -520,19 +529,28 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const 
         // write LDS directly and the explicit wait is the one they need.
         wait_vm<0>();
         asm volatile("s_barrier" ::: "memory");
-        if (s + NBUF - 1 < nstages) issue(s + NBUF - 1, bufs[(u + NBUF - 1) % NBUF]);
         const uint8_t* buf = bufs[u % NBUF];
-        // row groups past the operand's end hold the last group's record (their
-        // outputs are never stored), so every read is unconditional
-        constexpr int sc = (TM + Cfg::TN) * 128;
+        const uint8_t* rec = recs[(u / kPerRecord) % 2];
+        // the scale dwords are read before the next stage's loads are issued: read after
+        // them, the compiler made the stage's fragment reads wait for those loads too.
+        // Row groups past the operand's end hold the last group's record (their outputs
+        // are never stored), so every read is unconditional.
         uint32_t sa[IM], sb[JN];
 #pragma unroll
         for (int i = 0; i < IM; ++i)
-            sa[i] = *reinterpret_cast<const uint32_t*>(buf + (sc + (IM * wm + i) * 256 + 4 * lane));
+            sa[i] = *reinterpret_cast<const uint32_t*>(rec + ((IM * wm + i) * 256 + 4 * lane));
 #pragma unroll
         for (int i = 0; i < JN; ++i)
             sb[i] = *reinterpret_cast<const uint32_t*>(
-                buf + (sc + (TM / 16 + JN * wn + i) * 256 + 4 * lane));
+                rec + ((TM / 16 + JN * wn + i) * 256 + 4 * lane));
+        // the next stage's rows, and its record when it starts one (into the record buffer
+        // whose last reader finished before this barrier)
+        if (s + 1 < nstages) {
+            if ((u + 1) % kPerRecord == 0)
+                issue(s + 1, bufs[(u + 1) % NBUF], recs[((u + 1) / kPerRecord) % 2]);
+            else
+                issue(s + 1, bufs[(u + 1) % NBUF], nullptr);
+        }
         // every LDS address is the buffer plus one integer offset: a single step from
         // the LDS object keeps the compiler's knowledge of which buffer is read
         auto fragment = [&](int region, int r0, int j) {
@@ -565,55 +583,75 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const 
                 const mfma_v8i fa = fragment(0, 16 * (IM * wm + im), j);
 #pragma unroll
                 for (int jn = 0; jn < JN; ++jn) {
+                    // B as the first operand: the result is the tile of c transposed, so
+                    // lane l holds row l % 16 and columns 4 (l / 16) .. + 3 of c
                     switch (t) {
                         case 0: acc[im][jn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                    fa, fb[jn], acc[im][jn], kFmt, kFmt, 0, (int)sa[im], 0,
-                                    (int)sb[jn]); break;
+                                    fb[jn], fa, acc[im][jn], kFmt, kFmt, 0, (int)sb[jn], 0,
+                                    (int)sa[im]); break;
                         case 1: acc[im][jn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                    fa, fb[jn], acc[im][jn], kFmt, kFmt, 1, (int)sa[im], 1,
-                                    (int)sb[jn]); break;
+                                    fb[jn], fa, acc[im][jn], kFmt, kFmt, 1, (int)sb[jn], 1,
+                                    (int)sa[im]); break;
                         case 2: acc[im][jn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                    fa, fb[jn], acc[im][jn], kFmt, kFmt, 2, (int)sa[im], 2,
-                                    (int)sb[jn]); break;
+                                    fb[jn], fa, acc[im][jn], kFmt, kFmt, 2, (int)sb[jn], 2,
+                                    (int)sa[im]); break;
                         default: acc[im][jn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                    fa, fb[jn], acc[im][jn], kFmt, kFmt, 3, (int)sa[im], 3,
-                                    (int)sb[jn]); break;
+                                    fb[jn], fa, acc[im][jn], kFmt, kFmt, 3, (int)sb[jn], 3,
+                                    (int)sa[im]); break;
                     }
                 }
             }
         }
     }
     }
+    // one 16-byte store per lane and tile when its four columns exist and c's rows are
+    // 16-byte aligned, else one per element
+    const bool vec = ((reinterpret_cast<uintptr_t>(d.c) | (uintptr_t)(d.ldc * 4)) & 15) == 0;
 #pragma unroll
-    for (int im = 0; im < IM; ++im)
+    for (int im = 0; im < IM; ++im) {
+        const int64_t row = 16 * (IM * wm + im) + fr;
+        if (row >= d.c_rows) continue;
 #pragma unroll
         for (int jn = 0; jn < JN; ++jn) {
-            const int64_t col = 16 * (JN * wn + jn) + fr;
+            const int64_t col = 16 * (JN * wn + jn) + 4 * fg;
+            float* p = d.c + row * d.ldc + col;
+            if (vec && col + 4 <= d.c_cols) {
+                if constexpr (NT_STORE)
+                    __builtin_nontemporal_store(acc[im][jn], reinterpret_cast<mfma_v4f*>(p));
+                else
+                    *reinterpret_cast<mfma_v4f*>(p) = acc[im][jn];
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t row = 16 * (IM * wm + im) + 4 * fg + e;
-                if (row < d.c_rows && col < d.c_cols) d.c[row * d.ldc + col] = acc[im][jn][e];
+                for (int e = 0; e < 4; ++e) {
+                    if (col + e >= d.c_cols) continue;
+                    if constexpr (NT_STORE) __builtin_nontemporal_store(acc[im][jn][e], p + e);
+                    else p[e] = acc[im][jn][e];
+                }
             }
         }
+    }
 }
 
-// The stage buffers are separate LDS objects: the compiler then knows which
-// buffer each LDS read and each direct load touches, and waits only for the
-// loads into the buffer being read.
+// The stage and record buffers are separate LDS objects: the compiler then knows
+// which buffer each LDS read and each direct load touches, and waits only for
+// the loads into the buffer being read.
 // Two stage buffers (a third leaves one 128 x 128 workgroup per CU and
 // measured slower).
-#define BSQ_STAGE_BUFFERS(BYTES)                                                           \
-    __shared__ __attribute__((aligned(16))) uint8_t stage0[BYTES];                         \
-    __shared__ __attribute__((aligned(16))) uint8_t stage1[BYTES];
+#define BSQ_STAGE_BUFFERS(Cfg)                                                             \
+    __shared__ __attribute__((aligned(16))) uint8_t stage0[Cfg::kStageBytes];              \
+    __shared__ __attribute__((aligned(16))) uint8_t stage1[Cfg::kStageBytes];              \
+    __shared__ __attribute__((aligned(16))) uint8_t record0[Cfg::kRecordBytes];            \
+    __shared__ __attribute__((aligned(16))) uint8_t record1[Cfg::kRecordBytes];            \
+    uint8_t* const bufs[2] = {stage0, stage1};                                             \
+    uint8_t* const recs[2] = {record0, record1};
 
 template <int FMT, class Cfg>
 __global__ void __launch_bounds__(64 * Cfg::NW) mfma_gemm_tiled_kernel(const GemmArgs a,
                                                                         int64_t tiles_n) {
-    BSQ_STAGE_BUFFERS(Cfg::kStageBytes)
+    BSQ_STAGE_BUFFERS(Cfg)
     GemmTile d;
     dense_desc<Cfg::TM, Cfg::TN>(a, tiles_n, d);
-    uint8_t* const bufs[2] = {stage0, stage1};
-    gemm_tile_dma<FMT, 2, Cfg, false>(d, bufs);
+    gemm_tile_dma<FMT, 2, Cfg, false, false>(d, bufs, recs);
 }
 
 // The grouped form for groups of more than 16 rows on average.  Measured on
@@ -627,11 +665,10 @@ __global__ void __launch_bounds__(64 * Cfg::NW) mfma_gemm_tiled_kernel(const Gem
 template <int FMT>
 __global__ void __launch_bounds__(64 * Tile128::NW)
 mfma_gemm_grouped_kernel(const GemmArgs a, const GroupedGemmArgs g) {
-    BSQ_STAGE_BUFFERS(Tile128::kStageBytes)
+    BSQ_STAGE_BUFFERS(Tile128)
     GemmTile d;
     if (!grouped_desc_xcd<kTileM, kTileN>(a, g, d)) return;
-    uint8_t* const bufs[2] = {stage0, stage1};
-    gemm_tile_dma<FMT, 2, Tile128, true>(d, bufs);
+    gemm_tile_dma<FMT, 2, Tile128, true, true>(d, bufs, recs);
 }
 
 // ------------------------------------------------------------ decode regime
