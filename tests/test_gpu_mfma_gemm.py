@@ -230,11 +230,14 @@ def grouped_case(fmt, G, E, N, K, rows, seed, misaligned=None):
                                           (40, 16, 160, 1024, 900), (9, 4, 256, 7168, 700),
                                           (130, 20, 96, 512, 3000), (200, 7, 48, 256, 9000),
                                           (3, 2, 200, 128, 400), (4, 3, 130, 384, 500),
-                                          (6, 5, 272, 1664, 800)])
+                                          (6, 5, 272, 1664, 800), (256, 9, 48, 256, 9000),
+                                          (257, 9, 48, 256, 9000), (300, 11, 64, 512, 10000)])
 def test_grouped_mfma_matches_oracle(bsq, fmt, G, E, N, K, rows):
-    """Groups of more than 16 rows on average: 128-row tiles, A through LDS and
-    B into registers, three stages in flight.  K = 128 and 384 end on a half
-    stage in MXFP4 (256 elements a stage); 1664 is 13 K steps."""
+    """Groups of more than 16 rows on average: 128 x 128 tiles, both operands
+    staged through LDS.  K = 128 and 384 end on a half stage in MXFP4 (256
+    elements a stage); 1664 is 13 K steps.  Up to 256 groups the tile's group
+    comes from one round of metadata loads held in registers; 257 and 300 take
+    the search over 64 groups at a time."""
     d = grouped_case(fmt, G, E, N, K, rows, seed=G + N + K + fmt)
     assert d["max_rows"] > 16 * G
     check_grouped_run(bsq, fmt, d, G, E, N, K)
