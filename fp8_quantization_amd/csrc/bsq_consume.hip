@@ -509,12 +509,17 @@ __device__ __forceinline__ void wait_vm() {
 // not multiplied; the dense form keeps straight-line stages (the skip costs its
 // 256 x 256 MXFP8 tile registers enough to spill).
 //
-// NT_STORE: c leaves with nontemporal stores.  The grouped form's tiles end
+// NT_STORE (the grouped form): c leaves with nontemporal stores of whole
+// rows of the wave's block, staged through LDS.  The grouped form's tiles end
 // throughout the launch, and written through ordinary stores they stayed
 // dirty in the XCDs' L2: nontemporal stores took 3-5 us off the 73-78 us of
-// the prefill routing.  The dense form's tiles all end together, and there
-// ordinary stores measured faster (4096 x 4096 x 7168: 68 against 74 us for
-// MXFP4, 112 against 117 for MXFP8).  Same outputs, A/B runs on one box.
+// the prefill routing.  Stored straight from the MFMA layout, each such store
+// covered 64 bytes of 16 rows, half lines that were written to memory apart
+// (48.9 MB of writes for 33.5 MB of c); staged, each covers 256 bytes of 4
+// rows: 71.2 -> 66.7 us.  The dense form's tiles all end together, and there
+// ordinary stores from registers measured faster (4096 x 4096 x 7168: 68
+// against 74 us for MXFP4, 112 against 117 for MXFP8).  Same outputs, A/B
+// runs on one box.
 template <int FMT, int NBUF, class Cfg, bool SKIP_PAD, bool NT_STORE>
 __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const (&bufs)[NBUF],
                                               uint8_t* const (&recs)[2]) {
@@ -679,30 +684,58 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmTile& d, uint8_t* const 
         }
     }
     }
-    // one 16-byte store per lane and tile when its four columns exist and c's rows are
-    // 16-byte aligned, else one per element
     const bool vec = ((reinterpret_cast<uintptr_t>(d.c) | (uintptr_t)(d.ldc * 4)) & 15) == 0;
+    // one 16-byte store when its four columns exist and c's rows are 16-byte aligned, else
+    // one per element
+    auto store4 = [&](const mfma_v4f& v, int64_t row, int64_t col) {
+        float* p = d.c + row * d.ldc + col;
+        if (vec && col + 4 <= d.c_cols) {
+            if constexpr (NT_STORE) __builtin_nontemporal_store(v, reinterpret_cast<mfma_v4f*>(p));
+            else *reinterpret_cast<mfma_v4f*>(p) = v;
+        } else {
 #pragma unroll
-    for (int im = 0; im < IM; ++im) {
-        const int64_t row = 16 * (IM * wm + im) + fr;
-        if (row >= d.c_rows) continue;
-#pragma unroll
-        for (int jn = 0; jn < JN; ++jn) {
-            const int64_t col = 16 * (JN * wn + jn) + 4 * fg;
-            float* p = d.c + row * d.ldc + col;
-            if (vec && col + 4 <= d.c_cols) {
-                if constexpr (NT_STORE)
-                    __builtin_nontemporal_store(acc[im][jn], reinterpret_cast<mfma_v4f*>(p));
-                else
-                    *reinterpret_cast<mfma_v4f*>(p) = acc[im][jn];
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (col + e >= d.c_cols) continue;
-                    if constexpr (NT_STORE) __builtin_nontemporal_store(acc[im][jn][e], p + e);
-                    else p[e] = acc[im][jn][e];
-                }
+            for (int e = 0; e < 4; ++e) {
+                if (col + e >= d.c_cols) continue;
+                if constexpr (NT_STORE) __builtin_nontemporal_store(v[e], p + e);
+                else p[e] = v[e];
             }
+        }
+    };
+    if constexpr (NT_STORE) {
+        // the wave's (16 IM) x (16 JN) block goes to its own part of the stage buffers, free
+        // once every wave is past its last stage (16-byte piece q of row r at q ^ (r % 16)),
+        // and leaves as runs of 64 JN bytes: lane l stores piece l % (4 JN) of a row
+        constexpr int kPieces = 4 * JN, kRowsPer = 64 / kPieces;
+        constexpr int kWaveBytes = 16 * IM * 16 * kPieces;
+        static_assert(Cfg::NW == 4 && 2 * kWaveBytes == Cfg::kStageBytes && kPieces == 16,
+                      "two waves' blocks per stage buffer");
+        __syncthreads();
+        uint8_t* blk = (wave < 2 ? bufs[0] : bufs[1]) + (wave & 1) * kWaveBytes;
+#pragma unroll
+        for (int im = 0; im < IM; ++im)
+#pragma unroll
+            for (int jn = 0; jn < JN; ++jn) {
+                const int r = 16 * im + fr, q = 4 * jn + fg;
+                *reinterpret_cast<mfma_v4f*>(blk + r * (16 * kPieces) + 16 * (q ^ (r & 15))) =
+                    acc[im][jn];
+            }
+        const int q = lane % kPieces;
+#pragma unroll
+        for (int k = 0; k < 16 * IM / kRowsPer; ++k) {
+            const int r = kRowsPer * k + lane / kPieces;
+            const int64_t row = 16 * IM * wm + r;
+            if (row >= d.c_rows) continue;
+            store4(*reinterpret_cast<const mfma_v4f*>(blk + r * (16 * kPieces) + 16 * (q ^ (r & 15))),
+                   row, 16 * JN * wn + 4 * q);
+        }
+    } else {
+        // lane l holds row l % 16 and columns 4 (l / 16) .. + 3 of each 16 x 16 tile
+#pragma unroll
+        for (int im = 0; im < IM; ++im) {
+            const int64_t row = 16 * (IM * wm + im) + fr;
+            if (row >= d.c_rows) continue;
+#pragma unroll
+            for (int jn = 0; jn < JN; ++jn) store4(acc[im][jn], row, 16 * (JN * wn + jn) + 4 * fg);
         }
     }
 }
