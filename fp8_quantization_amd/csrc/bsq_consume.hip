@@ -765,11 +765,18 @@ __global__ void __launch_bounds__(64 * Cfg::NW) mfma_gemm_tiled_kernel(const Gem
 // The grouped form for groups of more than 16 rows on average.  Measured on
 // the prefill routing (16384 rows over 128 experts, N = 512, K = 7168,
 // MXFP4), these 128 x 128 tiles of 4 waves with both operands staged through
-// two LDS buffers ran 77-80 us; the alternatives tried ran slower: 128 x 256
-// tiles of 8 waves (88.6 us), B straight to registers with three LDS stages
-// for A (92), 64 x 128 tiles (91).  Copies of this kernel that skip the LDS
-// fragment reads, or the MFMAs, ran within 3% of it, and one that loads only
-// its first stage ran 40.7 us; one workgroup per CU instead of two ran 116.
+// two LDS buffers run 66-68.5 us.  The alternatives tried ran slower: 128 x 256
+// tiles of 8 waves (88.6 us), 128 x 512 tiles of 8 waves that read each A row
+// tile once (77 against 77), B straight to registers with three LDS stages for
+// A (92), 64 x 128 tiles (91), four stage buffers and one workgroup per CU (94
+// against 77), every workgroup of an XCD given an equal run of K stages over
+// consecutive tiles (99 against 73.5: neighbouring workgroups then no longer
+// share A and B in the XCD's L2 at the same time).  A copy that skips the LDS
+// fragment reads and the MFMAs runs within 6% of it; one that loads only its
+// first stage ran at half its time.  Its 804 tiles fill 1.57 rounds of the
+// 512 slots (two per CU), and a tile's time is set by its 28 stages' latency,
+// not by how many tiles share the chip: the second, partial round costs about
+// as much as the first.
 template <int FMT>
 __global__ void __launch_bounds__(64 * Tile128::NW)
 mfma_gemm_grouped_kernel(const GemmArgs a, const GroupedGemmArgs g) {
