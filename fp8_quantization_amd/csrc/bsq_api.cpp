@@ -646,9 +646,8 @@ int grouped_block_scaled_matmul_mfma(int format, int block_size, int scale_layou
     const int64_t tile_n = g.row_blocks ? bsq::kDecodeTileCols : 128;
     g.m_tiles = (max_rows + tile_m - 1) / tile_m + num_groups;  // each group adds at most one
                                                                 // partial tile
-    // the 128-row kernel takes one workgroup per (row tile, column tile), in one dimension
-    if (g.m_tiles > 0x7FFFFFFFLL || (N + tile_n - 1) / tile_n > 65535 ||
-        (!g.row_blocks && g.m_tiles * ((N + tile_n - 1) / tile_n) > 0x7FFFFFF0LL))
+    // both forms take one workgroup per (row tile, column tile), in one dimension
+    if (g.m_tiles > 0x7FFFFFFFLL || g.m_tiles * ((N + tile_n - 1) / tile_n) > 0x7FFFFFF0LL)
         return fail(BSQ_ERR_INVALID_ARG, "problem too large for one launch");
     bsq::GemmArgs a{};
     a.a_codes = static_cast<const uint8_t*>(a_codes);
