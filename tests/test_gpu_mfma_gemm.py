@@ -376,6 +376,38 @@ def test_grouped_mfma_skips_bad_expert_ids_and_rows_past_max_rows(bsq):
         gemm_bound.check(got[lo:hi], qa, sa, qb, sb, fmt, K, want)
 
 
+@pytest.mark.parametrize("fmt", [MXFP4, MXFP8])
+@pytest.mark.parametrize("G,rows,pad", [(5, 300, 4), (5, 300, 3), (40, 100, 4), (40, 100, 3)])
+def test_grouped_mfma_into_a_wider_output(bsq, fmt, G, rows, pad):
+    """c as a view of a wider buffer (ldc = N + pad): 128-row tiles (5 groups,
+    300 rows) and 16-row tiles (40 groups, 100 rows); with pad 4 the rows stay
+    16-byte aligned and c leaves in 16-byte stores, with pad 3 in 4-byte ones.
+    Every owned row matches the oracle within the bound, and the pad columns
+    and the rows no group owns keep their 7.0."""
+    E, N, K = 3, 100, 512
+    d = grouped_case(fmt, G, E, N, K, rows, seed=G + rows + pad + fmt)
+    max_rows = d["max_rows"]
+    wide = torch.full((max_rows, N + pad), 7.0, dtype=torch.float32, device="cuda")
+    out = wide[:, :N]
+    bsq.grouped_block_scaled_matmul_mfma(
+        dev(d["qa"]), dev(d["la"]), dev(d["ro"].view(np.int32)), dev(d["so"].view(np.int32)),
+        dev(d["ids"]), max_rows, d["nsr"], dev(d["qb"]), dev(d["lb"]), E, fmt, K, out=out)
+    torch.cuda.synchronize()
+    got = wide.cpu().numpy().astype(np.float64)
+    assert np.all(got[:, N:] == 7.0)
+    owned = np.zeros(max_rows, bool)
+    for g in range(G):
+        lo, hi, so, e = int(d["ro"][g]), int(d["ro"][g + 1]), int(d["so"][g]), int(d["ids"][g])
+        if hi == lo:
+            continue
+        owned[lo:hi] = True
+        qa, sa = d["qa"][lo:hi], d["sa"][so:so + hi - lo]
+        qb, sb = d["qb"][e * N:(e + 1) * N], d["sb"][e * N:(e + 1) * N]
+        want = oracle.block_scaled_matmul(qa, sa, qb, sb, fmt, K)
+        gemm_bound.check(got[lo:hi, :N], qa, sa, qb, sb, fmt, K, want)
+    assert np.all(got[~owned, :N] == 7.0)
+
+
 @pytest.mark.parametrize("rows", [300, 30])
 def test_grouped_zero_k_writes_zeros(bsq, rows):
     """K = 0 with 128-row (300 rows over 2 groups) and 32-row tiles: every
